@@ -1,0 +1,130 @@
+"""The benchmark and parity workloads: shapes, dtypes, distributions, seeds.
+
+Feature-map shapes follow the operator benchmarks of "Efficient Deformable
+ConvNets" (CSDN walkthrough "DCNv4论文解析", section 3.1: maps of a 224x224
+input at /4, /8, /16, /32 with batch 64, and a batch-1 high-resolution map)
+with 16 channels per group, the 3x3 grid, stride 1, pad 1, dilation 1 and
+offset_scale 1.0.  Inputs are synthetic (``synth``); sigma values are standard
+deviations.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+from . import synth
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    N: int
+    H: int
+    W: int
+    C: int
+    G: int
+    dtype: str            # storage dtype: fp32 | fp16 | bf16
+    seed: int
+    sigma_value: float
+    sigma_off: float
+    sigma_m: float
+    direction: str        # fwd | bwd
+    remove_center: bool = False
+    integer_offsets: bool = False
+    kernel: tuple = (3, 3)
+    stride: tuple = (1, 1)
+    pad: tuple = (1, 1)
+    dilation: tuple = (1, 1)
+    offset_scale: float = 1.0
+    sigma_grad: float = 1.0
+    note: str = field(default="", compare=False)
+
+    @property
+    def Cg(self) -> int:
+        return self.C // self.G
+
+    @property
+    def K(self) -> int:
+        return self.kernel[0] * self.kernel[1] - int(self.remove_center)
+
+    @property
+    def P(self) -> int:
+        return synth.om_channels(self.G, self.K)
+
+    @property
+    def Ho(self) -> int:
+        kh, s, p, d = self.kernel[0], self.stride[0], self.pad[0], self.dilation[0]
+        return (self.H + 2 * p - (d * (kh - 1) + 1)) // s + 1
+
+    @property
+    def Wo(self) -> int:
+        kw, s, p, d = self.kernel[1], self.stride[1], self.pad[1], self.dilation[1]
+        return (self.W + 2 * p - (d * (kw - 1) + 1)) // s + 1
+
+    @property
+    def points(self) -> int:
+        """Sampled points per call: N * Ho * Wo * G * K * C'."""
+        return self.N * self.Ho * self.Wo * self.G * self.K * self.Cg
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "fp32" else 2
+
+    def fwd_bytes(self) -> int:
+        """Compulsory forward bytes: value + offset_mask + output."""
+        s = self.elem_bytes
+        return s * (self.N * self.H * self.W * self.C + self.N * self.Ho * self.Wo * (self.P + self.C))
+
+    def bwd_bytes(self) -> int:
+        """Compulsory backward bytes: read value, offset_mask, grad_output;
+        write grad_value, grad_offset_mask (all fp32)."""
+        s = self.elem_bytes
+        nv = self.N * self.H * self.W * self.C
+        no = self.N * self.Ho * self.Wo
+        return s * (2 * nv + no * (2 * self.P + self.C))
+
+    def kwargs(self) -> dict:
+        return dict(kernel_h=self.kernel[0], kernel_w=self.kernel[1],
+                    stride_h=self.stride[0], stride_w=self.stride[1],
+                    pad_h=self.pad[0], pad_w=self.pad[1],
+                    dilation_h=self.dilation[0], dilation_w=self.dilation[1],
+                    group=self.G, group_channels=self.Cg,
+                    offset_scale=self.offset_scale, remove_center=self.remove_center)
+
+    def make_inputs(self, pad_fill: float = float("nan"), N: int | None = None,
+                    with_grad: bool | None = None):
+        """float32 numpy (value, offset_mask[, grad_out]) before storage rounding.
+
+        grad_out is drawn when ``with_grad`` (default: backward workloads).
+
+        ``N`` < self.N draws the first N images of the same streams (a bounded
+        sample of the same workload)."""
+        n = self.N if N is None else N
+        v = synth.value_f32((n, self.H, self.W, self.C), self.seed, self.sigma_value)
+        om = synth.offset_mask_f32(n, self.Ho, self.Wo, self.G, self.K, self.P, self.seed,
+                                   self.sigma_off, self.sigma_m, pad_fill,
+                                   self.integer_offsets)
+        out = [v, om]
+        if with_grad if with_grad is not None else self.direction == "bwd":
+            out.append(synth.grad_out_f32((n, self.Ho, self.Wo, self.C), self.seed, self.sigma_grad))
+        return tuple(out)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("c1_fwd_fp32_14x14", 1, 14, 14, 64, 4, "fp32", 0, 1.0, 1.5, 1.0, "fwd",
+                 note="small forward case"),
+        Workload("c2_fwd_fp32_56x56_b64", 64, 56, 56, 64, 4, "fp32", 2, 1.0, 2.0, 0.5, "fwd",
+                 note="FlashInternImage-T-like stage 1"),
+        Workload("c3a_fwd_fp16_56x56x64_g4", 64, 56, 56, 64, 4, "fp16", 30, 1.0, 2.0, 0.5, "fwd"),
+        Workload("c3b_fwd_fp16_28x28x128_g8", 64, 28, 28, 128, 8, "fp16", 31, 1.0, 2.0, 0.5, "fwd"),
+        Workload("c3c_fwd_fp16_14x14x256_g16", 64, 14, 14, 256, 16, "fp16", 32, 1.0, 2.0, 0.5, "fwd"),
+        Workload("c3d_fwd_fp16_7x7x512_g32", 64, 7, 7, 512, 32, "fp16", 33, 1.0, 2.0, 0.5, "fwd"),
+        Workload("c4_fwd_bf16_270x480_k9", 1, 270, 480, 256, 16, "bf16", 40, 1.0, 4.0, 1.0, "fwd",
+                 note="stride-4 map of a 1080x1920 frame"),
+        Workload("c4_fwd_bf16_270x480_k8", 1, 270, 480, 256, 16, "bf16", 41, 1.0, 4.0, 1.0, "fwd",
+                 remove_center=True),
+        Workload("c5_bwd_fp32_56x56_b16", 16, 56, 56, 64, 4, "fp32", 5, 1.0, 2.0, 0.5, "bwd",
+                 integer_offsets=True),
+    ]
+}
