@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the DCNv4 spatial aggregation on one MI355X.
+
+A step is one pass of the whole hot path -- forward (dcnv4_forward) and
+backward (dcnv4_backward: zero-fill, grad_value, grad_offset_mask) -- over one
+batch of the N=64, 56x56, C=64, G=4 (C'=16), 3x3 (K=9), fp32 workload (a
+FlashInternImage-T-like first stage; synthetic inputs: value ~ N(0,1),
+offsets ~ N(0,2) px, mask ~ N(0,0.5), grad_output ~ N(0,1)).
+
+`value` is sampled points per second, N*Ho*Wo*G*K*C' per step divided by the
+step time; every point is sampled by the forward and differentiated by the
+backward in the same step.  Inputs are resident in HBM before timing starts;
+several buffer sets are rotated so each step reads data that is not in the
+256 MB Infinity Cache.
+
+Per-call durations come from HIP events recorded on the stream the library
+launches on; the roofline object reports the dominant call.  The CPU oracle
+is timed on the host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DCNv4 fwd/bwd sampled points/s (N·H·W·G·K·C') + achieved HBM GB/s % of peak"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "dynamic_sparse_vision_amd", "csrc", "dcnv4_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str, call: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    the kernel source has not changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    entry = t.get("workloads", {}).get(workload, {}).get(call)
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
+
+
+def make_sets(w, nsets, dev):
+    import torch
+
+    from dynamic_sparse_vision_amd import synth
+
+    v32, om32, g32 = w.make_inputs(pad_fill=0.0, with_grad=True)
+    v_st, _ = synth.to_storage(v32, w.dtype)
+    om_st, _ = synth.to_storage(om32, w.dtype)
+    g_st, _ = synth.to_storage(g32, w.dtype)
+    base = dict(v=v_st.to(dev), om=om_st.to(dev), g=g_st.to(dev))
+    sets = []
+    for i in range(nsets):
+        s = {k: (t if i == 0 else t.clone()) for k, t in base.items()}
+        s["out"] = torch.empty((w.N, w.Ho, w.Wo, w.C), dtype=s["v"].dtype, device=dev)
+        s["gv"] = torch.empty_like(s["v"])
+        s["gom"] = torch.empty_like(s["om"])
+        sets.append(s)
+    return sets, (v32, om32, g32)
+
+
+def set_bytes(s):
+    return sum(t.numel() * t.element_size() for t in s.values())
+
+
+def cpu_baseline(w, arrays, seconds):
+    """The oracle as it stands, forward + backward, image by image until the
+    time budget is spent (a bounded sample of the same workload)."""
+    import oracle
+
+    v32, om32, g32 = arrays
+    nthreads = min(int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), os.cpu_count() or 1)
+    lib = oracle.load()
+    images = 0
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    while images < w.N and elapsed < seconds:
+        sl = slice(images, images + 1)
+        oracle.forward(v32[sl], om32[sl], nthreads=nthreads, lib=lib, **w.kwargs())
+        oracle.backward(v32[sl], om32[sl], g32[sl], nthreads=nthreads, lib=lib, **w.kwargs())
+        images += 1
+        elapsed = time.perf_counter() - t0
+    pts = images * w.Ho * w.Wo * w.G * w.K * w.Cg
+    return {"value": pts / elapsed, "unit": "sampled points/s", "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"{images} of {w.N} images of the same workload, forward + backward "
+                      f"(oracle threads parallel over output rows / images), {elapsed:.1f} s"}
+
+
+def time_configs(path, steps, warmup):
+    """One informational JSON line per workload (forward or backward alone),
+    with a 512 MB cache flush between calls; written to ``path``."""
+    import torch
+
+    from dynamic_sparse_vision_amd import dcnv4
+    from dynamic_sparse_vision_amd.workloads import WORKLOADS
+
+    dev = torch.device("cuda")
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    lines = []
+    for name, w in WORKLOADS.items():
+        sets, _ = make_sets(w, 1, dev)
+        s = sets[0]
+        kw = w.kwargs()
+        if w.direction == "fwd":
+            call = lambda: dcnv4.dcnv4_forward(s["v"], s["om"], s["out"], **kw)  # noqa: E731
+            nbytes = w.fwd_bytes()
+        else:
+            call = lambda: dcnv4.dcnv4_backward(s["v"], s["om"], s["g"], s["gv"], s["gom"], **kw)  # noqa: E731
+            nbytes = w.bwd_bytes() + w.N * w.H * w.W * w.C * 4
+        times = []
+        for i in range(warmup + steps):
+            flush.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call()
+            e1.record()
+            e1.synchronize()
+            if i >= warmup:
+                times.append(e0.elapsed_time(e1))
+        ms = statistics.median(times)
+        line = {"workload": name, "direction": w.direction, "dtype": w.dtype, "ms": ms,
+                "points_per_s": w.points / (ms * 1e-3), "compulsory_bytes": nbytes,
+                "gbps": nbytes / (ms * 1e-3) / 1e9,
+                "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        lines.append(line)
+        print(json.dumps(line), file=sys.stderr, flush=True)
+        del sets, s
+        torch.cuda.empty_cache()
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as f:
+        for line in lines:
+            f.write(json.dumps(line) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2_fwd_fp32_56x56_b64")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--configs-out", default=None,
+                    help="also time every workload alone and write JSON lines there")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: --gpus {args.gpus} (WORLD_SIZE {world}) requested, but this operator "
+              "library is measured on one GPU only; the multi-GPU path (batch sharding, no "
+              "communication inside the operator) is not built. Run with --gpus 1.",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+
+    from dynamic_sparse_vision_amd import dcnv4
+    from dynamic_sparse_vision_amd.workloads import WORKLOADS
+
+    dcnv4.load()  # fails loudly if the HIP library is missing
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda")
+    print(f"bench: generating {w.name}", file=sys.stderr, flush=True)
+    probe, arrays = make_sets(w, 1, dev)
+    per_set = set_bytes(probe[0])
+    nsets = max(2, -(-(768 * 1024 * 1024) // per_set))
+    del probe
+    sets, arrays = make_sets(w, nsets, dev)
+    kw = w.kwargs()
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        s = sets[i % nsets]
+        if ev is not None:
+            ev[0].record(stream)
+        dcnv4.dcnv4_forward(s["v"], s["om"], s["out"], **kw)
+        if ev is not None:
+            ev[1].record(stream)
+        dcnv4.dcnv4_backward(s["v"], s["om"], s["g"], s["gv"], s["gom"], **kw)
+        if ev is not None:
+            ev[2].record(stream)
+
+    print(f"bench: {nsets} buffer sets of {per_set / 1e6:.0f} MB; warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    fwd_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in events)
+    bwd_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in events)
+    print(f"bench: {ms_per_step:.4f} ms/step (forward {fwd_ms:.4f} ms, backward {bwd_ms:.4f} ms)",
+          file=sys.stderr, flush=True)
+
+    fwd_bytes = w.fwd_bytes()
+    bwd_bytes = w.bwd_bytes() + w.N * w.H * w.W * w.C * 4   # + the zero-fill of grad_value
+    calls = {"dcnv4_forward": (fwd_ms, fwd_bytes), "dcnv4_backward": (bwd_ms, bwd_bytes)}
+    dom = max(calls, key=lambda c: calls[c][0])
+    dom_ms, dom_bytes = calls[dom]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(w.name, dom),
+                "kernel": dom,
+                "algorithmic_bytes_per_launch": dom_bytes,
+                "avg_launch_ms": round(dom_ms, 5)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, arrays, args.cpu_seconds)
+
+    detail = {
+        "forward_ms": round(fwd_ms, 5), "backward_ms": round(bwd_ms, 5),
+        "forward_gbps": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1),
+        "backward_gbps": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1),
+        "forward_bytes": fwd_bytes, "backward_bytes": bwd_bytes,
+        "buffer_sets": nsets, "set_bytes": per_set,
+    }
+    line = {
+        "metric": METRIC,
+        "value": w.points / (ms_per_step * 1e-3),
+        "unit": "sampled points/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "fp32" else w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"DCNv4 forward+backward, N={w.N}, {w.H}x{w.W}, C={w.C}, G={w.G}, "
+                               f"C'={w.Cg}, K={w.K}, {w.dtype}",
+                   "N": w.N, "H": w.H, "W": w.W, "C": w.C, "G": w.G, "K": w.K,
+                   "points_per_step": w.points},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    if args.configs_out:
+        time_configs(args.configs_out, steps=max(20, args.steps), warmup=5)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+"""ctypes binding of libdcnv4.so (argument marshalling only).
+
+The names follow the C ABI in include/dcnv4.h.  ``dcnv4_forward`` and
+``dcnv4_backward`` take torch tensors (device memory and the current stream
+come from torch) and pass raw pointers and sizes to the library; every step
+of the operator runs in the library's HIP kernels.  There is no fallback:
+if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdcnv4.so")
+
+DCNV4_OK = 0
+STATUS = {0: "DCNV4_OK", -1: "DCNV4_ERR_NULL", -2: "DCNV4_ERR_SHAPE", -3: "DCNV4_ERR_PARAM",
+          -4: "DCNV4_ERR_DTYPE", -5: "DCNV4_ERR_ALIGN", -6: "DCNV4_ERR_UNSUPPORTED",
+          -7: "DCNV4_ERR_OVERFLOW", -8: "DCNV4_ERR_HIP"}
+DTYPE_CODES = {"fp32": 0, "fp16": 1, "bf16": 2}
+
+_lib = None
+
+
+class Dcnv4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load()
+        msg = lib.dcnv4_status_string(status).decode()
+        hip = lib.dcnv4_last_hip_error().decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({msg}){' ' + hip if hip else ''}")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libdcnv4.so from the package directory (built by
+    ``python -m dynamic_sparse_vision_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m dynamic_sparse_vision_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i, f, p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    geo = [i] * 13 + [f, i, i, i, p]  # N H W kh kw sh sw ph pw dh dw G Cg | scale | rc P dtype | stream
+    lib.dcnv4_forward.argtypes = [p, p, p] + geo
+    lib.dcnv4_forward.restype = i
+    lib.dcnv4_backward.argtypes = [p, p, p, p, p] + geo
+    lib.dcnv4_backward.restype = i
+    lib.dcnv4_output_size.argtypes = [i] * 10 + [ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.dcnv4_output_size.restype = i
+    lib.dcnv4_om_channels.argtypes = [i, i, i, i]
+    lib.dcnv4_om_channels.restype = i
+    lib.dcnv4_status_string.argtypes = [i]
+    lib.dcnv4_status_string.restype = ctypes.c_char_p
+    lib.dcnv4_last_hip_error.argtypes = []
+    lib.dcnv4_last_hip_error.restype = ctypes.c_char_p
+    lib.dcnv4_abi_version.argtypes = []
+    lib.dcnv4_abi_version.restype = i
+    _lib = lib
+    return lib
+
+
+def dcnv4_abi_version() -> int:
+    return load().dcnv4_abi_version()
+
+
+def dcnv4_status_string(status: int) -> str:
+    return load().dcnv4_status_string(status).decode()
+
+
+def dcnv4_last_hip_error() -> str:
+    return load().dcnv4_last_hip_error().decode()
+
+
+def dcnv4_output_size(H, W, kernel_h=3, kernel_w=3, stride_h=1, stride_w=1, pad_h=1, pad_w=1,
+                      dilation_h=1, dilation_w=1):
+    ho, wo = ctypes.c_int(), ctypes.c_int()
+    st = load().dcnv4_output_size(H, W, kernel_h, kernel_w, stride_h, stride_w, pad_h, pad_w,
+                                  dilation_h, dilation_w, ctypes.byref(ho), ctypes.byref(wo))
+    if st != DCNV4_OK:
+        raise Dcnv4Error(st, "dcnv4_output_size")
+    return ho.value, wo.value
+
+
+def dcnv4_om_channels(group, kernel_h=3, kernel_w=3, remove_center=False) -> int:
+    st = load().dcnv4_om_channels(group, kernel_h, kernel_w, int(bool(remove_center)))
+    if st < 0:
+        raise Dcnv4Error(st, "dcnv4_om_channels")
+    return st
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _check(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (channel-last, dense)")
+
+
+def _stream_ptr(stream):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def dcnv4_forward(value, offset_mask, output, *, kernel_h=3, kernel_w=3, stride_h=1, stride_w=1,
+                  pad_h=1, pad_w=1, dilation_h=1, dilation_w=1, group, group_channels,
+                  offset_scale=1.0, remove_center=False, stream=None) -> None:
+    """value (N,H,W,C), offset_mask (N,Ho,Wo,P), output (N,Ho,Wo,C): device
+    tensors of one dtype.  Enqueues the forward on ``stream`` (default: torch's
+    current stream)."""
+    for t, nm in ((value, "value"), (offset_mask, "offset_mask"), (output, "output")):
+        _check(t, nm)
+        if t.dtype != value.dtype:
+            raise TypeError(f"{nm} dtype {t.dtype} != value dtype {value.dtype}")
+    N, H, W, C = value.shape
+    st = load().dcnv4_forward(
+        ctypes.c_void_p(value.data_ptr()), ctypes.c_void_p(offset_mask.data_ptr()),
+        ctypes.c_void_p(output.data_ptr()), N, H, W, kernel_h, kernel_w, stride_h, stride_w,
+        pad_h, pad_w, dilation_h, dilation_w, group, group_channels, float(offset_scale),
+        int(bool(remove_center)), offset_mask.shape[-1], _dtype_code(value), _stream_ptr(stream))
+    if st != DCNV4_OK:
+        raise Dcnv4Error(st, "dcnv4_forward")
+
+
+def dcnv4_backward(value, offset_mask, grad_output, grad_value, grad_offset_mask, *, kernel_h=3,
+                   kernel_w=3, stride_h=1, stride_w=1, pad_h=1, pad_w=1, dilation_h=1,
+                   dilation_w=1, group, group_channels, offset_scale=1.0, remove_center=False,
+                   stream=None) -> None:
+    """Backward into caller-allocated grad_value (N,H,W,C) and
+    grad_offset_mask (N,Ho,Wo,P) (both overwritten)."""
+    for t, nm in ((value, "value"), (offset_mask, "offset_mask"), (grad_output, "grad_output"),
+                  (grad_value, "grad_value"), (grad_offset_mask, "grad_offset_mask")):
+        _check(t, nm)
+        if t.dtype != value.dtype:
+            raise TypeError(f"{nm} dtype {t.dtype} != value dtype {value.dtype}")
+    N, H, W, C = value.shape
+    st = load().dcnv4_backward(
+        ctypes.c_void_p(value.data_ptr()), ctypes.c_void_p(offset_mask.data_ptr()),
+        ctypes.c_void_p(grad_output.data_ptr()), ctypes.c_void_p(grad_value.data_ptr()),
+        ctypes.c_void_p(grad_offset_mask.data_ptr()), N, H, W, kernel_h, kernel_w, stride_h,
+        stride_w, pad_h, pad_w, dilation_h, dilation_w, group, group_channels,
+        float(offset_scale), int(bool(remove_center)), offset_mask.shape[-1],
+        _dtype_code(value), _stream_ptr(stream))
+    if st != DCNV4_OK:
+        raise Dcnv4Error(st, "dcnv4_backward")
+
+
+def forward(value, offset_mask, **params):
+    """Allocate the output with torch and call dcnv4_forward."""
+    import torch
+
+    N, H, W, C = value.shape
+    Ho, Wo = dcnv4_output_size(H, W, params.get("kernel_h", 3), params.get("kernel_w", 3),
+                               params.get("stride_h", 1), params.get("stride_w", 1),
+                               params.get("pad_h", 1), params.get("pad_w", 1),
+                               params.get("dilation_h", 1), params.get("dilation_w", 1))
+    out = torch.empty((N, Ho, Wo, C), dtype=value.dtype, device=value.device)
+    dcnv4_forward(value, offset_mask, out, **params)
+    return out
+
+
+def backward(value, offset_mask, grad_output, **params):
+    """Allocate grad_value / grad_offset_mask with torch and call dcnv4_backward."""
+    import torch
+
+    gv = torch.empty_like(value)
+    gom = torch.empty_like(offset_mask)
+    dcnv4_backward(value, offset_mask, grad_output, gv, gom, **params)
+    return gv, gom

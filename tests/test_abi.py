@@ -1,0 +1,171 @@
+"""The C ABI of libdcnv4.so on the CPU: the library loads, exports every
+symbol include/dcnv4.h declares, and rejects bad arguments before any HIP
+call.  No call here reaches a kernel launch: each one fails validation (the
+pointers are fake, 16-byte aligned addresses that are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from dynamic_sparse_vision_amd import dcnv4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dcnv4.h")
+
+OK, NULL, SHAPE, PARAM, DTYPE, ALIGN, UNSUP, OVERFLOW, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+# fake device addresses: aligned, far apart, never dereferenced
+A, B, Cp, D, E = (ctypes.c_void_p(x) for x in (0x100000000, 0x200000000, 0x300000000,
+                                               0x400000000, 0x500000000))
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"DCNV4_API\s+[\w\s\*]+?\b(dcnv4_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_symbols() == sorted([
+        "dcnv4_abi_version", "dcnv4_status_string", "dcnv4_last_hip_error",
+        "dcnv4_output_size", "dcnv4_om_channels", "dcnv4_forward", "dcnv4_backward"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dcnv4.load()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", dcnv4.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (dcnv4_\w+)", out))
+    assert set(declared_symbols()) <= exported
+    # nothing else with the prefix leaks out
+    assert exported == set(declared_symbols())
+
+
+def test_version_and_status_strings():
+    lib = dcnv4.load()
+    assert lib.dcnv4_abi_version() == 1
+    for st in (OK, NULL, SHAPE, PARAM, DTYPE, ALIGN, UNSUP, OVERFLOW, HIP):
+        assert lib.dcnv4_status_string(st)
+    assert lib.dcnv4_status_string(12345) == b"unknown status"
+    assert lib.dcnv4_last_hip_error() == b""
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((56, 56, 3, 3, 1, 1, 1, 1, 1, 1), (OK, 56, 56)),
+    ((14, 14, 3, 3, 2, 2, 1, 1, 1, 1), (OK, 7, 7)),
+    ((9, 8, 5, 3, 1, 2, 4, 1, 2, 1), (OK, 9, 4)),
+    ((7, 7, 5, 5, 1, 1, 0, 0, 2, 2), (SHAPE, None, None)),
+    ((7, 7, 0, 3, 1, 1, 1, 1, 1, 1), (PARAM, None, None)),
+    ((0, 7, 3, 3, 1, 1, 1, 1, 1, 1), (SHAPE, None, None)),
+])
+def test_output_size(args, expect):
+    lib = dcnv4.load()
+    ho, wo = ctypes.c_int(-1), ctypes.c_int(-1)
+    st = lib.dcnv4_output_size(*args, ctypes.byref(ho), ctypes.byref(wo))
+    assert st == expect[0]
+    if st == OK:
+        assert (ho.value, wo.value) == expect[1:]
+    assert lib.dcnv4_output_size(*args, None, None) == NULL
+
+
+def test_om_channels():
+    lib = dcnv4.load()
+    assert lib.dcnv4_om_channels(4, 3, 3, 0) == 112       # 108 -> 112
+    assert lib.dcnv4_om_channels(16, 3, 3, 0) == 432
+    assert lib.dcnv4_om_channels(16, 3, 3, 1) == 384
+    assert lib.dcnv4_om_channels(32, 3, 3, 0) == 864
+    assert lib.dcnv4_om_channels(1, 3, 3, 0) == 32        # 27 -> 32
+    assert lib.dcnv4_om_channels(1, 2, 2, 1) == PARAM     # even kernel with remove_center
+    assert lib.dcnv4_om_channels(0, 3, 3, 0) == PARAM
+
+
+BASE = dict(N=2, H=8, W=8, kh=3, kw=3, sh=1, sw=1, ph=1, pw=1, dh=1, dw=1, G=4, Cg=16,
+            scale=1.0, rc=0, P=112, dtype=0)
+
+
+def fwd(ptrs=(A, B, Cp), **over):
+    a = dict(BASE, **over)
+    return dcnv4.load().dcnv4_forward(*ptrs, a["N"], a["H"], a["W"], a["kh"], a["kw"], a["sh"],
+                                      a["sw"], a["ph"], a["pw"], a["dh"], a["dw"], a["G"], a["Cg"],
+                                      a["scale"], a["rc"], a["P"], a["dtype"], None)
+
+
+def bwd(ptrs=(A, B, Cp, D, E), **over):
+    a = dict(BASE, **over)
+    return dcnv4.load().dcnv4_backward(*ptrs, a["N"], a["H"], a["W"], a["kh"], a["kw"], a["sh"],
+                                       a["sw"], a["ph"], a["pw"], a["dh"], a["dw"], a["G"],
+                                       a["Cg"], a["scale"], a["rc"], a["P"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("call", [fwd, bwd], ids=["forward", "backward"])
+@pytest.mark.parametrize("over,expect", [
+    (dict(dtype=3), DTYPE),
+    (dict(dtype=-1), DTYPE),
+    (dict(N=-1), SHAPE),
+    (dict(H=0), SHAPE),
+    (dict(W=-3), SHAPE),
+    (dict(kh=0), PARAM),
+    (dict(sw=0), PARAM),
+    (dict(ph=-1), PARAM),
+    (dict(dw=0), PARAM),
+    (dict(G=0), PARAM),
+    (dict(Cg=0), PARAM),
+    (dict(rc=2), PARAM),
+    (dict(rc=1, kh=2, P=112), PARAM),              # remove_center needs odd kernels
+    (dict(rc=1, kh=1, kw=1, P=8), PARAM),          # ... and more than one point
+    (dict(scale=float("nan")), PARAM),
+    (dict(scale=float("inf")), PARAM),
+    (dict(P=108), PARAM),                          # not a multiple of 8
+    (dict(P=104), PARAM),                          # fewer than 3*G*K
+    (dict(H=2, W=2, ph=0, pw=0), SHAPE),           # empty output
+    (dict(Cg=2), UNSUP),                           # 8 bytes: not a 128-bit vector
+    (dict(H=1 << 16, W=1 << 14, Cg=16, G=4), OVERFLOW),   # one image > 2^31 bytes
+])
+def test_rejected_before_any_device_work(call, over, expect):
+    assert call(**over) == expect
+
+
+def test_forward_pointer_and_layout_checks():
+    assert fwd(ptrs=(None, B, Cp)) == NULL
+    assert fwd(ptrs=(A, None, Cp)) == NULL
+    assert fwd(ptrs=(A, B, None)) == NULL
+    assert fwd(ptrs=(ctypes.c_void_p(0x100000008), B, Cp)) == ALIGN
+    assert fwd(ptrs=(A, B, ctypes.c_void_p(0x100000010))) == PARAM      # output overlaps value
+    assert fwd(ptrs=(A, B, ctypes.c_void_p(0x200000000 + 32))) == PARAM  # ... overlaps offset_mask
+    assert fwd(dtype=1, Cg=4) == UNSUP                                    # 8 bytes of fp16
+    assert fwd(N=0, ptrs=(None, None, None)) == OK                        # empty batch: no-op
+
+
+def test_backward_pointer_and_dtype_checks():
+    assert bwd(dtype=1) == UNSUP
+    assert bwd(dtype=2) == UNSUP
+    for i in range(5):
+        ptrs = [A, B, Cp, D, E]
+        ptrs[i] = None
+        assert bwd(ptrs=tuple(ptrs)) == NULL
+    assert bwd(ptrs=(A, B, Cp, ctypes.c_void_p(0x400000004), E)) == ALIGN
+    assert bwd(ptrs=(A, B, Cp, ctypes.c_void_p(0x100000040), E)) == PARAM  # grad_value overlaps value
+    assert bwd(ptrs=(A, B, Cp, D, ctypes.c_void_p(0x400000010))) == PARAM  # grad outputs overlap
+    assert bwd(Cg=12) == UNSUP        # 3 lanes of 4 channels: not a power of two
+    assert bwd(N=0, ptrs=(None,) * 5) == OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    v = torch.zeros(1, 4, 4, 64)
+    om = torch.zeros(1, 4, 4, 112)
+    with pytest.raises(ValueError):
+        dcnv4.dcnv4_forward(v, om, torch.zeros_like(v), group=4, group_channels=16)
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="only meaningful where no GPU device exists")
+def test_valid_call_without_a_device_reports_hip_error():
+    # every argument is valid, so the library reaches the HIP runtime, which
+    # has no device here: the call must fail with DCNV4_ERR_HIP, not crash
+    st = fwd()
+    assert st == HIP
+    assert dcnv4.load().dcnv4_last_hip_error() != b""

@@ -1,0 +1,219 @@
+"""HIP path against the CPU oracle, element by element, through the C ABI.
+
+Tolerances (elementwise, ref = oracle in double on the same rounded inputs):
+  fp32       |gpu - ref| <= 1e-5 + 1e-5 * |ref|       (outputs and all gradients)
+  fp16/bf16  |gpu - ref| <= 2e-2 + ulp_dtype(|ref|)   (the storage rounding of
+             the output alone can exceed 2e-2 for bf16 once |y| >= 8; the plain
+             max error and the count above 2e-2 are printed)
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dynamic_sparse_vision_amd import dcnv4, synth
+from dynamic_sparse_vision_amd.workloads import WORKLOADS, Workload
+
+pytestmark = pytest.mark.gpu
+
+TORCH_DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def ulp(ref, dtype):
+    a = np.abs(ref)
+    if dtype == "fp16":
+        return np.spacing(a.astype(np.float16)).astype(np.float64)
+    if dtype == "bf16":
+        e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+        return 2.0 ** (e - 7)
+    return np.zeros_like(a)
+
+
+def check(gpu, ref, dtype, what):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    assert np.isfinite(gpu).all(), f"{what}: non-finite GPU values"
+    err = np.abs(gpu - ref)
+    if dtype == "fp32":
+        bound = 1e-5 + 1e-5 * np.abs(ref)
+    else:
+        bound = 2e-2 + ulp(ref, dtype)
+    bad = err > bound
+    say(f"  {what}: max|err| {err.max():.3e}  n>2e-2 {int((err > 2e-2).sum())}  "
+        f"n>bound {int(bad.sum())} of {err.size}")
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements out of tolerance, first at {np.argwhere(bad)[0]}"
+
+
+def device_inputs(w: Workload, N=None, pad_fill=float("nan"), with_grad=False):
+    arrs = w.make_inputs(pad_fill=pad_fill, N=N, with_grad=with_grad)
+    v_st, v_ref = synth.to_storage(arrs[0], w.dtype)
+    om_st, om_ref = synth.to_storage(arrs[1], w.dtype)
+    out = dict(v=v_st.cuda(), om=om_st.cuda(), v_ref=v_ref, om_ref=om_ref)
+    if with_grad:
+        g_st, g_ref = synth.to_storage(arrs[2], w.dtype)
+        out.update(g=g_st.cuda(), g_ref=g_ref)
+    return out
+
+
+FWD_WORKLOADS = [n for n, w in WORKLOADS.items() if w.direction == "fwd"]
+
+
+@pytest.mark.parametrize("name", FWD_WORKLOADS)
+def test_forward_workload(name):
+    w = WORKLOADS[name]
+    say(f"[forward] {name} N={w.N} {w.H}x{w.W}x{w.C} G={w.G} K={w.K} {w.dtype}")
+    d = device_inputs(w)
+    out = dcnv4.forward(d["v"], d["om"], **w.kwargs())
+    torch.cuda.synchronize()
+    ref = oracle.forward(d["v_ref"], d["om_ref"], **w.kwargs())
+    check(out.float().cpu().numpy(), ref, w.dtype, name)
+
+
+def _backward_case(w, N=None):
+    d = device_inputs(w, N=N, with_grad=True)
+    gv, gom = dcnv4.backward(d["v"], d["om"], d["g"], **w.kwargs())
+    torch.cuda.synchronize()
+    rgv, rgom = oracle.backward(d["v_ref"], d["om_ref"], d["g_ref"], **w.kwargs())
+    return gv.cpu().numpy(), gom.cpu().numpy(), rgv, rgom
+
+
+def test_backward_workload():
+    w = WORKLOADS["c5_bwd_fp32_56x56_b16"]
+    say(f"[backward] {w.name} N={w.N} {w.H}x{w.W}x{w.C} G={w.G} (integer offsets mixed in)")
+    gv, gom, rgv, rgom = _backward_case(w)
+    check(gv, rgv, "fp32", "grad_value")
+    check(gom, rgom, "fp32", "grad_offset_mask")
+    assert np.all(gom[..., 3 * w.G * w.K:] == 0)
+
+
+def test_backward_at_benchmark_scale():
+    """The benchmark step (forward + backward of the N=64, 56x56x64, G=4 fp32
+    workload), compared in full."""
+    w = WORKLOADS["c2_fwd_fp32_56x56_b64"]
+    say(f"[backward] {w.name} N={w.N} full")
+    gv, gom, rgv, rgom = _backward_case(w)
+    check(gv, rgv, "fp32", "grad_value")
+    check(gom, rgom, "fp32", "grad_offset_mask")
+
+
+def _wl(name, dtype, N=2, H=9, W=11, C=32, G=2, **kw):
+    base = dict(seed=77, sigma_value=1.0, sigma_off=2.0, sigma_m=0.7, direction="fwd")
+    base.update(kw)
+    return Workload(name, N, H, W, C, G, dtype, **base)
+
+
+COVERAGE = [
+    # ragged pixel tails, several tiles, odd group counts, other DP choices
+    _wl("g3_c8_fp32", "fp32", N=3, H=13, W=7, C=24, G=3),
+    _wl("g1_c4_fp32", "fp32", N=1, H=17, W=19, C=4, G=1),
+    _wl("g2_c32_fp32", "fp32", N=2, H=10, W=9, C=64, G=2),
+    _wl("g5_c16_fp16", "fp16", N=2, H=11, W=13, C=80, G=5),
+    _wl("g2_c8_bf16", "bf16", N=2, H=6, W=23, C=16, G=2),
+    _wl("g8_c32_bf16", "bf16", N=1, H=12, W=12, C=256, G=8),
+    # geometry: dilation, stride, larger and rectangular grids, remove_center
+    _wl("dil2_fp32", "fp32", N=2, H=12, W=12, C=32, G=2, dilation=(2, 2), pad=(2, 2)),
+    _wl("stride2_fp16", "fp16", N=2, H=15, W=14, C=32, G=2, stride=(2, 2)),
+    _wl("k5x5_rc_fp32", "fp32", N=1, H=11, W=10, C=32, G=2, kernel=(5, 5), pad=(2, 2),
+        remove_center=True),
+    _wl("k3x5_s12_d21_bf16", "bf16", N=2, H=13, W=12, C=32, G=2, kernel=(3, 5), pad=(2, 1),
+        stride=(1, 2), dilation=(2, 1)),
+    _wl("k1x1_fp32", "fp32", N=2, H=5, W=6, C=32, G=2, kernel=(1, 1), pad=(0, 0)),
+    _wl("scale_half_fp32", "fp32", N=2, H=9, W=9, C=32, G=2, offset_scale=0.5),
+    _wl("far_offsets_fp16", "fp16", N=1, H=8, W=8, C=32, G=2, sigma_off=40.0),
+    _wl("tiny_1x1_image_fp32", "fp32", N=3, H=1, W=1, C=32, G=2),
+    _wl("int_offsets_fp32", "fp32", N=2, H=7, W=9, C=32, G=2, integer_offsets=True),
+]
+
+
+@pytest.mark.parametrize("w", COVERAGE, ids=lambda w: w.name)
+def test_forward_coverage(w):
+    say(f"[forward] {w.name}")
+    d = device_inputs(w)
+    out = dcnv4.forward(d["v"], d["om"], **w.kwargs())
+    torch.cuda.synchronize()
+    ref = oracle.forward(d["v_ref"], d["om_ref"], **w.kwargs())
+    check(out.float().cpu().numpy(), ref, w.dtype, w.name)
+
+
+BWD_COVERAGE = [w for w in COVERAGE if w.dtype == "fp32" and w.Cg % 4 == 0
+                and ((w.Cg // 4) & (w.Cg // 4 - 1)) == 0]
+
+
+@pytest.mark.parametrize("w", BWD_COVERAGE, ids=lambda w: w.name)
+def test_backward_coverage(w):
+    say(f"[backward] {w.name}")
+    gv, gom, rgv, rgom = _backward_case(w)
+    check(gv, rgv, "fp32", f"{w.name} grad_value")
+    check(gom, rgom, "fp32", f"{w.name} grad_offset_mask")
+
+
+def test_forward_is_deterministic_and_ignores_padding():
+    w = WORKLOADS["c3b_fwd_fp16_28x28x128_g8"]
+    say(f"[forward] determinism / padding {w.name} N=8")
+    d = device_inputs(w, N=8)
+    y1 = dcnv4.forward(d["v"], d["om"], **w.kwargs())
+    y2 = dcnv4.forward(d["v"], d["om"], **w.kwargs())
+    d0 = device_inputs(w, N=8, pad_fill=0.0)
+    y3 = dcnv4.forward(d0["v"], d0["om"], **w.kwargs())
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert torch.equal(y1, y3)
+
+
+def test_guard_bands_untouched():
+    """Outputs written through views into larger canary-filled buffers: no
+    byte outside the views changes."""
+    w = _wl("guard_fp32", "fp32", N=2, H=9, W=10, C=32, G=2)
+    say("[forward/backward] guard bands")
+    d = device_inputs(w, with_grad=True)
+    canary = 12345.0
+    pad = 64
+    n_out = w.N * w.Ho * w.Wo * w.C
+    buf = torch.full((n_out + 2 * pad,), canary, device="cuda")
+    out = buf[pad:pad + n_out].view(w.N, w.Ho, w.Wo, w.C)
+    dcnv4.dcnv4_forward(d["v"], d["om"], out, **w.kwargs())
+    n_v = d["v"].numel()
+    n_om = d["om"].numel()
+    gbuf = torch.full((n_v + n_om + 4 * pad,), canary, device="cuda")
+    gv = gbuf[pad:pad + n_v].view_as(d["v"])
+    gom = gbuf[3 * pad + n_v:3 * pad + n_v + n_om].view_as(d["om"])
+    dcnv4.dcnv4_backward(d["v"], d["om"], d["g"], gv, gom, **w.kwargs())
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == canary) and torch.all(buf[pad + n_out:] == canary)
+    assert torch.all(gbuf[:pad] == canary)
+    assert torch.all(gbuf[pad + n_v:3 * pad + n_v] == canary)
+    assert torch.all(gbuf[3 * pad + n_v + n_om:] == canary)
+    ref = oracle.forward(d["v_ref"], d["om_ref"], **w.kwargs())
+    check(out.cpu().numpy(), ref, "fp32", "guarded forward")
+
+
+def test_empty_batch_and_side_stream():
+    w = _wl("stream_fp16", "fp16", N=2, H=7, W=8, C=32, G=2)
+    say("[forward] empty batch, side stream")
+    d = device_inputs(w)
+    empty_v = d["v"][:0]
+    empty_om = d["om"][:0]
+    assert dcnv4.forward(empty_v, empty_om, **w.kwargs()).shape[0] == 0
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y = dcnv4.forward(d["v"], d["om"], **w.kwargs())
+    s.synchronize()
+    ref = oracle.forward(d["v_ref"], d["om_ref"], **w.kwargs())
+    check(y.float().cpu().numpy(), ref, "fp16", "side stream")
+
+
+def test_backward_repeatability():
+    w = WORKLOADS["c5_bwd_fp32_56x56_b16"]
+    say(f"[backward] repeatability {w.name} N=4")
+    d = device_inputs(w, N=4, with_grad=True)
+    gv1, gom1 = dcnv4.backward(d["v"], d["om"], d["g"], **w.kwargs())
+    gv2, gom2 = dcnv4.backward(d["v"], d["om"], d["g"], **w.kwargs())
+    torch.cuda.synchronize()
+    assert torch.equal(gom1, gom2)            # no atomics: bitwise stable
+    diff = (gv1 - gv2).abs().max().item()     # atomics: order may differ
+    assert diff <= 1e-5, diff
