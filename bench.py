@@ -159,6 +159,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--configs-out", default=None,
                     help="also time every workload alone and write JSON lines there")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -262,6 +264,13 @@ def main():
     }
     if args.configs_out:
         time_configs(args.configs_out, steps=max(20, args.steps), warmup=5)
+    if args.copy_probe:
+        # a copy kernel of known size: 256 MiB read + 256 MiB written per launch
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     print(json.dumps(line), flush=True)
 
 
