@@ -32,13 +32,17 @@ sys.path.insert(0, ROOT)
 
 METRIC = "DCNv4 fwd/bwd sampled points/s (N·H·W·G·K·C') + achieved HBM GB/s % of peak"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "dynamic_sparse_vision_amd", "csrc", "dcnv4_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "dynamic_sparse_vision_amd", "csrc", n) for n in
+               ("dcnv4_device.h", "dcnv4_kernels.hip", "dcnv4_tiled.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str, call: str):

@@ -200,6 +200,165 @@ int plan_backward(const Problem &p, Plan *plan)
     return DCNV4_OK;
 }
 
+namespace {
+
+bool pow2(int v)
+{
+    return v > 0 && (v & (v - 1)) == 0;
+}
+
+int ilog2(int v)
+{
+    int s = 0;
+    while ((1 << s) < v)
+        ++s;
+    return s;
+}
+
+// Output tile for halo radius R: th x tw pixels with `lanes` threads per
+// pixel, at most 256 threads and at least two waves (unless the map is
+// smaller).  Cost, in 16-byte LDS operations: corner gathers of every wave
+// slot (partial waves count in full) plus three per staged region vector.
+void choose_out_tile(const Problem &p, int lanes, int nvl, int nvp, int R, int *th, int *tw)
+{
+    const long min_threads = std::min<long>(128, (long)p.Ho * p.Wo * lanes);
+    double best = -1;
+    for (int w = 1; w <= 64 && w <= p.Wo; ++w) {
+        for (int h = 1; h <= 64 && h <= p.Ho; ++h) {
+            const int threads = h * w * lanes;
+            if (threads > 256)
+                break;
+            if (threads < min_threads)
+                continue;
+            const double blocks = (double)((p.Ho + h - 1) / h) * ((p.Wo + w - 1) / w);
+            const double rh = (h - 1) * p.sh + (p.kh - 1) * p.dh + 2 * R + 2;
+            const double rw = (w - 1) * p.sw + (p.kw - 1) * p.dw + 2 * R + 2;
+            const double cost = blocks * ((threads + 63) / 64) * 64.0 * p.K * 4 * nvl + blocks * rh * rw * nvp * 3;
+            if (best < 0 || cost < best) {
+                best = cost;
+                *th = h;
+                *tw = w;
+            }
+        }
+    }
+}
+
+// Cell tile of the grad_value kernel (one thread per cell, at most 256):
+// minimise the samples evaluated, i.e. blocks x source pixels x K, plus a
+// fixed per-block cost.
+void choose_cell_tile(const Problem &p, int R, int *ch, int *cw)
+{
+    double best = -1;
+    for (int w = 1; w <= 256 && w <= p.W; ++w) {
+        for (int h = 1; h <= 256 && h <= p.H; ++h) {
+            if (h * w > 256)
+                break;
+            const double blocks = (double)((p.H + h - 1) / h) * ((p.W + w - 1) / w);
+            const double sh = (double)(h + (p.kh - 1) * p.dh + 2 * R + 2) / p.sh + 1;
+            const double sw = (double)(w + (p.kw - 1) * p.dw + 2 * R + 2) / p.sw + 1;
+            const double cost = blocks * (sh * sw * p.K + 2048);
+            if (best < 0 || cost < best) {
+                best = cost;
+                *ch = h;
+                *cw = w;
+            }
+        }
+    }
+}
+
+// Fill the LDS region geometry for halo radius R; returns total LDS bytes.
+int tile_lds(const Problem &p, TilePlan *tp, int R, int elem)
+{
+    tp->R = R;
+    tp->rh = (tp->th - 1) * p.sh + (p.kh - 1) * p.dh + 2 * R + 2;
+    tp->rw = (tp->tw - 1) * p.sw + (p.kw - 1) * p.dw + 2 * R + 2;
+    const int om = tp->th * tp->tw * 3 * p.K * elem;
+    tp->om_lds_bytes = (om + 15) / 16 * 16;
+    tp->lds_bytes = tp->om_lds_bytes + tp->rh * tp->rw * tp->nvp * 16;
+    return tp->lds_bytes;
+}
+
+constexpr int kTiledMaxLds = 80 * 1024;
+
+int plan_tiled_common(const Problem &p, int elem, int r_max, int lds_budget, TilePlan *tp)
+{
+    if ((p.Cg * elem) % 16 != 0)
+        return DCNV4_ERR_UNSUPPORTED;
+    tp->nvp = p.Cg * elem / 16;
+    if (!pow2(tp->nvp))
+        return DCNV4_ERR_UNSUPPORTED;
+    int dp = 0;
+    for (int cand : {16, 8, 4}) {
+        if (p.Cg % cand == 0 && (cand * elem) % 16 == 0) {
+            dp = cand;
+            break;
+        }
+    }
+    if (dp == 0)
+        return DCNV4_ERR_UNSUPPORTED;
+    tp->dp = dp;
+    tp->lanes = p.Cg / dp;
+    if (!pow2(tp->lanes) || tp->lanes > 64)
+        return DCNV4_ERR_UNSUPPORTED;
+    // 16 LDS banks of 16 bytes: rotate the vector index by higher pixel bits
+    tp->swz_mask = (tp->nvp >= 2) ? (tp->nvp < 16 ? tp->nvp : 16) - 1 : 0;
+    tp->swz_shift = tp->nvp < 16 ? ilog2(16 / tp->nvp) : 0;
+    const int nvl = dp * elem / 16;
+    // the largest halo radius whose best tile fits the LDS budget
+    for (int R = r_max; R >= 1; --R) {
+        choose_out_tile(p, tp->lanes, nvl, tp->nvp, R, &tp->th, &tp->tw);
+        if (tile_lds(p, tp, R, elem) <= lds_budget) {
+            // whole waves: the kernels' staging loops stride by 64 lanes
+            tp->threads = (tp->th * tp->tw * tp->lanes + 63) / 64 * 64;
+            tp->tiles_y = (p.Ho + tp->th - 1) / tp->th;
+            tp->tiles_x = (p.Wo + tp->tw - 1) / tp->tw;
+            tp->images_per_launch = 0;
+            return DCNV4_OK;
+        }
+    }
+    return DCNV4_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+int plan_forward_tiled(const Problem &p, TilePlan *tp)
+{
+    *tp = TilePlan{};
+    // fp32 rows are twice as wide: a smaller halo keeps two blocks per CU
+    const int r_max = p.elem == 4 ? 5 : 8;
+    const int budget = p.elem == 4 ? kTiledMaxLds : 64 * 1024;
+    int st = plan_tiled_common(p, p.elem, r_max, budget, tp);
+    if (st != DCNV4_OK)
+        return st;
+    tp->images_per_launch = (int)(kMaxBytesPerLaunch / image_bytes_max(p, false));
+    return DCNV4_OK;
+}
+
+int plan_backward_tiled(const Problem &p, TilePlan *tp)
+{
+    *tp = TilePlan{};
+    if (p.dtype != DCNV4_FP32)
+        return DCNV4_ERR_UNSUPPORTED;
+    if (p.Cg != 4 && p.Cg != 8 && p.Cg != 16 && p.Cg != 32)
+        return DCNV4_ERR_UNSUPPORTED;
+    int st = plan_tiled_common(p, 4, 5, kTiledMaxLds, tp);
+    if (st != DCNV4_OK)
+        return st;
+    // cell tiles for grad_value: one thread per cell, at most 256 cells
+    choose_cell_tile(p, tp->R, &tp->ch, &tp->cw);
+    tp->ctiles_y = (p.H + tp->ch - 1) / tp->ch;
+    tp->ctiles_x = (p.W + tp->cw - 1) / tp->cw;
+    // a batch holds at most 1024 samples (4 per thread), i.e. 4096 corner
+    // records, and at most 128 source pixels (their grad_out rows sit in LDS)
+    tp->src_batch = std::min(1024 / p.K, 128);
+    if (tp->src_batch < 1)
+        return DCNV4_ERR_UNSUPPORTED;
+    tp->max_records = 4096;
+    tp->splat_lds_bytes = 3 * 256 * 4 + 16 + tp->max_records * 8 + tp->src_batch * p.Cg * 4;
+    tp->images_per_launch = (int)(kMaxBytesPerLaunch / image_bytes_max(p, true));
+    return DCNV4_OK;
+}
+
 }  // namespace dcnv4
 
 using namespace dcnv4;
@@ -294,8 +453,10 @@ int dcnv4_forward(const void *value, const void *offset_mask, void *output, int 
     if (st != DCNV4_OK)
         return st;
     Plan plan;
+    TilePlan tp;
+    const bool tiled = plan_forward_tiled(p, &tp) == DCNV4_OK;
     st = plan_forward(p, &plan);
-    if (st != DCNV4_OK)
+    if (st != DCNV4_OK && !tiled)
         return st;
     if (N == 0)
         return DCNV4_OK;
@@ -310,12 +471,14 @@ int dcnv4_forward(const void *value, const void *offset_mask, void *output, int 
     if (ranges_overlap(output, no, value, nv) || ranges_overlap(output, no, offset_mask, nom))
         return DCNV4_ERR_PARAM;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    for (int n0 = 0; n0 < N; n0 += plan.images_per_launch) {
+    const int per_launch = tiled ? tp.images_per_launch : plan.images_per_launch;
+    for (int n0 = 0; n0 < N; n0 += per_launch) {
         Problem q = p;
-        q.N = std::min(plan.images_per_launch, N - n0);
-        hipError_t e = launch_forward(q, plan, static_cast<const char *>(value) + img_v * n0,
-                                      static_cast<const char *>(offset_mask) + img_om * n0,
-                                      static_cast<char *>(output) + img_o * n0, s);
+        q.N = std::min(per_launch, N - n0);
+        const void *v = static_cast<const char *>(value) + img_v * n0;
+        const void *om = static_cast<const char *>(offset_mask) + img_om * n0;
+        void *o = static_cast<char *>(output) + img_o * n0;
+        hipError_t e = tiled ? launch_forward_tiled(q, tp, v, om, o, s) : launch_forward_general(q, plan, v, om, o, s);
         if (e != hipSuccess)
             return hip_status(e);
     }
@@ -335,8 +498,10 @@ int dcnv4_backward(const void *value, const void *offset_mask, const void *grad_
     if (st != DCNV4_OK)
         return st;
     Plan plan;
+    TilePlan tp;
+    const bool tiled = plan_backward_tiled(p, &tp) == DCNV4_OK;
     st = plan_backward(p, &plan);
-    if (st != DCNV4_OK)
+    if (st != DCNV4_OK && !tiled)
         return st;
     if (N == 0)
         return DCNV4_OK;
@@ -357,14 +522,17 @@ int dcnv4_backward(const void *value, const void *offset_mask, const void *grad_
     if (ranges_overlap(grad_value, nv, grad_offset_mask, nom))
         return DCNV4_ERR_PARAM;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    for (int n0 = 0; n0 < N; n0 += plan.images_per_launch) {
+    const int per_launch = tiled ? tp.images_per_launch : plan.images_per_launch;
+    for (int n0 = 0; n0 < N; n0 += per_launch) {
         Problem q = p;
-        q.N = std::min(plan.images_per_launch, N - n0);
-        hipError_t e = launch_backward(q, plan, static_cast<const char *>(value) + img_v * n0,
-                                       static_cast<const char *>(offset_mask) + img_om * n0,
-                                       static_cast<const char *>(grad_output) + img_o * n0,
-                                       static_cast<char *>(grad_value) + img_v * n0,
-                                       static_cast<char *>(grad_offset_mask) + img_om * n0, s);
+        q.N = std::min(per_launch, N - n0);
+        const void *v = static_cast<const char *>(value) + img_v * n0;
+        const void *om = static_cast<const char *>(offset_mask) + img_om * n0;
+        const void *go = static_cast<const char *>(grad_output) + img_o * n0;
+        void *gv = static_cast<char *>(grad_value) + img_v * n0;
+        void *gom = static_cast<char *>(grad_offset_mask) + img_om * n0;
+        hipError_t e = tiled ? launch_backward_tiled(q, tp, v, om, go, gv, gom, s)
+                             : launch_backward_general(q, plan, v, om, go, gv, gom, s);
         if (e != hipSuccess)
             return hip_status(e);
     }

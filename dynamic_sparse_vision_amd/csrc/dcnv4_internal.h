@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI layer (dcnv4_api.cpp) and the HIP
-// kernels (dcnv4_kernels.hip).  Not installed; not part of the ABI.
+// kernels (dcnv4_kernels.hip: general path; dcnv4_tiled.hip: LDS-tiled
+// path).  Not installed; not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -8,6 +9,10 @@
 #include <cstdint>
 
 namespace dcnv4 {
+
+namespace dev {
+struct Geom;
+}
 
 // A fully validated call.  All sizes are positive and every derived byte
 // count of one image fits in 31 bits.
@@ -21,10 +26,9 @@ struct Problem {
     float offset_scale;
 };
 
-// Launch plan shared by the forward and backward kernels: a block covers
-// `pix_per_block` consecutive output pixels (in (n, ho, wo) order) and all
-// of their groups; each (pixel, group) is handled by `lanes` threads of
-// `dp` channels each.
+// General path: a block covers `pix_per_block` consecutive output pixels
+// (in (n, ho, wo) order) and all of their groups; each (pixel, group) is
+// handled by `lanes` threads of `dp` channels each.
 struct Plan {
     int dp;             // channels per thread
     int lanes;          // threads per (pixel, group) = Cg / dp
@@ -34,16 +38,52 @@ struct Plan {
     int images_per_launch;
 };
 
-// Host-side planning (pure C++, no HIP calls).  Returns a dcnv4_status.
+// Tiled path.  A sample (output pixel, group, grid point k) is "near" when
+// the integer part of its displacement is within R pixels on both axes:
+// floor(loc) - (integer grid position) in [-R, R].  Every near sample's four
+// corners lie in an LDS region of rh x rw pixels around the block's tile.
+struct TilePlan {
+    // output tiles (forward, backward grad_offset_mask): th x tw pixels of
+    // one (image, group); lanes threads of dp channels per pixel
+    int dp, lanes, th, tw, threads;
+    int tiles_y, tiles_x;
+    int R;
+    int rh, rw;          // LDS value region, pixels
+    int nvp;             // 16-byte vectors per region pixel (Cg * elem / 16)
+    int swz_mask, swz_shift;
+    int om_ppi;          // pixels per wave-iteration when staging offset/mask
+    int om_lds_bytes;    // LDS for the staged offset/mask entries (16-byte multiple)
+    int lds_bytes;       // total LDS of an output-tile block
+    // cell tiles (backward grad_value): ch x cw input cells of one (image, group)
+    int ch, cw;
+    int ctiles_y, ctiles_x;
+    int src_batch;       // source pixels per batch (src_batch * K * 4 records at most)
+    int max_records;
+    int splat_lds_bytes;
+    int images_per_launch;
+};
+
+// Host-side planning (pure C++, no HIP calls).  Return a dcnv4_status.
 int plan_forward(const Problem &p, Plan *plan);
 int plan_backward(const Problem &p, Plan *plan);
+// Return DCNV4_OK when the tiled path applies, DCNV4_ERR_UNSUPPORTED if not.
+int plan_forward_tiled(const Problem &p, TilePlan *tp);
+int plan_backward_tiled(const Problem &p, TilePlan *tp);
 
-// Enqueue the kernels for images [0, p.N) of the given tensors (the caller
-// has already offset the pointers).  Return hipError_t.
-hipError_t launch_forward(const Problem &p, const Plan &plan, const void *value,
-                          const void *offset_mask, void *output, hipStream_t stream);
-hipError_t launch_backward(const Problem &p, const Plan &plan, const void *value,
-                           const void *offset_mask, const void *grad_output, void *grad_value,
-                           void *grad_offset_mask, hipStream_t stream);
+dev::Geom make_geom(const Problem &p);
+
+// Enqueue kernels for images [0, p.N) of the given tensors (the caller has
+// already offset the pointers).  Return hipError_t.
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
+hipError_t launch_forward_general(const Problem &p, const Plan &plan, const void *value,
+                                  const void *offset_mask, void *output, hipStream_t stream);
+hipError_t launch_backward_general(const Problem &p, const Plan &plan, const void *value,
+                                   const void *offset_mask, const void *grad_output, void *grad_value,
+                                   void *grad_offset_mask, hipStream_t stream);
+hipError_t launch_forward_tiled(const Problem &p, const TilePlan &tp, const void *value,
+                                const void *offset_mask, void *output, hipStream_t stream);
+hipError_t launch_backward_tiled(const Problem &p, const TilePlan &tp, const void *value,
+                                 const void *offset_mask, const void *grad_output, void *grad_value,
+                                 void *grad_offset_mask, hipStream_t stream);
 
 }  // namespace dcnv4

@@ -1,4 +1,4 @@
-// HIP kernels of the DCNv4 spatial aggregation for gfx950 (CDNA4).
+// General-path HIP kernels of the DCNv4 spatial aggregation (gfx950).
 //
 // Operation ("Efficient Deformable ConvNets", DCNv3 recap equation of the
 // CSDN walkthrough "DCNv4论文解析", section 1.2, without the softmax of
@@ -7,140 +7,35 @@
 //   (ho*stride_h - pad_h + j*dil_h + s*dy,  wo*stride_w - pad_w + i*dil_w + s*dx)
 // with zero padding, times an unnormalised scalar m, summed over k.
 //
-// Mapping (the method's own memory-access ideas, walkthrough section 2.2 and
-// the blog "DCNv4架构解析", section "并行计算架构设计", kept where they hold on
-// CDNA4):
-//   * one thread owns DP contiguous channels of one (pixel, group): offsets,
-//     masks and bilinear coefficients are read/computed once per DP channels;
-//   * corner rows are fetched with 128-bit buffer loads (channel-last layout
-//     makes the DP channels of a corner contiguous);
-//   * the offset/mask rows of a block's pixels are staged in LDS with
-//     coalesced 128-bit loads (rows are 16-byte multiples by the pad-to-8
-//     rule), and read from LDS per grid point;
-//   * fp32 coordinates (one fma, bit-identical to the reference definition),
-//     fp32 weights and fp32 accumulation; RNE rounding on the store.
-// CDNA4-specific choices: raw buffer resources give a hardware range check,
-// so corners outside the tensor read 0 (and atomics outside it are dropped)
-// without branches; the workgroup -> tile map is XCD-aware; no MFMA (a
-// gather-weighted sum is not a dense contraction).
+// These kernels handle any validated shape: one thread owns DP contiguous
+// channels of one (pixel, group) (walkthrough section 2.2: offsets, masks and
+// bilinear coefficients read/computed once per D' channels), the block's
+// offset/mask rows are staged in LDS (blog "DCNv4架构解析", section
+// "并行计算架构设计"), corners are 128-bit raw buffer loads whose range check
+// returns 0 outside the tensor, and grad_value is summed with device atomics.
+// The tiled kernels (dcnv4_tiled.hip) are used where their LDS budget fits.
 
+#include "dcnv4_device.h"
 #include "dcnv4_internal.h"
 
-#include <hip/hip_runtime.h>
-
-// buffer_atomic_add_f32 through a buffer resource (the hardware range check
-// drops lanes whose offset lies outside the resource).
-__device__ float buffer_atomic_fadd(float v, __amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset,
-                                    int aux) __asm("llvm.amdgcn.raw.ptr.buffer.atomic.fadd.f32");
+#include <algorithm>
 
 namespace dcnv4 {
 namespace {
 
-// dword3 of a raw (stride 0) buffer resource on gfx9-family devices.
-constexpr int kRawBufferConfig = 0x00020000;
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-// Note: __builtin_bit_cast is only ever applied to whole vectors or scalars
-// here; applied to a vector-element lvalue it reads element 0 with this
-// compiler.
-
+using namespace dev;
 
 struct KArgs {
+    Geom geo;
     const void *value;
     const void *om;
     void *out;            // forward output
     const float *gout;    // backward: grad_output
     float *gvalue;        // backward: grad_value
     float *gom;           // backward: grad_offset_mask
-    int H, W, Ho, Wo, G, Cg, C, K, P;
-    int kh, sh, sw, ph, pw, dh, dw;
-    int rc, kc;           // remove_center, index of the centre in the full grid
-    float scale;
+    int G, Cg, K, P;
     int lanes, pix_per_block, total_pix;
     int value_bytes;      // bytes of value (and of grad_value) in this launch
-};
-
-// Round-robin dispatch puts consecutive workgroups on different XCDs, each
-// with its own L2.  Renumber so that XCD x processes one contiguous range of
-// tiles: neighbouring pixel tiles sample overlapping value rows, and those
-// re-reads then hit the same L2.
-__device__ __forceinline__ int xcd_tile(int b, int nb)
-{
-    const int xcd = b & 7, idx = b >> 3;
-    const int per = nb >> 3, rem = nb & 7;
-    return xcd * per + min(xcd, rem) + idx;
-}
-
-// ---- storage types -------------------------------------------------------
-
-struct bf16_t {
-    unsigned short bits;
-};
-
-template <typename T>
-struct Store;
-
-template <>
-struct Store<float> {
-    __device__ static float scalar(float v) { return v; }
-    __device__ static float get(const u32x4 *r, int c)
-    {
-        const f32x4 f = __builtin_bit_cast(f32x4, r[c >> 2]);
-        return f[c & 3];
-    }
-    __device__ static void pack(const float *acc, u32x4 *r, int nv)
-    {
-        for (int v = 0; v < nv; ++v) {
-            f32x4 f;
-            for (int e = 0; e < 4; ++e)
-                f[e] = acc[4 * v + e];
-            r[v] = __builtin_bit_cast(u32x4, f);
-        }
-    }
-};
-
-template <>
-struct Store<_Float16> {
-    __device__ static float scalar(_Float16 v) { return (float)v; }
-    __device__ static float get(const u32x4 *r, int c)
-    {
-        const f16x8 h = __builtin_bit_cast(f16x8, r[c >> 3]);
-        return (float)h[c & 7];
-    }
-    __device__ static void pack(const float *acc, u32x4 *r, int nv)
-    {
-        for (int v = 0; v < nv; ++v) {
-            f16x8 h;
-            for (int e = 0; e < 8; ++e)
-                h[e] = (_Float16)acc[8 * v + e];   // round to nearest even
-            r[v] = __builtin_bit_cast(u32x4, h);
-        }
-    }
-};
-
-__device__ __forceinline__ unsigned bf16_round(float f)
-{
-    // fp32 -> bf16 bits, round to nearest even (inputs are finite).
-    const unsigned u = __builtin_bit_cast(unsigned, f);
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-template <>
-struct Store<bf16_t> {
-    __device__ static float scalar(bf16_t v) { return __builtin_bit_cast(float, (unsigned)v.bits << 16); }
-    __device__ static float get(const u32x4 *r, int c)
-    {
-        const unsigned w = r[c >> 3][(c & 7) >> 1];
-        return __builtin_bit_cast(float, (c & 1) ? (w & 0xffff0000u) : (w << 16));
-    }
-    __device__ static void pack(const float *acc, u32x4 *r, int nv)
-    {
-        for (int v = 0; v < nv; ++v)
-            for (int e = 0; e < 4; ++e)
-                r[v][e] = bf16_round(acc[8 * v + 2 * e]) | (bf16_round(acc[8 * v + 2 * e + 1]) << 16);
-    }
 };
 
 // Copy rows [pix0, pix0+npix) of the offset_mask tensor into LDS.
@@ -153,62 +48,12 @@ __device__ __forceinline__ void stage_rows(const KArgs &a, int pix0, int npix, u
         dst[i] = src[i];
 }
 
-// Bilinear footprint of one sample: the top-left corner, the fractional
-// parts, and which of the two rows / two columns lie inside the image (a
-// corner outside [0,H)x[0,W) has value 0: zero-extended image).
-struct Footprint {
-    float lh, lw;            // loc - floor(loc)
-    bool r0, r1, c0, c1;     // rows h0, h0+1 and columns w0, w0+1 inside the image
-    unsigned off;            // byte offset of corner (h0, w0) plus the channel offset
-};
-
-__device__ __forceinline__ bool footprint(const KArgs &a, int n, int ho, int wo, int k,
-                                          float dx, float dy, int es, int chan_off, Footprint &f)
-{
-    const int kk = k + ((a.rc && k >= a.kc) ? 1 : 0);
-    const int i = kk / a.kh, j = kk - i * a.kh;
-    const float loc_w = __builtin_fmaf(a.scale, dx, (float)(wo * a.sw - a.pw + i * a.dw));
-    const float loc_h = __builtin_fmaf(a.scale, dy, (float)(ho * a.sh - a.ph + j * a.dh));
-    if (!(loc_h >= -1.0f && loc_h < (float)a.H && loc_w >= -1.0f && loc_w < (float)a.W))
-        return false;   // all four corners outside (or NaN): the sample adds nothing
-    const float fh = floorf(loc_h), fw = floorf(loc_w);
-    const int h0 = (int)fh, w0 = (int)fw;
-    f.lh = loc_h - fh;
-    f.lw = loc_w - fw;
-    f.r0 = h0 >= 0;
-    f.r1 = h0 + 1 < a.H;
-    f.c0 = w0 >= 0;
-    f.c1 = w0 + 1 < a.W;
-    // Negative offsets (row -1 of image 0) wrap to huge unsigned values and
-    // fail the buffer range check like offsets past the end.
-    f.off = ((unsigned)(n * a.H + h0) * (unsigned)a.W + (unsigned)w0) * (unsigned)(a.C * es) + (unsigned)chan_off;
-    return true;
-}
-
-// Corner weights m*w_q with corners outside the image set to 0 (the loads of
-// such corners return neighbouring or zero data, multiplied by 0; values are
-// finite by contract).
-__device__ __forceinline__ void corner_weights(const Footprint &f, float m, float &w00, float &w01,
-                                               float &w10, float &w11)
-{
-    const float hh = f.r0 ? 1.0f - f.lh : 0.0f;
-    const float lh = f.r1 ? f.lh : 0.0f;
-    const float hw = f.c0 ? 1.0f - f.lw : 0.0f;
-    const float lw = f.c1 ? f.lw : 0.0f;
-    const float mh = m * hh, ml = m * lh;
-    w00 = mh * hw;
-    w01 = mh * lw;
-    w10 = ml * hw;
-    w11 = ml * lw;
-}
-
-// ---- forward -------------------------------------------------------------
-
 template <typename T, int DP>
-__global__ __launch_bounds__(256) void dcnv4_fwd_kernel(KArgs a)
+__global__ __launch_bounds__(256) void dcnv4_fwd_general(KArgs a)
 {
     extern __shared__ u32x4 smem[];
     constexpr int NV = DP * (int)sizeof(T) / 16;   // 128-bit vectors per corner
+    const Geom &geo = a.geo;
     const int tile = xcd_tile(blockIdx.x, gridDim.x);
     const int pix0 = tile * a.pix_per_block;
     const int npix = min(a.pix_per_block, a.total_pix - pix0);
@@ -223,16 +68,15 @@ __global__ __launch_bounds__(256) void dcnv4_fwd_kernel(KArgs a)
     const int g = rr / a.lanes;
     const int chunk = rr - g * a.lanes;
     const int pix = pix0 + lp;
-    const int wo = pix % a.Wo;
-    const int t = pix / a.Wo;
-    const int ho = t % a.Ho;
-    const int n = t / a.Ho;
+    const int wo = pix % geo.Wo;
+    const int t = pix / geo.Wo;
+    const int ho = t % geo.Ho;
+    const int n = t / geo.Ho;
     const int es = (int)sizeof(T);
     const int chan_off = (g * a.Cg + chunk * DP) * es;
-    const unsigned cs = (unsigned)(a.C * es), rs = (unsigned)a.W * cs;
+    const unsigned cs = (unsigned)(geo.C * es), rs = (unsigned)geo.W * cs;
     const T *om = reinterpret_cast<const T *>(smem) + lp * a.P + g * 3 * a.K;
-    const __amdgpu_buffer_rsrc_t vr =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.value), 0, a.value_bytes, kRawBufferConfig);
+    const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
 
     float acc[DP];
 #pragma unroll
@@ -243,18 +87,20 @@ __global__ __launch_bounds__(256) void dcnv4_fwd_kernel(KArgs a)
         const float dx = Store<T>::scalar(om[2 * k]);
         const float dy = Store<T>::scalar(om[2 * k + 1]);
         const float m = Store<T>::scalar(om[2 * a.K + k]);
-        Footprint f;
-        if (!footprint(a, n, ho, wo, k, dx, dy, es, chan_off, f))
+        const Loc l = locate(geo, ho, wo, k, dx, dy);
+        if (!live(geo, l))
             continue;
+        const Footprint f = footprint(geo, l);
+        const unsigned off = corner_offset(geo, n, f, es, chan_off);
         float w00, w01, w10, w11;
-        corner_weights(f, m, w00, w01, w10, w11);
+        masked_weights(f, m, w00, w01, w10, w11);
         u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            v00[v] = __builtin_amdgcn_raw_buffer_load_b128(vr, f.off + 16 * v, 0, 0);
-            v01[v] = __builtin_amdgcn_raw_buffer_load_b128(vr, f.off + cs + 16 * v, 0, 0);
-            v10[v] = __builtin_amdgcn_raw_buffer_load_b128(vr, f.off + rs + 16 * v, 0, 0);
-            v11[v] = __builtin_amdgcn_raw_buffer_load_b128(vr, f.off + rs + cs + 16 * v, 0, 0);
+            v00[v] = load16(vr, off + 16 * v);
+            v01[v] = load16(vr, off + cs + 16 * v);
+            v10[v] = load16(vr, off + rs + 16 * v);
+            v11[v] = load16(vr, off + rs + cs + 16 * v);
         }
 #pragma unroll
         for (int c = 0; c < DP; ++c) {
@@ -269,13 +115,11 @@ __global__ __launch_bounds__(256) void dcnv4_fwd_kernel(KArgs a)
 
     u32x4 res[NV];
     Store<T>::pack(acc, res, NV);
-    u32x4 *dst = reinterpret_cast<u32x4 *>(static_cast<T *>(a.out) + (size_t)pix * a.C + g * a.Cg + chunk * DP);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(static_cast<T *>(a.out) + (size_t)pix * geo.C + g * a.Cg + chunk * DP);
 #pragma unroll
     for (int v = 0; v < NV; ++v)
         dst[v] = res[v];
 }
-
-// ---- backward (fp32) -----------------------------------------------------
 
 __global__ __launch_bounds__(256) void dcnv4_zero_kernel(u32x4 *p, size_t nvec)
 {
@@ -285,10 +129,11 @@ __global__ __launch_bounds__(256) void dcnv4_zero_kernel(u32x4 *p, size_t nvec)
 }
 
 template <int DP>
-__global__ __launch_bounds__(256) void dcnv4_bwd_kernel(KArgs a)
+__global__ __launch_bounds__(256) void dcnv4_bwd_general(KArgs a)
 {
     extern __shared__ u32x4 smem[];
     constexpr int NV = DP / 4;
+    const Geom &geo = a.geo;
     const int tile = xcd_tile(blockIdx.x, gridDim.x);
     const int pix0 = tile * a.pix_per_block;
     const int npix = min(a.pix_per_block, a.total_pix - pix0);
@@ -306,22 +151,20 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_kernel(KArgs a)
         const int g = rr / a.lanes;
         const int chunk = rr - g * a.lanes;
         const int pix = pix0 + lp;
-        const int wo = pix % a.Wo;
-        const int t = pix / a.Wo;
-        const int ho = t % a.Ho;
-        const int n = t / a.Ho;
+        const int wo = pix % geo.Wo;
+        const int t = pix / geo.Wo;
+        const int ho = t % geo.Ho;
+        const int n = t / geo.Ho;
         const int chan_off = (g * a.Cg + chunk * DP) * 4;
-        const unsigned cs = (unsigned)(a.C * 4), rs = (unsigned)a.W * cs;
+        const unsigned cs = (unsigned)(geo.C * 4), rs = (unsigned)geo.W * cs;
         const float *om = s_om + lp * a.P + g * 3 * a.K;
         float *gomr = s_grad + lp * a.P + g * 3 * a.K;
-        const __amdgpu_buffer_rsrc_t vr =
-            __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(a.value), 0, a.value_bytes, kRawBufferConfig);
-        const __amdgpu_buffer_rsrc_t gr =
-            __builtin_amdgcn_make_buffer_rsrc(a.gvalue, 0, a.value_bytes, kRawBufferConfig);
+        const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
+        const __amdgpu_buffer_rsrc_t gr = rsrc(a.gvalue, a.value_bytes);
 
         float go[DP];
         {
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(a.gout + (size_t)pix * a.C + g * a.Cg + chunk * DP);
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(a.gout + (size_t)pix * geo.C + g * a.Cg + chunk * DP);
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
                 const f32x4 r = __builtin_bit_cast(f32x4, src[v]);
@@ -332,17 +175,18 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_kernel(KArgs a)
 
         for (int k = 0; k < a.K; ++k) {
             const float dx = om[2 * k], dy = om[2 * k + 1], m = om[2 * a.K + k];
-            Footprint f;
             float gm = 0.0f, gw = 0.0f, gh = 0.0f;
-            const bool live = footprint(a, n, ho, wo, k, dx, dy, 4, chan_off, f);
-            if (live) {
+            const Loc l = locate(geo, ho, wo, k, dx, dy);
+            if (live(geo, l)) {
+                const Footprint f = footprint(geo, l);
+                const unsigned off = corner_offset(geo, n, f, 4, chan_off);
                 u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
 #pragma unroll
                 for (int v = 0; v < NV; ++v) {
-                    v00[v] = __builtin_amdgcn_raw_buffer_load_b128(vr, f.off + 16 * v, 0, 0);
-                    v01[v] = __builtin_amdgcn_raw_buffer_load_b128(vr, f.off + cs + 16 * v, 0, 0);
-                    v10[v] = __builtin_amdgcn_raw_buffer_load_b128(vr, f.off + rs + 16 * v, 0, 0);
-                    v11[v] = __builtin_amdgcn_raw_buffer_load_b128(vr, f.off + rs + cs + 16 * v, 0, 0);
+                    v00[v] = load16(vr, off + 16 * v);
+                    v01[v] = load16(vr, off + cs + 16 * v);
+                    v10[v] = load16(vr, off + rs + 16 * v);
+                    v11[v] = load16(vr, off + rs + cs + 16 * v);
                 }
                 // t_q = sum_c grad_out_c * v_q,c : every gradient of the
                 // sample is a fixed combination of the four corner dots.
@@ -355,11 +199,10 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_kernel(KArgs a)
                     t11 = __builtin_fmaf(go[c], Store<float>::get(v11, c), t11);
                 }
                 // Zero-extended image: dots of corners outside are 0.
-                const bool q00 = f.r0 && f.c0, q01 = f.r0 && f.c1, q10 = f.r1 && f.c0, q11 = f.r1 && f.c1;
-                t00 = q00 ? t00 : 0.0f;
-                t01 = q01 ? t01 : 0.0f;
-                t10 = q10 ? t10 : 0.0f;
-                t11 = q11 ? t11 : 0.0f;
+                t00 = (f.r0 && f.c0) ? t00 : 0.0f;
+                t01 = (f.r0 && f.c1) ? t01 : 0.0f;
+                t10 = (f.r1 && f.c0) ? t10 : 0.0f;
+                t11 = (f.r1 && f.c1) ? t11 : 0.0f;
                 const float lh = f.lh, lw = f.lw, hh = 1.0f - lh, hw = 1.0f - lw;
                 // d/dm: the sample; d/d loc_w and d/d loc_h of the bilinear
                 // sample inside the cell chosen by floor (right derivative).
@@ -370,14 +213,14 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_kernel(KArgs a)
                 // outside the image get a zero weight, and those outside the
                 // tensor are dropped by the buffer range check.
                 float w00, w01, w10, w11;
-                corner_weights(f, m, w00, w01, w10, w11);
+                masked_weights(f, m, w00, w01, w10, w11);
 #pragma unroll
                 for (int c = 0; c < DP; ++c) {
-                    const unsigned o = f.off + 4 * c;
-                    buffer_atomic_fadd(w00 * go[c], gr, o, 0, 0);
-                    buffer_atomic_fadd(w01 * go[c], gr, o + cs, 0, 0);
-                    buffer_atomic_fadd(w10 * go[c], gr, o + rs, 0, 0);
-                    buffer_atomic_fadd(w11 * go[c], gr, o + rs + cs, 0, 0);
+                    const unsigned o = off + 4 * c;
+                    dcnv4_buffer_atomic_fadd(w00 * go[c], gr, o, 0, 0);
+                    dcnv4_buffer_atomic_fadd(w01 * go[c], gr, o + cs, 0, 0);
+                    dcnv4_buffer_atomic_fadd(w10 * go[c], gr, o + rs, 0, 0);
+                    dcnv4_buffer_atomic_fadd(w11 * go[c], gr, o + rs + cs, 0, 0);
                 }
             }
             // reduce the partial sums of the lanes sharing this (pixel, group);
@@ -388,7 +231,7 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_kernel(KArgs a)
                 gh += __shfl_xor(gh, d);
             }
             if (chunk == 0) {
-                const float sm = a.scale * m;
+                const float sm = geo.scale * m;
                 gomr[2 * k] = sm * gw;
                 gomr[2 * k + 1] = sm * gh;
                 gomr[2 * a.K + k] = gm;
@@ -407,50 +250,35 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_kernel(KArgs a)
 }
 
 template <typename T>
-hipError_t launch_fwd_t(const Problem &p, const Plan &plan, const KArgs &a, int blocks, hipStream_t s)
+hipError_t launch_fwd_t(const Plan &plan, const KArgs &a, int blocks, hipStream_t s)
 {
     switch (plan.dp) {
     case 16:
-        hipLaunchKernelGGL((dcnv4_fwd_kernel<T, 16>), dim3(blocks), dim3(plan.threads), plan.lds_bytes, s, a);
+        hipLaunchKernelGGL((dcnv4_fwd_general<T, 16>), dim3(blocks), dim3(plan.threads), plan.lds_bytes, s, a);
         break;
     case 8:
-        hipLaunchKernelGGL((dcnv4_fwd_kernel<T, 8>), dim3(blocks), dim3(plan.threads), plan.lds_bytes, s, a);
+        hipLaunchKernelGGL((dcnv4_fwd_general<T, 8>), dim3(blocks), dim3(plan.threads), plan.lds_bytes, s, a);
         break;
     case 4:
         if constexpr (sizeof(T) == 4) {
-            hipLaunchKernelGGL((dcnv4_fwd_kernel<T, 4>), dim3(blocks), dim3(plan.threads), plan.lds_bytes, s, a);
+            hipLaunchKernelGGL((dcnv4_fwd_general<T, 4>), dim3(blocks), dim3(plan.threads), plan.lds_bytes, s, a);
             break;
         }
         return hipErrorInvalidValue;
     default:
         return hipErrorInvalidValue;
     }
-    (void)p;
     return hipGetLastError();
 }
 
 KArgs make_args(const Problem &p, const Plan &plan)
 {
     KArgs a{};
-    a.H = p.H;
-    a.W = p.W;
-    a.Ho = p.Ho;
-    a.Wo = p.Wo;
+    a.geo = make_geom(p);
     a.G = p.G;
     a.Cg = p.Cg;
-    a.C = p.C;
     a.K = p.K;
     a.P = p.P;
-    a.kh = p.kh;
-    a.sh = p.sh;
-    a.sw = p.sw;
-    a.ph = p.ph;
-    a.pw = p.pw;
-    a.dh = p.dh;
-    a.dw = p.dw;
-    a.rc = p.remove_center;
-    a.kc = ((p.kw - 1) / 2) * p.kh + (p.kh - 1) / 2;
-    a.scale = p.offset_scale;
     a.lanes = plan.lanes;
     a.pix_per_block = plan.pix_per_block;
     a.total_pix = p.N * p.Ho * p.Wo;
@@ -460,8 +288,40 @@ KArgs make_args(const Problem &p, const Plan &plan)
 
 }  // namespace
 
-hipError_t launch_forward(const Problem &p, const Plan &plan, const void *value, const void *offset_mask,
-                          void *output, hipStream_t stream)
+dev::Geom make_geom(const Problem &p)
+{
+    dev::Geom g{};
+    g.H = p.H;
+    g.W = p.W;
+    g.C = p.C;
+    g.Ho = p.Ho;
+    g.Wo = p.Wo;
+    g.kh = p.kh;
+    g.kw = p.kw;
+    g.sh = p.sh;
+    g.sw = p.sw;
+    g.ph = p.ph;
+    g.pw = p.pw;
+    g.dh = p.dh;
+    g.dw = p.dw;
+    g.rc = p.remove_center;
+    g.kc = ((p.kw - 1) / 2) * p.kh + (p.kh - 1) / 2;
+    g.scale = p.offset_scale;
+    return g;
+}
+
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream)
+{
+    const size_t nvec = bytes / 16;
+    const int blocks = (int)std::min<size_t>((nvec + 255) / 256, 4096);
+    if (blocks == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(dcnv4_zero_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<u32x4 *>(p), nvec);
+    return hipGetLastError();
+}
+
+hipError_t launch_forward_general(const Problem &p, const Plan &plan, const void *value, const void *offset_mask,
+                                  void *output, hipStream_t stream)
 {
     KArgs a = make_args(p, plan);
     a.value = value;
@@ -470,19 +330,19 @@ hipError_t launch_forward(const Problem &p, const Plan &plan, const void *value,
     const int blocks = (a.total_pix + plan.pix_per_block - 1) / plan.pix_per_block;
     switch (p.dtype) {
     case 0:
-        return launch_fwd_t<float>(p, plan, a, blocks, stream);
+        return launch_fwd_t<float>(plan, a, blocks, stream);
     case 1:
-        return launch_fwd_t<_Float16>(p, plan, a, blocks, stream);
+        return launch_fwd_t<_Float16>(plan, a, blocks, stream);
     case 2:
-        return launch_fwd_t<bf16_t>(p, plan, a, blocks, stream);
+        return launch_fwd_t<bf16_t>(plan, a, blocks, stream);
     default:
         return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_backward(const Problem &p, const Plan &plan, const void *value, const void *offset_mask,
-                           const void *grad_output, void *grad_value, void *grad_offset_mask,
-                           hipStream_t stream)
+hipError_t launch_backward_general(const Problem &p, const Plan &plan, const void *value, const void *offset_mask,
+                                   const void *grad_output, void *grad_value, void *grad_offset_mask,
+                                   hipStream_t stream)
 {
     KArgs a = make_args(p, plan);
     a.value = value;
@@ -490,23 +350,19 @@ hipError_t launch_backward(const Problem &p, const Plan &plan, const void *value
     a.gout = static_cast<const float *>(grad_output);
     a.gvalue = static_cast<float *>(grad_value);
     a.gom = static_cast<float *>(grad_offset_mask);
-    const size_t nvec = (size_t)a.value_bytes / 16;
-    const int zblocks = (int)std::min<size_t>((nvec + 255) / 256, 4096);
-    hipLaunchKernelGGL(dcnv4_zero_kernel, dim3(zblocks), dim3(256), 0, stream,
-                       static_cast<u32x4 *>(grad_value), nvec);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_zero(grad_value, (size_t)a.value_bytes, stream);
     if (e != hipSuccess)
         return e;
     const int blocks = (a.total_pix + plan.pix_per_block - 1) / plan.pix_per_block;
     switch (plan.dp) {
     case 4:
-        hipLaunchKernelGGL((dcnv4_bwd_kernel<4>), dim3(blocks), dim3(plan.threads), plan.lds_bytes, stream, a);
+        hipLaunchKernelGGL((dcnv4_bwd_general<4>), dim3(blocks), dim3(plan.threads), plan.lds_bytes, stream, a);
         break;
     case 8:
-        hipLaunchKernelGGL((dcnv4_bwd_kernel<8>), dim3(blocks), dim3(plan.threads), plan.lds_bytes, stream, a);
+        hipLaunchKernelGGL((dcnv4_bwd_general<8>), dim3(blocks), dim3(plan.threads), plan.lds_bytes, stream, a);
         break;
     case 16:
-        hipLaunchKernelGGL((dcnv4_bwd_kernel<16>), dim3(blocks), dim3(plan.threads), plan.lds_bytes, stream, a);
+        hipLaunchKernelGGL((dcnv4_bwd_general<16>), dim3(blocks), dim3(plan.threads), plan.lds_bytes, stream, a);
         break;
     default:
         return hipErrorInvalidValue;
