@@ -272,7 +272,10 @@ int tile_lds(const Problem &p, TilePlan *tp, int R, int elem)
     tp->R = R;
     tp->rh = (tp->th - 1) * p.sh + (p.kh - 1) * p.dh + 2 * R + 2;
     tp->rw = (tp->tw - 1) * p.sw + (p.kw - 1) * p.dw + 2 * R + 2;
-    const int om = tp->th * tp->tw * 3 * p.K * elem;
+    // a group's 3K entries, widened to whole dwords (2-byte entries may start
+    // mid-dword)
+    tp->om_dw = elem == 4 ? 3 * p.K : (3 * p.K + 2) / 2;
+    const int om = tp->th * tp->tw * tp->om_dw * 4;
     tp->om_lds_bytes = (om + 15) / 16 * 16;
     tp->lds_bytes = tp->om_lds_bytes + tp->rh * tp->rw * tp->nvp * 16;
     return tp->lds_bytes;

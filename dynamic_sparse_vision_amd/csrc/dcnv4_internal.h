@@ -51,7 +51,7 @@ struct TilePlan {
     int rh, rw;          // LDS value region, pixels
     int nvp;             // 16-byte vectors per region pixel (Cg * elem / 16)
     int swz_mask, swz_shift;
-    int om_ppi;          // pixels per wave-iteration when staging offset/mask
+    int om_dw;           // staged dwords per pixel: one group's 3K entries, dword-aligned
     int om_lds_bytes;    // LDS for the staged offset/mask entries (16-byte multiple)
     int lds_bytes;       // total LDS of an output-tile block
     // cell tiles (backward grad_value): ch x cw input cells of one (image, group)

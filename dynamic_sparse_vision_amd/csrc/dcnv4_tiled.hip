@@ -52,8 +52,11 @@ struct TArgs {
     int th, tw, tiles_y, tiles_x, lanes_shift;
     int R, rh, rw, nvp_shift, swz_mask, swz_shift;
     int om_lds_vecs;             // 16-byte LDS vectors reserved for the offset/mask stage
+    int om_dw;                   // staged dwords per pixel (offset/mask entries of one group)
     unsigned k3_magic;           // ceil(2^32 / (3K)): e / (3K) == mulhi(e, k3_magic) for small e
     unsigned tw_magic;           // ceil(2^32 / tw)
+    unsigned omdw_magic;         // ceil(2^32 / om_dw)
+    unsigned rw_magic;           // ceil(2^32 / rw)
     // cell tiles (backward grad_value)
     int ch, cw, ctiles_y, ctiles_x, src_batch;
     unsigned k_magic;            // ceil(2^32 / K)
@@ -103,73 +106,92 @@ __device__ __forceinline__ float load_elem<float>(__amdgpu_buffer_rsrc_t r, unsi
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
-template <>
-__device__ __forceinline__ _Float16 load_elem<_Float16>(__amdgpu_buffer_rsrc_t r, unsigned off)
+
+// Staging uses direct-to-LDS buffer loads: lane t of a wave instruction
+// writes its 4 or 16 bytes at LDS base + t*size, a source offset outside the
+// buffer writes zeros, and inactive lanes write nothing.  Every wave walks
+// contiguous 64-slot chunks of the LDS image, computes the source of each
+// slot, and issues all loads before a single wait (the data never passes
+// through registers).  Blocks are whole waves (the host rounds the thread
+// count up to a multiple of 64; lanes past the tile only help staging).
+
+constexpr unsigned kOutOfRange = 0x80000000u;   // >= any buffer size used here
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds_chunk, unsigned off)
 {
-    return __builtin_bit_cast(_Float16, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
-}
-template <>
-__device__ __forceinline__ bf16_t load_elem<bf16_t>(__amdgpu_buffer_rsrc_t r, unsigned off)
-{
-    return __builtin_bit_cast(bf16_t, __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_chunk, 16, off, 0, 0, 0);
 }
 
-// Staging and write-back loops stride by 64 lanes: blocks are whole waves
-// (the host rounds the thread count up to a multiple of 64; lanes past the
-// tile only help staging).
-//
-// The 3K offset/mask entries of group g for every pixel of the tile:
-// om_s[q*3K + j], q = py*tw + px.  A wave copies one tile row per
-// iteration; element e of a row is (px, j) = (e / 3K, e % 3K).  Pixels
-// outside the image read 0 (they are never used).
-template <typename T>
-__device__ void stage_offsets(const TArgs &a, const Tile &t, T *om_s)
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void *lds_chunk, unsigned off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_chunk, 4, off, 0, 0, 0);
+}
+
+// Offset/mask entries of group g for the tile's pixels, in dwords: pixel q
+// owns om_dw dwords starting at dword q*om_dw; they cover its 3K elements
+// from the dword-aligned element below g*3K (for 2-byte elements the block's
+// entries start om_par elements into each pixel's slice).  Pixels outside the
+// image read zeros.
+__device__ void stage_offsets(const TArgs &a, const Tile &t, unsigned *om_s, int es)
 {
     const Geom &geo = a.geo;
-    const int K3 = 3 * a.K;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = (blockDim.x + 63) >> 6;
-    const int row_elems = a.tw * K3;
+    const int total = a.th * a.tw * a.om_dw;
+    const int epd = 4 / es;   // elements per dword
     const __amdgpu_buffer_rsrc_t r = rsrc(a.om, a.om_bytes);
-    for (int py = wave; py < a.th; py += nwaves) {
-        const int oy = t.oy0 + py;
-        for (int e = lane; e < row_elems; e += 64) {
-            const int px = (int)divm((unsigned)e, a.k3_magic);
-            const int j = e - px * K3;
-            const int ox = t.ox0 + px;
-            T v;
-            __builtin_memset(&v, 0, sizeof v);
+    for (int c0 = wave * 64; c0 < total; c0 += nwaves * 64) {
+        const int i = c0 + lane;
+        if (i < total) {
+            const int q = (int)divm((unsigned)i, a.omdw_magic);
+            const int d = i - q * a.om_dw;
+            const int py = (int)divm((unsigned)q, a.tw_magic);
+            const int px = q - py * a.tw;
+            const int oy = t.oy0 + py, ox = t.ox0 + px;
+            unsigned off = kOutOfRange;
             if (oy < geo.Ho && ox < geo.Wo) {
-                const unsigned idx = (unsigned)(((t.n * geo.Ho + oy) * geo.Wo + ox) * a.P + t.g * K3 + j);
-                v = load_elem<T>(r, idx * (unsigned)sizeof(T));
+                const unsigned e0 = (unsigned)(((t.n * geo.Ho + oy) * geo.Wo + ox) * a.P + t.g * 3 * a.K);
+                off = (e0 / (unsigned)epd + (unsigned)d) * 4u;
             }
-            om_s[(py * a.tw + px) * K3 + j] = v;
+            dma4(r, om_s + c0, off);
         }
     }
 }
 
 // Value rows of group g for the tile plus a halo: region pixel (rr, cc) is
-// image pixel (ry0 + rr, rx0 + cc); zeros outside the image.
+// image pixel (ry0 + rr, rx0 + cc); zeros outside the image.  Slot s holds
+// vector (s & (nvp-1)) ^ swizzle(p) of region pixel p = s / nvp (see vslot).
 __device__ void stage_region(const TArgs &a, const Tile &t, u32x4 *val_s, int es)
 {
     const Geom &geo = a.geo;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = (blockDim.x + 63) >> 6;
     const int ry0 = t.oy0 * geo.sh - geo.ph - a.R, rx0 = t.ox0 * geo.sw - geo.pw - a.R;
-    const int row_vecs = a.rw << a.nvp_shift;
+    const int total = (a.rh * a.rw) << a.nvp_shift;
     const int vmask = (1 << a.nvp_shift) - 1;
     const unsigned cs = (unsigned)(geo.C * es), goff = (unsigned)(t.g * a.Cg * es);
     const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
-    for (int rr = wave; rr < a.rh; rr += nwaves) {
-        const int y = ry0 + rr;
-        const bool yin = (unsigned)y < (unsigned)geo.H;
-        for (int e = lane; e < row_vecs; e += 64) {
-            const int cc = e >> a.nvp_shift, v = e & vmask;
-            const int x = rx0 + cc;
-            u32x4 d = {0u, 0u, 0u, 0u};
-            if (yin && (unsigned)x < (unsigned)geo.W)
-                d = load16(vr, (unsigned)((t.n * geo.H + y) * geo.W + x) * cs + goff + 16u * (unsigned)v);
-            val_s[vslot(a, rr * a.rw + cc, v)] = d;
+    for (int c0 = wave * 64; c0 < total; c0 += nwaves * 64) {
+        const int s = c0 + lane;
+        if (s < total) {
+            const int p = s >> a.nvp_shift;
+            const int v = (s & vmask) ^ ((p >> a.swz_shift) & a.swz_mask);
+            const int rr = (int)divm((unsigned)p, a.rw_magic);
+            const int cc = p - rr * a.rw;
+            const int y = ry0 + rr, x = rx0 + cc;
+            unsigned off = kOutOfRange;
+            if ((unsigned)y < (unsigned)geo.H && (unsigned)x < (unsigned)geo.W)
+                off = (unsigned)((t.n * geo.H + y) * geo.W + x) * cs + goff + 16u * (unsigned)v;
+            dma16(vr, val_s + c0, off);
         }
     }
+}
+
+// Wait for this thread's direct-to-LDS loads, then for the whole block.
+__device__ __forceinline__ void staging_done()
+{
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 }
 
 // Near test: the integer displacement of the sample is within R pixels.
@@ -187,11 +209,11 @@ __global__ __launch_bounds__(256) void dcnv4_fwd_tiled(TArgs a)
     constexpr int NV = DP * (int)sizeof(T) / 16;
     const Geom &geo = a.geo;
     const Tile t = out_tile(a);
-    T *om_s = reinterpret_cast<T *>(smem);
+    unsigned *om_s = reinterpret_cast<unsigned *>(smem);
     u32x4 *val_s = smem + a.om_lds_vecs;
-    stage_offsets<T>(a, t, om_s);
+    stage_offsets(a, t, om_s, (int)sizeof(T));
     stage_region(a, t, val_s, (int)sizeof(T));
-    __syncthreads();
+    staging_done();
 
     const int q = threadIdx.x >> a.lanes_shift;
     const int chunk = threadIdx.x - (q << a.lanes_shift);
@@ -201,8 +223,8 @@ __global__ __launch_bounds__(256) void dcnv4_fwd_tiled(TArgs a)
     if (py >= a.th || oy >= geo.Ho || ox >= geo.Wo)
         return;   // no barrier follows
     const int es = (int)sizeof(T);
-    const int K3 = 3 * a.K;
-    const T *om = om_s + q * K3;
+    constexpr int epd = 4 / (int)sizeof(T);   // elements per staged dword
+    const T *om = reinterpret_cast<const T *>(om_s) + q * a.om_dw * epd + ((t.g * 3 * a.K) & (epd - 1));
     const int ry0 = t.oy0 * geo.sh - geo.ph - a.R, rx0 = t.ox0 * geo.sw - geo.pw - a.R;
     const int chan_off = (t.g * a.Cg + chunk * DP) * es;
     const unsigned cs = (unsigned)(geo.C * es), rs = (unsigned)geo.W * cs;
@@ -283,9 +305,9 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_offsets_tiled(TArgs a)
     const Tile t = out_tile(a);
     float *om_s = reinterpret_cast<float *>(smem);
     u32x4 *val_s = smem + a.om_lds_vecs;
-    stage_offsets<float>(a, t, om_s);
+    stage_offsets(a, t, reinterpret_cast<unsigned *>(om_s), 4);
     stage_region(a, t, val_s, 4);
-    __syncthreads();
+    staging_done();
 
     const int K3 = 3 * a.K;
     const int q = threadIdx.x >> a.lanes_shift;
@@ -295,7 +317,7 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_offsets_tiled(TArgs a)
     const int px = q - py * a.tw;
     const int oy = t.oy0 + py, ox = t.ox0 + px;
     if (py < a.th && oy < geo.Ho && ox < geo.Wo) {
-        float *om = om_s + q * K3;   // overwritten in place with the gradients
+        float *om = om_s + q * a.om_dw;   // overwritten in place with the gradients
         const int ry0 = t.oy0 * geo.sh - geo.ph - a.R, rx0 = t.ox0 * geo.sw - geo.pw - a.R;
         const int chan_off = (t.g * a.Cg + chunk * DP) * 4;
         const unsigned cs = (unsigned)(geo.C * 4), rs = (unsigned)geo.W * cs;
@@ -408,7 +430,7 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_offsets_tiled(TArgs a)
                 const int ox2 = t.ox0 + px2;
                 if (ox2 < geo.Wo) {
                     const unsigned idx = (unsigned)(((t.n * geo.Ho + oy2) * geo.Wo + ox2) * a.P + t.g * K3 + j);
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, om_s[(py2 * a.tw + px2) * K3 + j]),
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, om_s[(py2 * a.tw + px2) * a.om_dw + j]),
                                                           r, idx * 4u, 0, 0);
                 }
             }
@@ -672,8 +694,11 @@ TArgs make_targs(const Problem &p, const TilePlan &tp)
     a.swz_mask = tp.swz_mask;
     a.swz_shift = tp.swz_shift;
     a.om_lds_vecs = tp.om_lds_bytes / 16;
+    a.om_dw = tp.om_dw;
     a.k3_magic = magic_for(3 * p.K);
     a.tw_magic = magic_for(tp.tw);
+    a.omdw_magic = magic_for(tp.om_dw);
+    a.rw_magic = magic_for(tp.rw);
     a.ch = tp.ch;
     a.cw = tp.cw;
     a.ctiles_y = tp.ctiles_y;
