@@ -316,99 +316,120 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_offsets_tiled(TArgs a)
     const int py = (int)divm((unsigned)q, a.tw_magic);
     const int px = q - py * a.tw;
     const int oy = t.oy0 + py, ox = t.ox0 + px;
-    if (py < a.th && oy < geo.Ho && ox < geo.Wo) {
-        float *om = om_s + q * a.om_dw;   // overwritten in place with the gradients
-        const int ry0 = t.oy0 * geo.sh - geo.ph - a.R, rx0 = t.ox0 * geo.sw - geo.pw - a.R;
-        const int chan_off = (t.g * a.Cg + chunk * DP) * 4;
-        const unsigned cs = (unsigned)(geo.C * 4), rs = (unsigned)geo.W * cs;
-        const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
-        const __amdgpu_buffer_rsrc_t gr = rsrc(a.gvalue, a.value_bytes);
-        const __amdgpu_buffer_rsrc_t gor = rsrc(a.gout, a.gout_bytes);
-        const int v0 = chunk * NV;
-        const unsigned pix_off = ((unsigned)((t.n * geo.Ho + oy) * geo.Wo + ox)) * cs + (unsigned)chan_off;
+    // every thread runs the k loop (far samples are written by whole waves);
+    // threads past the tile or the image only take part in that
+    const bool valid = py < a.th && oy < geo.Ho && ox < geo.Wo;
+    float *om = om_s + (valid ? q : 0) * a.om_dw;   // overwritten in place with the gradients
+    const int ry0 = t.oy0 * geo.sh - geo.ph - a.R, rx0 = t.ox0 * geo.sw - geo.pw - a.R;
+    const int chan_off = (t.g * a.Cg + chunk * DP) * 4;
+    const unsigned cs = (unsigned)(geo.C * 4), rs = (unsigned)geo.W * cs;
+    const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
+    const __amdgpu_buffer_rsrc_t gr = rsrc(a.gvalue, a.value_bytes);
+    const __amdgpu_buffer_rsrc_t gor = rsrc(a.gout, a.gout_bytes);
+    const int v0 = chunk * NV;
+    const unsigned pix_off = ((unsigned)((t.n * geo.Ho + oy) * geo.Wo + ox)) * cs + (unsigned)chan_off;
+    // lane's part in a far sample's grad_value update: corner lane / DP,
+    // channel lane % DP of the owner's DP channels
+    const int lane = threadIdx.x & 63;
+    const int my_corner = lane / DP, my_c = lane % DP;
+    const unsigned my_corner_off = (unsigned)(my_corner & 1) * cs + (unsigned)(my_corner >> 1) * rs + 4u * (unsigned)my_c;
 
-        float go[DP];
+    float go[DP];
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const f32x4 r = __builtin_bit_cast(f32x4, load16(gor, pix_off + 16 * v));
-            for (int e = 0; e < 4; ++e)
-                go[4 * v + e] = r[e];
+    for (int v = 0; v < NV; ++v) {
+        const f32x4 r = __builtin_bit_cast(f32x4, load16(gor, valid ? pix_off + 16 * v : kOutOfRange));
+        for (int e = 0; e < 4; ++e)
+            go[4 * v + e] = r[e];
+    }
+
+    for (int k = 0; k < a.K; ++k) {
+        const float dx = om[2 * k], dy = om[2 * k + 1], m = om[2 * a.K + k];
+        float gm = 0.0f, gw = 0.0f, gh = 0.0f;
+        const Loc l = locate(geo, oy, ox, k, dx, dy);
+        bool far = false;
+        unsigned far_off = 0;
+        float w00 = 0.0f, w01 = 0.0f, w10 = 0.0f, w11 = 0.0f;
+        if (valid && live(geo, l)) {
+            const Footprint f = footprint(geo, l);
+            u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
+            const bool nr = near_sample(f, l, a.R);
+            if (nr) {
+                const int p00 = (f.h0 - ry0) * a.rw + (f.w0 - rx0);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    v00[v] = val_s[vslot(a, p00, v0 + v)];
+                    v01[v] = val_s[vslot(a, p00 + 1, v0 + v)];
+                    v10[v] = val_s[vslot(a, p00 + a.rw, v0 + v)];
+                    v11[v] = val_s[vslot(a, p00 + a.rw + 1, v0 + v)];
+                }
+            } else {
+                far = true;
+                far_off = corner_offset(geo, t.n, f, 4, chan_off);
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    v00[v] = load16(vr, far_off + 16 * v);
+                    v01[v] = load16(vr, far_off + cs + 16 * v);
+                    v10[v] = load16(vr, far_off + rs + 16 * v);
+                    v11[v] = load16(vr, far_off + rs + cs + 16 * v);
+                }
+            }
+            // t_q = sum_c grad_out_c * v_q,c
+            float t00 = 0.0f, t01 = 0.0f, t10 = 0.0f, t11 = 0.0f;
+#pragma unroll
+            for (int c = 0; c < DP; ++c) {
+                t00 = __builtin_fmaf(go[c], Store<float>::get(v00, c), t00);
+                t01 = __builtin_fmaf(go[c], Store<float>::get(v01, c), t01);
+                t10 = __builtin_fmaf(go[c], Store<float>::get(v10, c), t10);
+                t11 = __builtin_fmaf(go[c], Store<float>::get(v11, c), t11);
+            }
+            if (far) {
+                // zero-extended image: dots of corners outside are 0
+                t00 = (f.r0 && f.c0) ? t00 : 0.0f;
+                t01 = (f.r0 && f.c1) ? t01 : 0.0f;
+                t10 = (f.r1 && f.c0) ? t10 : 0.0f;
+                t11 = (f.r1 && f.c1) ? t11 : 0.0f;
+                masked_weights(f, m, w00, w01, w10, w11);
+            }
+            const float lh = f.lh, lw = f.lw, hh = 1.0f - lh, hw = 1.0f - lw;
+            // d/dm: the sample; d/d loc of the bilinear sample inside the
+            // cell chosen by floor (right derivative at integers)
+            gm = hh * (hw * t00 + lw * t01) + lh * (hw * t10 + lw * t11);
+            gw = hh * (t01 - t00) + lh * (t11 - t10);
+            gh = hw * (t10 - t00) + lw * (t11 - t01);
         }
-
-        for (int k = 0; k < a.K; ++k) {
-            const float dx = om[2 * k], dy = om[2 * k + 1], m = om[2 * a.K + k];
-            float gm = 0.0f, gw = 0.0f, gh = 0.0f;
-            const Loc l = locate(geo, oy, ox, k, dx, dy);
-            if (live(geo, l)) {
-                const Footprint f = footprint(geo, l);
-                u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
-                const bool nr = near_sample(f, l, a.R);
-                if (nr) {
-                    const int p00 = (f.h0 - ry0) * a.rw + (f.w0 - rx0);
+        // grad_value of far samples: one device atomic per corner and
+        // channel, issued by the whole wave for one (sample, lane) at a time
+        // so that each instruction covers four contiguous corner rows
+        unsigned long long fm = __ballot(far);
+        while (fm) {
+            const int src = __builtin_ctzll(fm);
+            fm &= fm - 1;
+            const unsigned off = (unsigned)__builtin_amdgcn_readlane((int)far_off, src);
+            const float s00 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w00), src));
+            const float s01 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w01), src));
+            const float s10 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w10), src));
+            const float s11 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w11), src));
+            float g = 0.0f;
 #pragma unroll
-                    for (int v = 0; v < NV; ++v) {
-                        v00[v] = val_s[vslot(a, p00, v0 + v)];
-                        v01[v] = val_s[vslot(a, p00 + 1, v0 + v)];
-                        v10[v] = val_s[vslot(a, p00 + a.rw, v0 + v)];
-                        v11[v] = val_s[vslot(a, p00 + a.rw + 1, v0 + v)];
-                    }
-                } else {
-                    const unsigned off = corner_offset(geo, t.n, f, 4, chan_off);
-#pragma unroll
-                    for (int v = 0; v < NV; ++v) {
-                        v00[v] = load16(vr, off + 16 * v);
-                        v01[v] = load16(vr, off + cs + 16 * v);
-                        v10[v] = load16(vr, off + rs + 16 * v);
-                        v11[v] = load16(vr, off + rs + cs + 16 * v);
-                    }
-                }
-                // t_q = sum_c grad_out_c * v_q,c
-                float t00 = 0.0f, t01 = 0.0f, t10 = 0.0f, t11 = 0.0f;
-#pragma unroll
-                for (int c = 0; c < DP; ++c) {
-                    t00 = __builtin_fmaf(go[c], Store<float>::get(v00, c), t00);
-                    t01 = __builtin_fmaf(go[c], Store<float>::get(v01, c), t01);
-                    t10 = __builtin_fmaf(go[c], Store<float>::get(v10, c), t10);
-                    t11 = __builtin_fmaf(go[c], Store<float>::get(v11, c), t11);
-                }
-                if (!nr) {
-                    // zero-extended image: dots of corners outside are 0
-                    t00 = (f.r0 && f.c0) ? t00 : 0.0f;
-                    t01 = (f.r0 && f.c1) ? t01 : 0.0f;
-                    t10 = (f.r1 && f.c0) ? t10 : 0.0f;
-                    t11 = (f.r1 && f.c1) ? t11 : 0.0f;
-                    // far sample: its grad_value goes out with device atomics
-                    float w00, w01, w10, w11;
-                    masked_weights(f, m, w00, w01, w10, w11);
-                    const unsigned off = corner_offset(geo, t.n, f, 4, chan_off);
-#pragma unroll
-                    for (int c = 0; c < DP; ++c) {
-                        const unsigned o = off + 4 * c;
-                        dcnv4_buffer_atomic_fadd(w00 * go[c], gr, o, 0, 0);
-                        dcnv4_buffer_atomic_fadd(w01 * go[c], gr, o + cs, 0, 0);
-                        dcnv4_buffer_atomic_fadd(w10 * go[c], gr, o + rs, 0, 0);
-                        dcnv4_buffer_atomic_fadd(w11 * go[c], gr, o + rs + cs, 0, 0);
-                    }
-                }
-                const float lh = f.lh, lw = f.lw, hh = 1.0f - lh, hw = 1.0f - lw;
-                // d/dm: the sample; d/d loc of the bilinear sample inside the
-                // cell chosen by floor (right derivative at integers)
-                gm = hh * (hw * t00 + lw * t01) + lh * (hw * t10 + lw * t11);
-                gw = hh * (t01 - t00) + lh * (t11 - t10);
-                gh = hw * (t10 - t00) + lw * (t11 - t01);
+            for (int c = 0; c < DP; ++c) {
+                const float gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, go[c]), src));
+                g = my_c == c ? gc : g;
             }
-            for (int d = 1; d < lanes; d <<= 1) {
-                gm += __shfl_xor(gm, d);
-                gw += __shfl_xor(gw, d);
-                gh += __shfl_xor(gh, d);
-            }
-            if (chunk == 0) {
-                // the lanes of this pixel have read entry k already
-                const float sm = geo.scale * m;
-                om[2 * k] = sm * gw;
-                om[2 * k + 1] = sm * gh;
-                om[2 * a.K + k] = gm;
-            }
+            const float w = my_corner == 0 ? s00 : my_corner == 1 ? s01 : my_corner == 2 ? s10 : s11;
+            if (my_corner < 4 && w != 0.0f)
+                dcnv4_buffer_atomic_fadd(w * g, gr, off + my_corner_off, 0, 0);
+        }
+        for (int d = 1; d < lanes; d <<= 1) {
+            gm += __shfl_xor(gm, d);
+            gw += __shfl_xor(gw, d);
+            gh += __shfl_xor(gh, d);
+        }
+        if (valid && chunk == 0) {
+            // the lanes of this pixel have read entry k already
+            const float sm = geo.scale * m;
+            om[2 * k] = sm * gw;
+            om[2 * k + 1] = sm * gh;
+            om[2 * a.K + k] = gm;
         }
     }
     __syncthreads();
