@@ -207,33 +207,59 @@ bool pow2(int v)
     return v > 0 && (v & (v - 1)) == 0;
 }
 
-int ilog2(int v)
+constexpr int kRowSlots = 512;        // a staged LDS row spans at most 8 x 64 slots
+constexpr int kMaxTiledK = 25;        // grid points of the tiled kernels
+constexpr int kTiledMaxLds = 80 * 1024;
+constexpr int kLdsPerCu = 160 * 1024;
+constexpr int kTileThreads = 512;
+constexpr int kCellTileLds = 40 * 1024;   // four cell-tile blocks per CU
+constexpr int kMaxCellBins = 768;     // (ch + 1) * (cw + 1) corner-cell bins
+constexpr int kCellBinBytes = (2 * kMaxCellBins + 8) * 4;   // counters, prefix, scan scratch
+
+// Staged offset/mask dwords per pixel: a group's 3K entries, widened to whole
+// dwords (2-byte entries of odd groups start mid-dword).
+int staged_om_dwords(const Problem &p, int elem)
 {
-    int s = 0;
-    while ((1 << s) < v)
-        ++s;
-    return s;
+    return elem == 4 ? 3 * p.K : (3 * p.K + 2) / 2;
+}
+
+int region_rows(const Problem &p, int th, int R)
+{
+    return (th - 1) * p.sh + (p.kh - 1) * p.dh + 2 * R + 2;
+}
+
+int region_cols(const Problem &p, int tw, int R)
+{
+    return (tw - 1) * p.sw + (p.kw - 1) * p.dw + 2 * R + 2;
 }
 
 // Output tile for halo radius R: th x tw pixels with `lanes` threads per
-// pixel, at most 256 threads and at least two waves (unless the map is
-// smaller).  Cost, in 16-byte LDS operations: corner gathers of every wave
-// slot (partial waves count in full) plus three per staged region vector.
-void choose_out_tile(const Problem &p, int lanes, int nvl, int nvp, int R, int *th, int *tw)
+// pixel, at most kTileThreads threads, staged rows within the row limit.
+// Modelled time: per block, a lane-sample costs ~40 instructions plus one
+// FMA per channel and corner, a staged region slot ~8; blocks run
+// concurrently until 24 waves share a CU (fewer when LDS limits them).
+bool choose_out_tile(const Problem &p, int lanes, int dp, int ps, int om_dw, int R, int lds_budget, int elem,
+                     int *th, int *tw)
 {
-    const long min_threads = std::min<long>(128, (long)p.Ho * p.Wo * lanes);
     double best = -1;
     for (int w = 1; w <= 64 && w <= p.Wo; ++w) {
+        if (w * om_dw > kRowSlots || region_cols(p, w, R) * ps > kRowSlots)
+            break;
         for (int h = 1; h <= 64 && h <= p.Ho; ++h) {
             const int threads = h * w * lanes;
-            if (threads > 256)
+            if (threads > kTileThreads)
                 break;
-            if (threads < min_threads)
+            const int rh = region_rows(p, h, R), rw = region_cols(p, w, R);
+            const int om = (h * w * om_dw * 4 + 15) / 16 * 16;
+            const int lds = om + rh * rw * ps * 16;
+            if (lds > lds_budget)
                 continue;
+            const int waves = (threads + 63) / 64;
+            const int per_cu = std::min(kLdsPerCu / lds, 32 / waves);
+            const double occ = std::min(1.0, per_cu * waves / 24.0);
             const double blocks = (double)((p.Ho + h - 1) / h) * ((p.Wo + w - 1) / w);
-            const double rh = (h - 1) * p.sh + (p.kh - 1) * p.dh + 2 * R + 2;
-            const double rw = (w - 1) * p.sw + (p.kw - 1) * p.dw + 2 * R + 2;
-            const double cost = blocks * ((threads + 63) / 64) * 64.0 * p.K * 4 * nvl + blocks * rh * rw * nvp * 3;
+            const double work = waves * 64.0 * p.K * (40 + 4 * dp) + (double)rh * rw * ps * 8;
+            const double cost = blocks * work / occ;
             if (best < 0 || cost < best) {
                 best = cost;
                 *th = h;
@@ -241,22 +267,38 @@ void choose_out_tile(const Problem &p, int lanes, int nvl, int nvp, int R, int *
             }
         }
     }
+    return best >= 0;
+}
+
+// Upper bound of the source window width of a cell tile cw cells wide.
+int window_cols(const Problem &p, int cw, int R)
+{
+    return (cw + 2 * R + (p.kw - 1) * p.dw + 1) / p.sw + 2;
+}
+
+int window_rows(const Problem &p, int ch, int R)
+{
+    return (ch + 2 * R + (p.kh - 1) * p.dh + 1) / p.sh + 2;
 }
 
 // Cell tile of the grad_value kernel (one thread per cell, at most 256):
-// minimise the samples evaluated, i.e. blocks x source pixels x K, plus a
-// fixed per-block cost.
-void choose_cell_tile(const Problem &p, int R, int *ch, int *cw)
+// minimise the samples evaluated, i.e. blocks x window pixels x K, plus a
+// per-batch cost; the window's rows must fit a batch of src_cap sources and
+// the staged row limit.
+bool choose_cell_tile(const Problem &p, int R, int src_cap, int gps, int *ch, int *cw)
 {
     double best = -1;
     for (int w = 1; w <= 256 && w <= p.W; ++w) {
+        const int sw = window_cols(p, w, R);
+        if (sw > src_cap || sw * gps > kRowSlots)
+            break;
         for (int h = 1; h <= 256 && h <= p.H; ++h) {
-            if (h * w > 256)
+            if (h * w > 256 || (h + 1) * (w + 1) > kMaxCellBins)
                 break;
             const double blocks = (double)((p.H + h - 1) / h) * ((p.W + w - 1) / w);
-            const double sh = (double)(h + (p.kh - 1) * p.dh + 2 * R + 2) / p.sh + 1;
-            const double sw = (double)(w + (p.kw - 1) * p.dw + 2 * R + 2) / p.sw + 1;
-            const double cost = blocks * (sh * sw * p.K + 2048);
+            const int sh = window_rows(p, h, R);
+            const double batches = std::ceil((double)sh / (src_cap / sw));
+            const double cost = blocks * ((double)sh * sw * p.K + 1024.0 * batches);
             if (best < 0 || cost < best) {
                 best = cost;
                 *ch = h;
@@ -264,34 +306,35 @@ void choose_cell_tile(const Problem &p, int R, int *ch, int *cw)
             }
         }
     }
+    return best >= 0;
 }
 
-// Fill the LDS region geometry for halo radius R; returns total LDS bytes.
+// Fill the LDS geometry for halo radius R; returns total LDS bytes.
 int tile_lds(const Problem &p, TilePlan *tp, int R, int elem)
 {
     tp->R = R;
-    tp->rh = (tp->th - 1) * p.sh + (p.kh - 1) * p.dh + 2 * R + 2;
-    tp->rw = (tp->tw - 1) * p.sw + (p.kw - 1) * p.dw + 2 * R + 2;
-    // a group's 3K entries, widened to whole dwords (2-byte entries may start
-    // mid-dword)
-    tp->om_dw = elem == 4 ? 3 * p.K : (3 * p.K + 2) / 2;
+    tp->rh = region_rows(p, tp->th, R);
+    tp->rw = region_cols(p, tp->tw, R);
+    tp->om_dw = staged_om_dwords(p, elem);
     const int om = tp->th * tp->tw * tp->om_dw * 4;
     tp->om_lds_bytes = (om + 15) / 16 * 16;
-    tp->lds_bytes = tp->om_lds_bytes + tp->rh * tp->rw * tp->nvp * 16;
+    tp->lds_bytes = tp->om_lds_bytes + tp->rh * tp->rw * tp->ps * 16;
     return tp->lds_bytes;
 }
 
-constexpr int kTiledMaxLds = 80 * 1024;
-
 int plan_tiled_common(const Problem &p, int elem, int r_max, int lds_budget, TilePlan *tp)
 {
-    if ((p.Cg * elem) % 16 != 0)
+    if ((p.Cg * elem) % 16 != 0 || p.K > kMaxTiledK)
         return DCNV4_ERR_UNSUPPORTED;
     tp->nvp = p.Cg * elem / 16;
     if (!pow2(tp->nvp))
         return DCNV4_ERR_UNSUPPORTED;
+    // an odd pixel stride spreads random pixel reads over the 16-byte banks
+    tp->ps = tp->nvp | 1;
+    // 8 channels per lane: two lanes share a 16-channel pixel, which doubles
+    // the waves that hide LDS latency at little extra per-sample work
     int dp = 0;
-    for (int cand : {16, 8, 4}) {
+    for (int cand : {8, 16, 4}) {
         if (p.Cg % cand == 0 && (cand * elem) % 16 == 0) {
             dp = cand;
             break;
@@ -303,21 +346,18 @@ int plan_tiled_common(const Problem &p, int elem, int r_max, int lds_budget, Til
     tp->lanes = p.Cg / dp;
     if (!pow2(tp->lanes) || tp->lanes > 64)
         return DCNV4_ERR_UNSUPPORTED;
-    // 16 LDS banks of 16 bytes: rotate the vector index by higher pixel bits
-    tp->swz_mask = (tp->nvp >= 2) ? (tp->nvp < 16 ? tp->nvp : 16) - 1 : 0;
-    tp->swz_shift = tp->nvp < 16 ? ilog2(16 / tp->nvp) : 0;
-    const int nvl = dp * elem / 16;
-    // the largest halo radius whose best tile fits the LDS budget
+    const int om_dw = staged_om_dwords(p, elem);
+    // the largest halo radius that has a tile within the LDS budget
     for (int R = r_max; R >= 1; --R) {
-        choose_out_tile(p, tp->lanes, nvl, tp->nvp, R, &tp->th, &tp->tw);
-        if (tile_lds(p, tp, R, elem) <= lds_budget) {
-            // whole waves: the kernels' staging loops stride by 64 lanes
-            tp->threads = (tp->th * tp->tw * tp->lanes + 63) / 64 * 64;
-            tp->tiles_y = (p.Ho + tp->th - 1) / tp->th;
-            tp->tiles_x = (p.Wo + tp->tw - 1) / tp->tw;
-            tp->images_per_launch = 0;
-            return DCNV4_OK;
-        }
+        if (!choose_out_tile(p, tp->lanes, dp, tp->ps, om_dw, R, lds_budget, elem, &tp->th, &tp->tw))
+            continue;
+        tile_lds(p, tp, R, elem);
+        // whole waves: the staging loops take rows per wave
+        tp->threads = (tp->th * tp->tw * tp->lanes + 63) / 64 * 64;
+        tp->tiles_y = (p.Ho + tp->th - 1) / tp->th;
+        tp->tiles_x = (p.Wo + tp->tw - 1) / tp->tw;
+        tp->images_per_launch = 0;
+        return DCNV4_OK;
     }
     return DCNV4_ERR_UNSUPPORTED;
 }
@@ -327,10 +367,7 @@ int plan_tiled_common(const Problem &p, int elem, int r_max, int lds_budget, Til
 int plan_forward_tiled(const Problem &p, TilePlan *tp)
 {
     *tp = TilePlan{};
-    // fp32 rows are twice as wide: a smaller halo keeps two blocks per CU
-    const int r_max = p.elem == 4 ? 5 : 8;
-    const int budget = p.elem == 4 ? kTiledMaxLds : 64 * 1024;
-    int st = plan_tiled_common(p, p.elem, r_max, budget, tp);
+    const int st = plan_tiled_common(p, p.elem, 5, kTiledMaxLds, tp);
     if (st != DCNV4_OK)
         return st;
     tp->images_per_launch = (int)(kMaxBytesPerLaunch / image_bytes_max(p, false));
@@ -347,17 +384,19 @@ int plan_backward_tiled(const Problem &p, TilePlan *tp)
     int st = plan_tiled_common(p, 4, 5, kTiledMaxLds, tp);
     if (st != DCNV4_OK)
         return st;
-    // cell tiles for grad_value: one thread per cell, at most 256 cells
-    choose_cell_tile(p, tp->R, &tp->ch, &tp->cw);
+    // cell tiles for grad_value: LDS holds the bins, up to src_cap*K sorted
+    // samples of 16 bytes and src_cap staged grad_output pixels
+    tp->gps = (p.Cg / 4) | 1;
+    tp->rec_offset = kCellBinBytes;
+    tp->src_cap = std::min(256, (kCellTileLds - kCellBinBytes) / (16 * (p.K + tp->gps)));
+    if (tp->src_cap < 1)
+        return DCNV4_ERR_UNSUPPORTED;
+    if (!choose_cell_tile(p, tp->R, tp->src_cap, tp->gps, &tp->ch, &tp->cw))
+        return DCNV4_ERR_UNSUPPORTED;
+    tp->gs_offset = tp->rec_offset + tp->src_cap * p.K * 16;
+    tp->splat_lds_bytes = tp->gs_offset + tp->src_cap * tp->gps * 16;
     tp->ctiles_y = (p.H + tp->ch - 1) / tp->ch;
     tp->ctiles_x = (p.W + tp->cw - 1) / tp->cw;
-    // a batch holds at most 1024 samples (4 per thread), i.e. 4096 corner
-    // records, and at most 128 source pixels (their grad_out rows sit in LDS)
-    tp->src_batch = std::min(1024 / p.K, 128);
-    if (tp->src_batch < 1)
-        return DCNV4_ERR_UNSUPPORTED;
-    tp->max_records = 4096;
-    tp->splat_lds_bytes = 3 * 256 * 4 + 16 + tp->max_records * 8 + tp->src_batch * p.Cg * 4;
     tp->images_per_launch = (int)(kMaxBytesPerLaunch / image_bytes_max(p, true));
     return DCNV4_OK;
 }

@@ -50,16 +50,18 @@ struct TilePlan {
     int R;
     int rh, rw;          // LDS value region, pixels
     int nvp;             // 16-byte vectors per region pixel (Cg * elem / 16)
-    int swz_mask, swz_shift;
+    int ps;              // LDS pixel stride, 16-byte slots (nvp rounded up to odd)
     int om_dw;           // staged dwords per pixel: one group's 3K entries, dword-aligned
     int om_lds_bytes;    // LDS for the staged offset/mask entries (16-byte multiple)
     int lds_bytes;       // total LDS of an output-tile block
     // cell tiles (backward grad_value): ch x cw input cells of one (image, group)
     int ch, cw;
     int ctiles_y, ctiles_x;
-    int src_batch;       // source pixels per batch (src_batch * K * 4 records at most)
-    int max_records;
-    int splat_lds_bytes;
+    int src_cap;         // source pixels per batch (whole source rows)
+    int gps;             // LDS stride of a staged grad_output pixel, 16-byte slots
+    int rec_offset;      // LDS byte offset of the sorted sample records
+    int gs_offset;       // LDS byte offset of the staged grad_output rows
+    int splat_lds_bytes; // total LDS of a cell-tile block
     int images_per_launch;
 };
 

@@ -9,23 +9,33 @@
 // these re-reads (walkthrough section 2.2; blog "DCNv4架构解析", section
 // "并行计算架构设计").  On CDNA4, 128-bit gathers through the texture path
 // cost one cache-tag lookup per distinct line and top out near 37 B/clk/CU,
-// while random 128-bit LDS reads reach ~77 B/clk/CU when reads are spread
-// over all banks.  So a block owns a 2-D tile of output pixels of one (image,
-// group), stages the group's value rows of the tile plus a halo of R pixels
-// into LDS once (zeros outside the image: the zero-extended image), and
-// gathers corners from LDS.  A sample whose integer displacement leaves the
-// halo (|floor(loc) - grid position| > R on an axis) is "far" and reads its
-// corners from global memory instead.
+// while random 128-bit LDS reads reach ~77 B/clk/CU when a pixel's vectors
+// start on an odd 16-byte slot.  So a block owns a 2-D tile of output pixels
+// of one (image, group), stages the group's value rows of the tile plus a
+// halo of R pixels into LDS once (zeros outside the image: the zero-extended
+// image), and gathers corners from LDS.
+//
+// A sample is "near" when its integer displacement is within R pixels on
+// both axes (|floor(loc) - grid position| <= R); its four corners then lie in
+// the staged region, so it needs no bounds test at all (corners outside the
+// image read the staged zeros).  Other samples are "far": the main loop only
+// records them in a bit mask and a second loop reads their corners from
+// global memory, so the near loop never waits on global loads.
+//
+// Staging uses direct-to-LDS buffer loads, one LDS row per group of wave
+// instructions: slot j of every row comes from the row's base plus a
+// per-lane offset that is the same for all rows, so a slot costs one add.
 //
 // Backward: device-scope fp32 atomics on this multi-XCD part are resolved
 // beyond L2 and LDS fp32 atomics are slow, so grad_value of near samples is
 // computed without float atomics: a block owns a tile of *input* cells,
-// enumerates the near samples of the output pixels that can reach it, sorts
-// their corner contributions by destination cell (a counting sort with
-// integer LDS atomics) and sums each cell's list in registers, then writes
-// the tile with plain stores.  grad_offset_mask is forward-shaped; it also
-// adds the contributions of far samples to grad_value with device atomics,
-// after the cell-tile kernel has written every cell.
+// evaluates the near samples of the output pixels that can reach it, sorts
+// them by their top-left corner cell (a counting sort with integer LDS
+// atomics), and every cell sums in registers the lists of the four corner
+// cells that reach it; the tile is then written with plain stores.
+// grad_offset_mask is forward-shaped; it also adds the contributions of far
+// samples to grad_value with device atomics (one 64-lane instruction per far
+// sample), after the cell-tile kernel has written every cell.
 
 #include "dcnv4_device.h"
 #include "dcnv4_internal.h"
@@ -39,6 +49,11 @@ namespace {
 
 using namespace dev;
 
+constexpr int kMaxRowChunks = 8;      // a staged row spans at most 8 x 64 slots
+constexpr int kMaxTileThreads = 512;  // threads of an output-tile block
+constexpr int kMaxBins = 768;         // corner-cell bins of a cell tile (3 per thread)
+constexpr unsigned kOutOfRange = 0x80000000u;   // >= any buffer size used here
+
 struct TArgs {
     Geom geo;
     const void *value;
@@ -48,18 +63,22 @@ struct TArgs {
     float *gvalue;
     float *gom;
     int G, Cg, K, P;
+    unsigned kh_magic;           // ceil(2^32 / kernel_h)
+    unsigned k3_magic;           // ceil(2^32 / (3K))
     // output tiles
     int th, tw, tiles_y, tiles_x, lanes_shift;
-    int R, rh, rw, nvp_shift, swz_mask, swz_shift;
-    int om_lds_vecs;             // 16-byte LDS vectors reserved for the offset/mask stage
-    int om_dw;                   // staged dwords per pixel (offset/mask entries of one group)
-    unsigned k3_magic;           // ceil(2^32 / (3K)): e / (3K) == mulhi(e, k3_magic) for small e
-    unsigned tw_magic;           // ceil(2^32 / tw)
-    unsigned omdw_magic;         // ceil(2^32 / om_dw)
-    unsigned rw_magic;           // ceil(2^32 / rw)
+    int R, rh, rw;               // halo radius; LDS value region, pixels
+    int ps, nvp;                 // LDS pixel stride; data vectors per pixel (16-byte units)
+    unsigned ps_magic;
+    int om_dw;                   // staged dwords per pixel
+    unsigned om_dw_magic, tw_magic;
+    int om_lds_bytes;
     // cell tiles (backward grad_value)
-    int ch, cw, ctiles_y, ctiles_x, src_batch;
-    unsigned k_magic;            // ceil(2^32 / K)
+    int ch, cw, ctiles_y, ctiles_x;
+    int src_cap;                 // source pixels per batch
+    int gps;                     // LDS stride of a staged grad_output pixel, 16-byte units
+    unsigned gps_magic;
+    int rec_offset, gs_offset;   // LDS byte offsets of the record list and the grad_output rows
     // buffer sizes of this launch, bytes
     int value_bytes, om_bytes, out_bytes, gout_bytes;
 };
@@ -69,13 +88,6 @@ struct TArgs {
 __device__ __forceinline__ unsigned divm(unsigned e, unsigned magic)
 {
     return magic ? __umulhi(e, magic) : e;
-}
-
-// LDS vector slot of vector v of region pixel p.  XOR-ing v with higher
-// pixel bits spreads the reads of random pixels over all LDS banks.
-__device__ __forceinline__ int vslot(const TArgs &a, int p, int v)
-{
-    return (p << a.nvp_shift) + (v ^ ((p >> a.swz_shift) & a.swz_mask));
 }
 
 struct Tile {
@@ -99,172 +111,267 @@ __device__ __forceinline__ Tile out_tile(const TArgs &a)
     return t;
 }
 
-template <typename T>
-__device__ __forceinline__ T load_elem(__amdgpu_buffer_rsrc_t r, unsigned off);
-template <>
-__device__ __forceinline__ float load_elem<float>(__amdgpu_buffer_rsrc_t r, unsigned off)
+// Location of grid point k for a per-lane k (the kernel_h division by
+// multiply-high); same arithmetic as the main loops.
+__device__ __forceinline__ Loc locate_lane(const TArgs &a, int ho, int wo, int k, float dx, float dy)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    const Geom &g = a.geo;
+    const int kk = k + ((g.rc && k >= g.kc) ? 1 : 0);
+    const int i = (int)divm((unsigned)kk, a.kh_magic);
+    const int j = kk - i * g.kh;
+    Loc l;
+    l.bh = ho * g.sh - g.ph + j * g.dh;
+    l.bw = wo * g.sw - g.pw + i * g.dw;
+    l.w = __builtin_fmaf(g.scale, dx, (float)l.bw);
+    l.h = __builtin_fmaf(g.scale, dy, (float)l.bh);
+    return l;
 }
 
-// Staging uses direct-to-LDS buffer loads: lane t of a wave instruction
-// writes its 4 or 16 bytes at LDS base + t*size, a source offset outside the
-// buffer writes zeros, and inactive lanes write nothing.  Every wave walks
-// contiguous 64-slot chunks of the LDS image, computes the source of each
-// slot, and issues all loads before a single wait (the data never passes
-// through registers).  Blocks are whole waves (the host rounds the thread
-// count up to a multiple of 64; lanes past the tile only help staging).
-
-constexpr unsigned kOutOfRange = 0x80000000u;   // >= any buffer size used here
+// ---- staging ----------------------------------------------------------------
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void *lds_chunk, unsigned off)
+// Direct-to-LDS buffer load: lane t of the wave writes its SZ bytes at
+// lds + t*SZ; a source offset outside the buffer writes zeros, inactive lanes
+// write nothing.
+template <int SZ>
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, void *lds, unsigned off)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_chunk, 16, off, 0, 0, 0);
+    static_assert(SZ == 4 || SZ == 16, "slot size");
+    if constexpr (SZ == 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 4, off, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, off, 0, 0, 0);
 }
 
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, void *lds_chunk, unsigned off)
+// Copy `nrows` rows of `row_slots` SZ-byte slots into LDS (row rr at slot
+// rr*row_slots).  Slot j of row rr is read from row_off(rr) + lane_off[j/64]
+// of lane j%64, or is zero when either is kOutOfRange.  Waves take whole rows.
+template <int SZ, typename RowOff>
+__device__ __forceinline__ void stage_rows(__amdgpu_buffer_rsrc_t r, char *lds, int nrows, int row_slots,
+                                           const unsigned (&lane_off)[kMaxRowChunks], RowOff row_off)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds_chunk, 4, off, 0, 0, 0);
-}
-
-// Offset/mask entries of group g for the tile's pixels, in dwords: pixel q
-// owns om_dw dwords starting at dword q*om_dw; they cover its 3K elements
-// from the dword-aligned element below g*3K (for 2-byte elements the block's
-// entries start om_par elements into each pixel's slice).  Pixels outside the
-// image read zeros.
-__device__ void stage_offsets(const TArgs &a, const Tile &t, unsigned *om_s, int es)
-{
-    const Geom &geo = a.geo;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = (blockDim.x + 63) >> 6;
-    const int total = a.th * a.tw * a.om_dw;
-    const int epd = 4 / es;   // elements per dword
-    const __amdgpu_buffer_rsrc_t r = rsrc(a.om, a.om_bytes);
-    for (int c0 = wave * 64; c0 < total; c0 += nwaves * 64) {
-        const int i = c0 + lane;
-        if (i < total) {
-            const int q = (int)divm((unsigned)i, a.omdw_magic);
-            const int d = i - q * a.om_dw;
-            const int py = (int)divm((unsigned)q, a.tw_magic);
-            const int px = q - py * a.tw;
-            const int oy = t.oy0 + py, ox = t.ox0 + px;
-            unsigned off = kOutOfRange;
-            if (oy < geo.Ho && ox < geo.Wo) {
-                const unsigned e0 = (unsigned)(((t.n * geo.Ho + oy) * geo.Wo + ox) * a.P + t.g * 3 * a.K);
-                off = (e0 / (unsigned)epd + (unsigned)d) * 4u;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    for (int rr = wave; rr < nrows; rr += nwaves) {
+        const unsigned base = row_off(rr);
+        char *dst = lds + rr * row_slots * SZ;
+#pragma unroll
+        for (int c = 0; c < kMaxRowChunks; ++c) {
+            if (c * 64 < row_slots && c * 64 + lane < row_slots) {
+                const unsigned lo = lane_off[c];
+                dma<SZ>(r, dst + c * 64 * SZ, (base == kOutOfRange || lo == kOutOfRange) ? kOutOfRange : base + lo);
             }
-            dma4(r, om_s + c0, off);
         }
     }
 }
 
-// Value rows of group g for the tile plus a halo: region pixel (rr, cc) is
-// image pixel (ry0 + rr, rx0 + cc); zeros outside the image.  Slot s holds
-// vector (s & (nvp-1)) ^ swizzle(p) of region pixel p = s / nvp (see vslot).
-__device__ void stage_region(const TArgs &a, const Tile &t, u32x4 *val_s, int es)
-{
-    const Geom &geo = a.geo;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = (blockDim.x + 63) >> 6;
-    const int ry0 = t.oy0 * geo.sh - geo.ph - a.R, rx0 = t.ox0 * geo.sw - geo.pw - a.R;
-    const int total = (a.rh * a.rw) << a.nvp_shift;
-    const int vmask = (1 << a.nvp_shift) - 1;
-    const unsigned cs = (unsigned)(geo.C * es), goff = (unsigned)(t.g * a.Cg * es);
-    const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
-    for (int c0 = wave * 64; c0 < total; c0 += nwaves * 64) {
-        const int s = c0 + lane;
-        if (s < total) {
-            const int p = s >> a.nvp_shift;
-            const int v = (s & vmask) ^ ((p >> a.swz_shift) & a.swz_mask);
-            const int rr = (int)divm((unsigned)p, a.rw_magic);
-            const int cc = p - rr * a.rw;
-            const int y = ry0 + rr, x = rx0 + cc;
-            unsigned off = kOutOfRange;
-            if ((unsigned)y < (unsigned)geo.H && (unsigned)x < (unsigned)geo.W)
-                off = (unsigned)((t.n * geo.H + y) * geo.W + x) * cs + goff + 16u * (unsigned)v;
-            dma16(vr, val_s + c0, off);
-        }
-    }
-}
-
-// Wait for this thread's direct-to-LDS loads, then for the whole block.
+// Wait for this thread's direct-to-LDS and buffer loads, then for the block.
 __device__ __forceinline__ void staging_done()
 {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 }
 
-// Near test: the integer displacement of the sample is within R pixels.
-__device__ __forceinline__ bool near_sample(const Footprint &f, const Loc &l, int R)
+// Offset/mask entries of group g for the tile's pixels, in dwords: pixel
+// q = py*tw + px owns om_dw dwords from dword q*om_dw, covering its 3K
+// entries from the dword that holds entry 0 (2-byte entries of odd groups
+// start one element into it).  Value rows of group g for the tile plus the
+// halo: region pixel (rr, cc) is image pixel (ry0 + rr, rx0 + cc) and starts
+// at 16-byte slot (rr*rw + cc)*ps; zeros outside the image.
+__device__ __forceinline__ void stage_tile(const TArgs &a, const Tile &t, char *om_s, char *val_s, int es)
 {
-    return (unsigned)(f.h0 - l.bh + R) <= (unsigned)(2 * R) && (unsigned)(f.w0 - l.bw + R) <= (unsigned)(2 * R);
+    const Geom &geo = a.geo;
+    const int lane = threadIdx.x & 63;
+    {
+        unsigned lo[kMaxRowChunks];
+        const int row_slots = a.tw * a.om_dw;
+        const unsigned gofs = (unsigned)((t.g * 3 * a.K * es) & ~3);
+#pragma unroll
+        for (int c = 0; c < kMaxRowChunks; ++c) {
+            lo[c] = kOutOfRange;
+            if (c * 64 < row_slots) {
+                const int j = c * 64 + lane;
+                const int px = (int)divm((unsigned)j, a.om_dw_magic);
+                const int d = j - px * a.om_dw;
+                const int ox = t.ox0 + px;
+                if (px < a.tw && ox < geo.Wo)
+                    lo[c] = (unsigned)(ox * a.P * es) + gofs + 4u * (unsigned)d;
+            }
+        }
+        const unsigned row_bytes = (unsigned)(geo.Wo * a.P * es);
+        const int row0 = t.n * geo.Ho + t.oy0;
+        const int rows_in = geo.Ho - t.oy0;
+        stage_rows<4>(rsrc(a.om, a.om_bytes), om_s, a.th, row_slots, lo, [&](int rr) {
+            return rr < rows_in ? (unsigned)(row0 + rr) * row_bytes : kOutOfRange;
+        });
+    }
+    {
+        unsigned lo[kMaxRowChunks];
+        const int row_slots = a.rw * a.ps;
+        const int rx0 = t.ox0 * geo.sw - geo.pw - a.R;
+        const unsigned cs = (unsigned)(geo.C * es), goff = (unsigned)(t.g * a.Cg * es);
+#pragma unroll
+        for (int c = 0; c < kMaxRowChunks; ++c) {
+            lo[c] = kOutOfRange;
+            if (c * 64 < row_slots) {
+                const int j = c * 64 + lane;
+                const int cc = (int)divm((unsigned)j, a.ps_magic);
+                const int v = j - cc * a.ps;
+                const int x = rx0 + cc;
+                if (v < a.nvp && cc < a.rw && (unsigned)x < (unsigned)geo.W)
+                    lo[c] = (unsigned)x * cs + goff + 16u * (unsigned)v;
+            }
+        }
+        const int ry0 = t.oy0 * geo.sh - geo.ph - a.R;
+        const unsigned row_bytes = (unsigned)geo.W * cs;
+        stage_rows<16>(rsrc(a.value, a.value_bytes), val_s, a.rh, row_slots, lo, [&](int rr) {
+            const int y = ry0 + rr;
+            return (unsigned)y < (unsigned)geo.H ? (unsigned)(t.n * geo.H + y) * row_bytes : kOutOfRange;
+        });
+    }
+}
+
+// Per-pixel constants of the near test and of LDS corner addresses.
+struct NearFrame {
+    float bh0, bw0;   // integer base of grid point (0, 0), as floats
+    float Rf;
+    int rowb, colb;   // LDS bytes per region row / pixel
+    int abase;        // LDS byte address of image pixel (0, 0) relative to the region
+};
+
+__device__ __forceinline__ NearFrame near_frame(const TArgs &a, const Tile &t, int oy, int ox)
+{
+    const Geom &geo = a.geo;
+    NearFrame f;
+    f.bh0 = (float)(oy * geo.sh - geo.ph);
+    f.bw0 = (float)(ox * geo.sw - geo.pw);
+    f.Rf = (float)a.R;
+    f.colb = a.ps * 16;
+    f.rowb = a.rw * f.colb;
+    const int ry0 = t.oy0 * geo.sh - geo.ph - a.R, rx0 = t.ox0 * geo.sw - geo.pw - a.R;
+    f.abase = -(ry0 * f.rowb + rx0 * f.colb);
+    return f;
+}
+
+// One sample in the main loops: location, floor, near test (false for NaN),
+// and the LDS byte address of the top-left corner when near (0 otherwise).
+struct NearSample {
+    float lh, lw, fh, fw;
+    bool nr;
+    int addr;
+};
+
+__device__ __forceinline__ NearSample near_sample(const NearFrame &f, float scale, float bh, float bw, float dx,
+                                                  float dy)
+{
+    NearSample s;
+    s.lh = __builtin_fmaf(scale, dy, bh);
+    s.lw = __builtin_fmaf(scale, dx, bw);
+    s.fh = __builtin_floorf(s.lh);
+    s.fw = __builtin_floorf(s.lw);
+    // fh - bh and fw - bw are differences of integers below 2^24 (or huge)
+    s.nr = __builtin_fabsf(s.fh - bh) <= f.Rf && __builtin_fabsf(s.fw - bw) <= f.Rf;
+    // near: |fh|, |fw| are below 2^23, so 24-bit multiplies are exact
+    const int addr = __mul24((int)s.fh, f.rowb) + __mul24((int)s.fw, f.colb) + f.abase;
+    s.addr = s.nr ? addr : 0;
+    return s;
+}
+
+__device__ __forceinline__ bool live_loc(const Geom &g, float lh, float lw)
+{
+    return lh >= -1.0f && lh < (float)g.H && lw >= -1.0f && lw < (float)g.W;
 }
 
 // ---- forward ---------------------------------------------------------------
 
 template <typename T, int DP>
-__global__ __launch_bounds__(256) void dcnv4_fwd_tiled(TArgs a)
+__global__ __launch_bounds__(kMaxTileThreads) void dcnv4_fwd_tiled(TArgs a)
 {
     extern __shared__ u32x4 smem[];
-    constexpr int NV = DP * (int)sizeof(T) / 16;
+    constexpr int es = (int)sizeof(T);
+    constexpr int NV = DP * es / 16;
     const Geom &geo = a.geo;
     const Tile t = out_tile(a);
-    unsigned *om_s = reinterpret_cast<unsigned *>(smem);
-    u32x4 *val_s = smem + a.om_lds_vecs;
-    stage_offsets(a, t, om_s, (int)sizeof(T));
-    stage_region(a, t, val_s, (int)sizeof(T));
+    char *om_s = reinterpret_cast<char *>(smem);
+    char *val_s = om_s + a.om_lds_bytes;
+    stage_tile(a, t, om_s, val_s, es);
     staging_done();
 
     const int q = threadIdx.x >> a.lanes_shift;
-    const int chunk = threadIdx.x - (q << a.lanes_shift);
+    const int chunk = threadIdx.x & ((1 << a.lanes_shift) - 1);
     const int py = (int)divm((unsigned)q, a.tw_magic);
     const int px = q - py * a.tw;
     const int oy = t.oy0 + py, ox = t.ox0 + px;
     if (py >= a.th || oy >= geo.Ho || ox >= geo.Wo)
         return;   // no barrier follows
-    const int es = (int)sizeof(T);
-    constexpr int epd = 4 / (int)sizeof(T);   // elements per staged dword
-    const T *om = reinterpret_cast<const T *>(om_s) + q * a.om_dw * epd + ((t.g * 3 * a.K) & (epd - 1));
-    const int ry0 = t.oy0 * geo.sh - geo.ph - a.R, rx0 = t.ox0 * geo.sw - geo.pw - a.R;
-    const int chan_off = (t.g * a.Cg + chunk * DP) * es;
-    const unsigned cs = (unsigned)(geo.C * es), rs = (unsigned)geo.W * cs;
-    const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
-    const int v0 = chunk * NV;
+
+    constexpr int epd = 4 / es;   // entries per staged dword
+    const T *om = reinterpret_cast<const T *>(om_s + q * a.om_dw * 4) + ((t.g * 3 * a.K) & (epd - 1));
+    const NearFrame nf = near_frame(a, t, oy, ox);
+    const char *vb = val_s + chunk * NV * 16;
 
     float acc[DP];
 #pragma unroll
     for (int c = 0; c < DP; ++c)
         acc[c] = 0.0f;
 
+    unsigned farbits = 0;
     for (int k = 0; k < a.K; ++k) {
+        int gi, gj;
+        grid_point(geo, k, gi, gj);
         const float dx = Store<T>::scalar(om[2 * k]);
         const float dy = Store<T>::scalar(om[2 * k + 1]);
         const float m = Store<T>::scalar(om[2 * a.K + k]);
-        const Loc l = locate(geo, oy, ox, k, dx, dy);
-        if (!live(geo, l))
-            continue;
-        const Footprint f = footprint(geo, l);
+        const float bh = nf.bh0 + (float)(gj * geo.dh), bw = nf.bw0 + (float)(gi * geo.dw);
+        const NearSample s = near_sample(nf, geo.scale, bh, bw, dx, dy);
+        farbits |= (!s.nr && live_loc(geo, s.lh, s.lw)) ? (1u << k) : 0u;
+        // a sample that is not near gets zero weights (its reads hit slot 0)
+        const float ah = s.nr ? s.lh - s.fh : 0.0f, aw = s.nr ? s.lw - s.fw : 0.0f;
+        const float mm = s.nr ? m : 0.0f;
+        const float mh = __builtin_fmaf(-mm, ah, mm), ml = mm * ah;
+        const float w00 = __builtin_fmaf(-mh, aw, mh), w01 = mh * aw;
+        const float w10 = __builtin_fmaf(-ml, aw, ml), w11 = ml * aw;
+        const u32x4 *p00 = reinterpret_cast<const u32x4 *>(vb + s.addr);
+        const u32x4 *p01 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.colb);
+        const u32x4 *p10 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.rowb);
+        const u32x4 *p11 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.rowb + nf.colb);
         u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
-        float w00, w01, w10, w11;
-        if (near_sample(f, l, a.R)) {
-            // corners inside the LDS region; outside the image they hold 0
-            const float hh = 1.0f - f.lh, hw = 1.0f - f.lw;
-            const float mh = m * hh, ml = m * f.lh;
-            w00 = mh * hw;
-            w01 = mh * f.lw;
-            w10 = ml * hw;
-            w11 = ml * f.lw;
-            const int p00 = (f.h0 - ry0) * a.rw + (f.w0 - rx0);
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                v00[v] = val_s[vslot(a, p00, v0 + v)];
-                v01[v] = val_s[vslot(a, p00 + 1, v0 + v)];
-                v10[v] = val_s[vslot(a, p00 + a.rw, v0 + v)];
-                v11[v] = val_s[vslot(a, p00 + a.rw + 1, v0 + v)];
-            }
-        } else {
-            const unsigned off = corner_offset(geo, t.n, f, es, chan_off);
+        for (int v = 0; v < NV; ++v) {
+            v00[v] = p00[v];
+            v01[v] = p01[v];
+            v10[v] = p10[v];
+            v11[v] = p11[v];
+        }
+#pragma unroll
+        for (int c = 0; c < DP; ++c) {
+            float x = acc[c];
+            x = __builtin_fmaf(w00, Store<T>::get(v00, c), x);
+            x = __builtin_fmaf(w01, Store<T>::get(v01, c), x);
+            x = __builtin_fmaf(w10, Store<T>::get(v10, c), x);
+            x = __builtin_fmaf(w11, Store<T>::get(v11, c), x);
+            acc[c] = x;
+        }
+    }
+
+    if (farbits) {
+        // far samples: corners from global memory; corners outside the image
+        // get weight 0 (the buffer range check zero-fills reads past the end)
+        const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
+        const int chan_off = (t.g * a.Cg + chunk * DP) * es;
+        const unsigned cs = (unsigned)(geo.C * es), rs = (unsigned)geo.W * cs;
+        do {
+            const int k = __builtin_ctz(farbits);
+            farbits &= farbits - 1;
+            const float dx = Store<T>::scalar(om[2 * k]);
+            const float dy = Store<T>::scalar(om[2 * k + 1]);
+            const float m = Store<T>::scalar(om[2 * a.K + k]);
+            const Loc l = locate_lane(a, oy, ox, k, dx, dy);
+            const Footprint f = footprint(geo, l);
+            float w00, w01, w10, w11;
             masked_weights(f, m, w00, w01, w10, w11);
+            const unsigned off = corner_offset(geo, t.n, f, es, chan_off);
+            u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
                 v00[v] = load16(vr, off + 16 * v);
@@ -272,16 +379,16 @@ __global__ __launch_bounds__(256) void dcnv4_fwd_tiled(TArgs a)
                 v10[v] = load16(vr, off + rs + 16 * v);
                 v11[v] = load16(vr, off + rs + cs + 16 * v);
             }
-        }
 #pragma unroll
-        for (int c = 0; c < DP; ++c) {
-            float s = acc[c];
-            s = __builtin_fmaf(w00, Store<T>::get(v00, c), s);
-            s = __builtin_fmaf(w01, Store<T>::get(v01, c), s);
-            s = __builtin_fmaf(w10, Store<T>::get(v10, c), s);
-            s = __builtin_fmaf(w11, Store<T>::get(v11, c), s);
-            acc[c] = s;
-        }
+            for (int c = 0; c < DP; ++c) {
+                float x = acc[c];
+                x = __builtin_fmaf(w00, Store<T>::get(v00, c), x);
+                x = __builtin_fmaf(w01, Store<T>::get(v01, c), x);
+                x = __builtin_fmaf(w10, Store<T>::get(v10, c), x);
+                x = __builtin_fmaf(w11, Store<T>::get(v11, c), x);
+                acc[c] = x;
+            }
+        } while (farbits);
     }
 
     u32x4 res[NV];
@@ -296,140 +403,193 @@ __global__ __launch_bounds__(256) void dcnv4_fwd_tiled(TArgs a)
 
 // ---- backward: grad_offset_mask (and far samples' grad_value) --------------
 
+// Gradients of one sample from the dot products t_q = sum_c grad_out_c *
+// v_q,c of its four corners: d/dm is the bilinear sample; d/d loc is the
+// derivative inside the cell chosen by floor (right derivative at integers).
+__device__ __forceinline__ void sample_grads(float ah, float aw, float t00, float t01, float t10, float t11,
+                                             float &gm, float &gw, float &gh)
+{
+    const float hh = 1.0f - ah, hw = 1.0f - aw;
+    gm = hh * __builtin_fmaf(hw, t00, aw * t01) + ah * __builtin_fmaf(hw, t10, aw * t11);
+    gw = hh * (t01 - t00) + ah * (t11 - t10);
+    gh = hw * (t10 - t00) + aw * (t11 - t01);
+}
+
 template <int DP>
-__global__ __launch_bounds__(256) void dcnv4_bwd_offsets_tiled(TArgs a)
+__global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs a)
 {
     extern __shared__ u32x4 smem[];
     constexpr int NV = DP / 4;
     const Geom &geo = a.geo;
     const Tile t = out_tile(a);
-    float *om_s = reinterpret_cast<float *>(smem);
-    u32x4 *val_s = smem + a.om_lds_vecs;
-    stage_offsets(a, t, reinterpret_cast<unsigned *>(om_s), 4);
-    stage_region(a, t, val_s, 4);
+    char *om_b = reinterpret_cast<char *>(smem);
+    char *val_s = om_b + a.om_lds_bytes;
+    stage_tile(a, t, om_b, val_s, 4);
     staging_done();
+    float *om_s = reinterpret_cast<float *>(om_b);
 
     const int K3 = 3 * a.K;
     const int q = threadIdx.x >> a.lanes_shift;
-    const int chunk = threadIdx.x - (q << a.lanes_shift);
+    const int chunk = threadIdx.x & ((1 << a.lanes_shift) - 1);
     const int lanes = 1 << a.lanes_shift;
     const int py = (int)divm((unsigned)q, a.tw_magic);
     const int px = q - py * a.tw;
     const int oy = t.oy0 + py, ox = t.ox0 + px;
-    // every thread runs the k loop (far samples are written by whole waves);
-    // threads past the tile or the image only take part in that
+    // every thread stays to the end (far samples are written by whole
+    // waves); threads past the tile or the image only take part in that
     const bool valid = py < a.th && oy < geo.Ho && ox < geo.Wo;
     float *om = om_s + (valid ? q : 0) * a.om_dw;   // overwritten in place with the gradients
-    const int ry0 = t.oy0 * geo.sh - geo.ph - a.R, rx0 = t.ox0 * geo.sw - geo.pw - a.R;
+    const NearFrame nf = near_frame(a, t, oy, ox);
     const int chan_off = (t.g * a.Cg + chunk * DP) * 4;
     const unsigned cs = (unsigned)(geo.C * 4), rs = (unsigned)geo.W * cs;
-    const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
-    const __amdgpu_buffer_rsrc_t gr = rsrc(a.gvalue, a.value_bytes);
-    const __amdgpu_buffer_rsrc_t gor = rsrc(a.gout, a.gout_bytes);
-    const int v0 = chunk * NV;
+    const char *vb = val_s + chunk * NV * 16;
     const unsigned pix_off = ((unsigned)((t.n * geo.Ho + oy) * geo.Wo + ox)) * cs + (unsigned)chan_off;
-    // lane's part in a far sample's grad_value update: corner lane / DP,
-    // channel lane % DP of the owner's DP channels
-    const int lane = threadIdx.x & 63;
-    const int my_corner = lane / DP, my_c = lane % DP;
-    const unsigned my_corner_off = (unsigned)(my_corner & 1) * cs + (unsigned)(my_corner >> 1) * rs + 4u * (unsigned)my_c;
 
     float go[DP];
+    {
+        const __amdgpu_buffer_rsrc_t gor = rsrc(a.gout, a.gout_bytes);
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-        const f32x4 r = __builtin_bit_cast(f32x4, load16(gor, valid ? pix_off + 16 * v : kOutOfRange));
-        for (int e = 0; e < 4; ++e)
-            go[4 * v + e] = r[e];
+        for (int v = 0; v < NV; ++v) {
+            const f32x4 r = __builtin_bit_cast(f32x4, load16(gor, valid ? pix_off + 16 * v : kOutOfRange));
+            for (int e = 0; e < 4; ++e)
+                go[4 * v + e] = r[e];
+        }
     }
 
+    unsigned farbits = 0;
     for (int k = 0; k < a.K; ++k) {
+        int gi, gj;
+        grid_point(geo, k, gi, gj);
         const float dx = om[2 * k], dy = om[2 * k + 1], m = om[2 * a.K + k];
-        float gm = 0.0f, gw = 0.0f, gh = 0.0f;
-        const Loc l = locate(geo, oy, ox, k, dx, dy);
-        bool far = false;
-        unsigned far_off = 0;
-        float w00 = 0.0f, w01 = 0.0f, w10 = 0.0f, w11 = 0.0f;
-        if (valid && live(geo, l)) {
-            const Footprint f = footprint(geo, l);
-            u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
-            const bool nr = near_sample(f, l, a.R);
-            if (nr) {
-                const int p00 = (f.h0 - ry0) * a.rw + (f.w0 - rx0);
+        const float bh = nf.bh0 + (float)(gj * geo.dh), bw = nf.bw0 + (float)(gi * geo.dw);
+        const NearSample s = near_sample(nf, geo.scale, bh, bw, dx, dy);
+        const bool nr = s.nr && valid;
+        const int addr = nr ? s.addr : 0;
+        const bool far = valid && !s.nr && live_loc(geo, s.lh, s.lw);
+        farbits |= far ? (1u << k) : 0u;
+        const u32x4 *p00 = reinterpret_cast<const u32x4 *>(vb + addr);
+        const u32x4 *p01 = reinterpret_cast<const u32x4 *>(vb + addr + nf.colb);
+        const u32x4 *p10 = reinterpret_cast<const u32x4 *>(vb + addr + nf.rowb);
+        const u32x4 *p11 = reinterpret_cast<const u32x4 *>(vb + addr + nf.rowb + nf.colb);
+        u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
 #pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    v00[v] = val_s[vslot(a, p00, v0 + v)];
-                    v01[v] = val_s[vslot(a, p00 + 1, v0 + v)];
-                    v10[v] = val_s[vslot(a, p00 + a.rw, v0 + v)];
-                    v11[v] = val_s[vslot(a, p00 + a.rw + 1, v0 + v)];
-                }
-            } else {
-                far = true;
-                far_off = corner_offset(geo, t.n, f, 4, chan_off);
-#pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    v00[v] = load16(vr, far_off + 16 * v);
-                    v01[v] = load16(vr, far_off + cs + 16 * v);
-                    v10[v] = load16(vr, far_off + rs + 16 * v);
-                    v11[v] = load16(vr, far_off + rs + cs + 16 * v);
-                }
-            }
-            // t_q = sum_c grad_out_c * v_q,c
-            float t00 = 0.0f, t01 = 0.0f, t10 = 0.0f, t11 = 0.0f;
-#pragma unroll
-            for (int c = 0; c < DP; ++c) {
-                t00 = __builtin_fmaf(go[c], Store<float>::get(v00, c), t00);
-                t01 = __builtin_fmaf(go[c], Store<float>::get(v01, c), t01);
-                t10 = __builtin_fmaf(go[c], Store<float>::get(v10, c), t10);
-                t11 = __builtin_fmaf(go[c], Store<float>::get(v11, c), t11);
-            }
-            if (far) {
-                // zero-extended image: dots of corners outside are 0
-                t00 = (f.r0 && f.c0) ? t00 : 0.0f;
-                t01 = (f.r0 && f.c1) ? t01 : 0.0f;
-                t10 = (f.r1 && f.c0) ? t10 : 0.0f;
-                t11 = (f.r1 && f.c1) ? t11 : 0.0f;
-                masked_weights(f, m, w00, w01, w10, w11);
-            }
-            const float lh = f.lh, lw = f.lw, hh = 1.0f - lh, hw = 1.0f - lw;
-            // d/dm: the sample; d/d loc of the bilinear sample inside the
-            // cell chosen by floor (right derivative at integers)
-            gm = hh * (hw * t00 + lw * t01) + lh * (hw * t10 + lw * t11);
-            gw = hh * (t01 - t00) + lh * (t11 - t10);
-            gh = hw * (t10 - t00) + lw * (t11 - t01);
+        for (int v = 0; v < NV; ++v) {
+            v00[v] = p00[v];
+            v01[v] = p01[v];
+            v10[v] = p10[v];
+            v11[v] = p11[v];
         }
-        // grad_value of far samples: one device atomic per corner and
-        // channel, issued by the whole wave for one (sample, lane) at a time
-        // so that each instruction covers four contiguous corner rows
-        unsigned long long fm = __ballot(far);
-        while (fm) {
-            const int src = __builtin_ctzll(fm);
-            fm &= fm - 1;
-            const unsigned off = (unsigned)__builtin_amdgcn_readlane((int)far_off, src);
-            const float s00 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w00), src));
-            const float s01 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w01), src));
-            const float s10 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w10), src));
-            const float s11 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w11), src));
-            float g = 0.0f;
+        float t00 = 0.0f, t01 = 0.0f, t10 = 0.0f, t11 = 0.0f;
 #pragma unroll
-            for (int c = 0; c < DP; ++c) {
-                const float gc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, go[c]), src));
-                g = my_c == c ? gc : g;
-            }
-            const float w = my_corner == 0 ? s00 : my_corner == 1 ? s01 : my_corner == 2 ? s10 : s11;
-            if (my_corner < 4 && w != 0.0f)
-                dcnv4_buffer_atomic_fadd(w * g, gr, off + my_corner_off, 0, 0);
+        for (int c = 0; c < DP; ++c) {
+            t00 = __builtin_fmaf(go[c], Store<float>::get(v00, c), t00);
+            t01 = __builtin_fmaf(go[c], Store<float>::get(v01, c), t01);
+            t10 = __builtin_fmaf(go[c], Store<float>::get(v10, c), t10);
+            t11 = __builtin_fmaf(go[c], Store<float>::get(v11, c), t11);
         }
+        float gm, gw, gh;
+        sample_grads(s.lh - s.fh, s.lw - s.fw, t00, t01, t10, t11, gm, gw, gh);
+        gm = nr ? gm : 0.0f;
+        gw = nr ? gw : 0.0f;
+        gh = nr ? gh : 0.0f;
         for (int d = 1; d < lanes; d <<= 1) {
             gm += __shfl_xor(gm, d);
             gw += __shfl_xor(gw, d);
             gh += __shfl_xor(gh, d);
         }
-        if (valid && chunk == 0) {
-            // the lanes of this pixel have read entry k already
+        if (valid && chunk == 0 && !far) {
+            // the lanes of this pixel have read entry k already; far entries
+            // are still needed by the loop below
             const float sm = geo.scale * m;
             om[2 * k] = sm * gw;
             om[2 * k + 1] = sm * gh;
             om[2 * a.K + k] = gm;
+        }
+    }
+
+    // far samples, one per lane and iteration; the whole wave stays in the
+    // loop for the grad_value atomics
+    {
+        const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
+        const __amdgpu_buffer_rsrc_t gr = rsrc(a.gvalue, a.value_bytes);
+        // this lane's part of a far sample's grad_value update: corner
+        // lane / DP, channel lane % DP of the owner's DP channels
+        const int lane = threadIdx.x & 63;
+        const int my_corner = lane / DP, my_c = lane % DP;
+        const unsigned my_corner_off =
+            (unsigned)(my_corner & 1) * cs + (unsigned)(my_corner >> 1) * rs + 4u * (unsigned)my_c;
+        while (__ballot(farbits != 0)) {
+            const bool has = farbits != 0;
+            int k = 0;
+            float gm = 0.0f, gw = 0.0f, gh = 0.0f, m = 0.0f;
+            unsigned off = 0;
+            float w00 = 0.0f, w01 = 0.0f, w10 = 0.0f, w11 = 0.0f;
+            if (has) {
+                k = __builtin_ctz(farbits);
+                farbits &= farbits - 1;
+                const float dx = om[2 * k], dy = om[2 * k + 1];
+                m = om[2 * a.K + k];
+                const Loc l = locate_lane(a, oy, ox, k, dx, dy);
+                const Footprint f = footprint(geo, l);
+                off = corner_offset(geo, t.n, f, 4, chan_off);
+                u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    v00[v] = load16(vr, off + 16 * v);
+                    v01[v] = load16(vr, off + cs + 16 * v);
+                    v10[v] = load16(vr, off + rs + 16 * v);
+                    v11[v] = load16(vr, off + rs + cs + 16 * v);
+                }
+                float t00 = 0.0f, t01 = 0.0f, t10 = 0.0f, t11 = 0.0f;
+#pragma unroll
+                for (int c = 0; c < DP; ++c) {
+                    t00 = __builtin_fmaf(go[c], Store<float>::get(v00, c), t00);
+                    t01 = __builtin_fmaf(go[c], Store<float>::get(v01, c), t01);
+                    t10 = __builtin_fmaf(go[c], Store<float>::get(v10, c), t10);
+                    t11 = __builtin_fmaf(go[c], Store<float>::get(v11, c), t11);
+                }
+                // zero-extended image: dots of corners outside are 0
+                t00 = (f.r0 && f.c0) ? t00 : 0.0f;
+                t01 = (f.r0 && f.c1) ? t01 : 0.0f;
+                t10 = (f.r1 && f.c0) ? t10 : 0.0f;
+                t11 = (f.r1 && f.c1) ? t11 : 0.0f;
+                sample_grads(f.lh, f.lw, t00, t01, t10, t11, gm, gw, gh);
+                masked_weights(f, m, w00, w01, w10, w11);
+            }
+            for (int d = 1; d < lanes; d <<= 1) {
+                gm += __shfl_xor(gm, d);
+                gw += __shfl_xor(gw, d);
+                gh += __shfl_xor(gh, d);
+            }
+            if (has && chunk == 0) {
+                const float sm = geo.scale * m;
+                om[2 * k] = sm * gw;
+                om[2 * k + 1] = sm * gh;
+                om[2 * a.K + k] = gm;
+            }
+            // grad_value: one device atomic per corner and channel, issued by
+            // the whole wave for one (sample, lane) at a time so that each
+            // instruction covers four contiguous corner rows
+            unsigned long long fm = __ballot(has);
+            while (fm) {
+                const int src = __builtin_ctzll(fm);
+                fm &= fm - 1;
+                const unsigned so = (unsigned)__builtin_amdgcn_readlane((int)off, src);
+                const float s00 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w00), src));
+                const float s01 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w01), src));
+                const float s10 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w10), src));
+                const float s11 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w11), src));
+                float g = 0.0f;
+#pragma unroll
+                for (int c = 0; c < DP; ++c) {
+                    const float gc =
+                        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, go[c]), src));
+                    g = my_c == c ? gc : g;
+                }
+                const float w = my_corner == 0 ? s00 : my_corner == 1 ? s01 : my_corner == 2 ? s10 : s11;
+                if (my_corner < 4 && w != 0.0f)
+                    dcnv4_buffer_atomic_fadd(w * g, gr, so + my_corner_off, 0, 0);
+            }
         }
     }
     __syncthreads();
@@ -437,7 +597,7 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_offsets_tiled(TArgs a)
     // write the group's gradient entries of the tile; group 0 also zeroes
     // the padding channels
     {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = (blockDim.x + 63) >> 6;
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
         const int row_elems = a.tw * K3;
         const __amdgpu_buffer_rsrc_t r = rsrc(a.gom, a.om_bytes);
         const int pad0 = a.G * K3, npad = a.P - pad0;
@@ -451,8 +611,8 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_offsets_tiled(TArgs a)
                 const int ox2 = t.ox0 + px2;
                 if (ox2 < geo.Wo) {
                     const unsigned idx = (unsigned)(((t.n * geo.Ho + oy2) * geo.Wo + ox2) * a.P + t.g * K3 + j);
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, om_s[(py2 * a.tw + px2) * a.om_dw + j]),
-                                                          r, idx * 4u, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        __builtin_bit_cast(unsigned, om_s[(py2 * a.tw + px2) * a.om_dw + j]), r, idx * 4u, 0, 0);
                 }
             }
             if (t.g == 0 && npad > 0) {
@@ -472,9 +632,6 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_offsets_tiled(TArgs a)
 
 // ---- backward: grad_value of near samples, per cell tile -------------------
 
-constexpr int kSamplesPerLane = 4;   // a batch holds at most 256 * 4 samples
-constexpr int kMaxRecords = 4 * 256 * kSamplesPerLane;
-
 __device__ __forceinline__ int floor_div(int a, int b)
 {
     const int q = a / b;
@@ -486,18 +643,42 @@ __device__ __forceinline__ int ceil_div(int a, int b)
     return -floor_div(-a, b);
 }
 
-template <int CG>
+// Entries e = 0..NOUT-1 of a slice that starts `mis` (0..3, the same for the
+// whole block) dwords into the 16-byte vectors v.  The shift is done with
+// bit masks, not as an array index (which would go through scratch memory).
+template <int NVEC, int NOUT>
+__device__ __forceinline__ void shifted_entries(const u32x4 (&v)[NVEC], int mis, float (&out)[NOUT])
+{
+    static_assert(NOUT + 3 <= 4 * NVEC, "vectors too short");
+    unsigned w[4 * NVEC];
+#pragma unroll
+    for (int i = 0; i < NVEC; ++i)
+        for (int e = 0; e < 4; ++e)
+            w[4 * i + e] = v[i][e];
+    const unsigned m1 = 0u - (unsigned)(mis & 1), m2 = 0u - (unsigned)((mis >> 1) & 1);
+    unsigned t[4 * NVEC - 1];
+#pragma unroll
+    for (int i = 0; i < 4 * NVEC - 1; ++i)
+        t[i] = w[i] ^ ((w[i] ^ w[i + 1]) & m1);
+#pragma unroll
+    for (int e = 0; e < NOUT; ++e)
+        out[e] = __builtin_bit_cast(float, t[e] ^ ((t[e] ^ t[e + 2]) & m2));
+}
+
+template <int CG, int KMAX>
 __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
 {
     extern __shared__ u32x4 smem[];
-    constexpr int NVG = CG / 4;   // 16-byte vectors of one source pixel's grad_out (fp32)
+    constexpr int NVG = CG / 4;                  // 16-byte vectors of one source pixel's grad_out
+    constexpr int NVO = (2 * KMAX + 3 + 3) / 4;  // vectors holding the 2K offsets after a shift
+    constexpr int NVM = (KMAX + 3 + 3) / 4;      // vectors holding the K masks after a shift
     const Geom &geo = a.geo;
-    unsigned *cnt = reinterpret_cast<unsigned *>(smem);   // [256] records per cell
-    unsigned *fill = cnt + 256;                           // [256] scatter cursors
-    unsigned *base = fill + 256;                          // [256] exclusive prefix of cnt
-    unsigned *wsum = base + 256;                          // [4]  (16 B reserved)
-    unsigned *rec = wsum + 4;                             // [2 * kMaxRecords] (weight bits, source)
-    u32x4 *g_s = reinterpret_cast<u32x4 *>(rec + 2 * kMaxRecords);   // [src_batch * NVG]
+    char *lds = reinterpret_cast<char *>(smem);
+    unsigned *cnt = reinterpret_cast<unsigned *>(lds);   // [kMaxBins] samples per corner cell
+    unsigned *base = cnt + kMaxBins;                     // [kMaxBins] exclusive prefix of cnt
+    unsigned *wsum = base + kMaxBins;                    // [8]
+    f32x4 *rec = reinterpret_cast<f32x4 *>(lds + a.rec_offset);   // (frac h, frac w, m, source)
+    char *g_s = lds + a.gs_offset;                       // grad_out of the batch's sources
 
     int b = xcd_tile(blockIdx.x, gridDim.x);
     const int g = b % a.G;
@@ -507,99 +688,116 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
     const int cty = b % a.ctiles_y;
     const int n = b / a.ctiles_y;
     const int cy0 = cty * a.ch, cx0 = ctx * a.cw;
-    const int kw = geo.kw;
 
     // output pixels whose near samples can touch rows [cy0, cy0+ch): a near
     // sample's top row h0 lies in [bh - R, bh + R] with bh = oy*sh - ph + j*dh,
     // and touching needs h0 in [cy0 - 1, cy0 + ch - 1]
     const int sy0 = max(0, ceil_div(cy0 - 1 - a.R + geo.ph - (geo.kh - 1) * geo.dh, geo.sh));
     const int sy1 = min(geo.Ho, floor_div(cy0 + a.ch - 1 + a.R + geo.ph, geo.sh) + 1);
-    const int sx0 = max(0, ceil_div(cx0 - 1 - a.R + geo.pw - (kw - 1) * geo.dw, geo.sw));
+    const int sx0 = max(0, ceil_div(cx0 - 1 - a.R + geo.pw - (geo.kw - 1) * geo.dw, geo.sw));
     const int sx1 = min(geo.Wo, floor_div(cx0 + a.cw - 1 + a.R + geo.pw, geo.sw) + 1);
-    const int SW = max(0, sx1 - sx0);
-    const int nsrc = max(0, sy1 - sy0) * SW;
+    const int SW = sx1 - sx0;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int my_cy = cy0 + tid / a.cw, my_cx = cx0 + tid % a.cw;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int AW = a.cw + 1, NB = (a.ch + 1) * AW;
+    // this thread's source within a batch of BR whole source rows
+    const int BR = SW > 0 ? max(1, a.src_cap / SW) : 1;
+    const int srow = SW > 0 ? tid / SW : 0, scol = tid - srow * SW;
+    const int sy_end = SW > 0 ? sy1 : sy0;   // no source column: no batch
+    // this thread's cell and the bins of the corner cells that reach it: the
+    // cell itself (corner 00), left (01), up (10), up-left (11)
+    const int ly = tid / a.cw, lx = tid - ly * a.cw;
     const bool my_cell = tid < a.ch * a.cw;
-    const int K3 = 3 * a.K;
+    const int a0 = (ly + 1) * AW + lx + 1, a1 = a0 - AW;
+
+    const unsigned cs = (unsigned)(geo.C * 4);
     const __amdgpu_buffer_rsrc_t omr = rsrc(a.om, a.om_bytes);
     const __amdgpu_buffer_rsrc_t gor = rsrc(a.gout, a.gout_bytes);
-    const unsigned cs = (unsigned)(geo.C * 4);
+    // grad_out rows: slot j of a row is vector j % gps of source column j / gps
+    unsigned glo[kMaxRowChunks];
+    const int grow_slots = SW * a.gps;
+#pragma unroll
+    for (int c = 0; c < kMaxRowChunks; ++c) {
+        glo[c] = kOutOfRange;
+        if (c * 64 < grow_slots) {
+            const int j = c * 64 + lane;
+            const int s = (int)divm((unsigned)j, a.gps_magic);
+            const int v = j - s * a.gps;
+            if (s < SW && v < NVG)
+                glo[c] = (unsigned)(sx0 + s) * cs + (unsigned)(g * CG * 4 + 16 * v);
+        }
+    }
+    // a source's offsets and masks: 16-byte aligned vectors from the one that
+    // holds the first entry (pixel rows are 32-byte multiples)
+    const int eo = g * 3 * a.K, em = eo + 2 * a.K;
+    const int mis_o = eo & 3, mis_m = em & 3;
+    const unsigned vo = (unsigned)(eo - mis_o) * 4u, vm = (unsigned)(em - mis_m) * 4u;
+    const float Rf = (float)a.R, chf = (float)a.ch, cwf = (float)a.cw;
+    const float ylo = (float)(cy0 - 1), xlo = (float)(cx0 - 1);
 
     float acc[CG];
 #pragma unroll
     for (int c = 0; c < CG; ++c)
         acc[c] = 0.0f;
 
-    for (int b0 = 0; b0 < nsrc; b0 += a.src_batch) {
-        const int nb = min(a.src_batch, nsrc - b0);
-        // (a) grad_out rows of the batch's source pixels
-        for (int e = tid; e < nb * NVG; e += 256) {
-            const int s = e / NVG, v = e - s * NVG;
-            const int src = b0 + s;
-            const int oy = sy0 + src / SW, ox = sx0 + src % SW;
-            g_s[s * NVG + (v ^ ((s >> a.swz_shift) & a.swz_mask))] =
-                load16(gor, (unsigned)((n * geo.Ho + oy) * geo.Wo + ox) * cs + (unsigned)(g * CG * 4 + 16 * v));
-        }
-        cnt[tid] = 0u;
-        fill[tid] = 0u;
-        __syncthreads();
+    for (int r0 = sy0; r0 < sy_end; r0 += BR) {
+        const int nrows = min(BR, sy1 - r0);
+        for (int i = tid; i < NB; i += 256)
+            cnt[i] = 0u;
+        const unsigned row_bytes = (unsigned)geo.Wo * cs;
+        stage_rows<16>(gor, g_s, nrows, grow_slots, glo,
+                       [&](int rr) { return (unsigned)(n * geo.Ho + r0 + rr) * row_bytes; });
+        const bool src_ok = srow < nrows;
+        const int oy = r0 + srow, ox = sx0 + scol;
+        const unsigned pix = (unsigned)((n * geo.Ho + oy) * geo.Wo + ox) * (unsigned)(a.P * 4);
+        u32x4 vov[NVO], vmv[NVM];
+#pragma unroll
+        for (int j = 0; j < NVO; ++j)
+            vov[j] = load16(omr, src_ok ? pix + vo + 16u * j : kOutOfRange);
+#pragma unroll
+        for (int j = 0; j < NVM; ++j)
+            vmv[j] = load16(omr, src_ok ? pix + vm + 16u * j : kOutOfRange);
+        staging_done();   // also orders the counter reset before the counting
 
-        // (b) evaluate this lane's samples; count corner records per cell
-        const int ns = nb * a.K;
-        unsigned cells[kSamplesPerLane][2];   // four 16-bit cell indices, 0xffff = none
-        float wts[kSamplesPerLane][4];
-        int srcs[kSamplesPerLane];
+        float offs[2 * KMAX], msk[KMAX];
+        shifted_entries(vov, mis_o, offs);
+        shifted_entries(vmv, mis_m, msk);
+        const float bh0 = (float)(oy * geo.sh - geo.ph), bw0 = (float)(ox * geo.sw - geo.pw);
+        unsigned slot[KMAX];
+        float fa[KMAX], fb[KMAX];
 #pragma unroll
-        for (int i = 0; i < kSamplesPerLane; ++i) {
-            cells[i][0] = cells[i][1] = 0xffffffffu;
-            const int e = tid + 256 * i;
-            srcs[i] = 0;
-            if (e < ns) {
-                const int s = (int)divm((unsigned)e, a.k_magic);
-                const int k = e - s * a.K;
-                const int src = b0 + s;
-                const int oy = sy0 + src / SW, ox = sx0 + src % SW;
-                const unsigned ob = (unsigned)(((n * geo.Ho + oy) * geo.Wo + ox) * a.P + g * K3);
-                const float dx = load_elem<float>(omr, (ob + 2 * k) * 4u);
-                const float dy = load_elem<float>(omr, (ob + 2 * k + 1) * 4u);
-                const float m = load_elem<float>(omr, (ob + 2 * a.K + k) * 4u);
-                const Loc l = locate(geo, oy, ox, k, dx, dy);
-                if (live(geo, l)) {
-                    const Footprint f = footprint(geo, l);
-                    if (near_sample(f, l, a.R)) {
-                        const float hh = 1.0f - f.lh, hw = 1.0f - f.lw;
-                        const float mh = m * hh, ml = m * f.lh;
-                        wts[i][0] = mh * hw;
-                        wts[i][1] = mh * f.lw;
-                        wts[i][2] = ml * hw;
-                        wts[i][3] = ml * f.lw;
-                        srcs[i] = s;
-#pragma unroll
-                        for (int qd = 0; qd < 4; ++qd) {
-                            const int y = f.h0 + (qd >> 1), x = f.w0 + (qd & 1);
-                            const int ly = y - cy0, lx = x - cx0;
-                            const bool in = (unsigned)ly < (unsigned)a.ch && (unsigned)lx < (unsigned)a.cw &&
-                                            (unsigned)y < (unsigned)geo.H && (unsigned)x < (unsigned)geo.W;
-                            if (in) {
-                                const unsigned cidx = (unsigned)(ly * a.cw + lx);
-                                const int word = qd >> 1, sh = (qd & 1) * 16;
-                                cells[i][word] = (cells[i][word] & ~(0xffffu << sh)) | (cidx << sh);
-                                atomicAdd(&cnt[cidx], 1u);
-                            }
-                        }
-                    }
+        for (int k = 0; k < KMAX; ++k) {
+            slot[k] = 0xffffffffu;
+            fa[k] = fb[k] = 0.0f;
+            if (k < a.K) {
+                int gi, gj;
+                grid_point(geo, k, gi, gj);
+                const float bh = bh0 + (float)(gj * geo.dh), bw = bw0 + (float)(gi * geo.dw);
+                const float lh = __builtin_fmaf(geo.scale, offs[2 * k + 1], bh);
+                const float lw = __builtin_fmaf(geo.scale, offs[2 * k], bw);
+                const float fh = __builtin_floorf(lh), fw = __builtin_floorf(lw);
+                const bool nr = __builtin_fabsf(fh - bh) <= Rf && __builtin_fabsf(fw - bw) <= Rf;
+                // top-left corner cell relative to (cy0 - 1, cx0 - 1)
+                const float ay = fh - ylo, ax = fw - xlo;
+                if (src_ok && nr && ay >= 0.0f && ay <= chf && ax >= 0.0f && ax <= cwf) {
+                    const unsigned bin = (unsigned)((int)ay * AW + (int)ax);
+                    const unsigned rank = atomicAdd(&cnt[bin], 1u);
+                    slot[k] = (bin << 16) | rank;
                 }
+                fa[k] = lh - fh;
+                fb[k] = lw - fw;
             }
         }
         __syncthreads();
 
-        // (c) exclusive prefix sum of the 256 counters
+        // exclusive prefix sum of the bins, three per thread
         {
-            const unsigned c = cnt[tid];
-            unsigned x = c;
+            const int i0 = 3 * tid;
+            const unsigned c0 = i0 < NB ? cnt[i0] : 0u;
+            const unsigned c1 = i0 + 1 < NB ? cnt[i0 + 1] : 0u;
+            const unsigned c2 = i0 + 2 < NB ? cnt[i0 + 2] : 0u;
+            const unsigned mine = c0 + c1 + c2;
+            unsigned x = mine;
             for (int d = 1; d < 64; d <<= 1) {
                 const unsigned y = __shfl_up(x, d);
                 if (lane >= d)
@@ -611,50 +809,66 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
             unsigned off = 0;
             for (int w = 0; w < wave; ++w)
                 off += wsum[w];
-            base[tid] = off + x - c;
+            const unsigned e0 = off + x - mine;
+            if (i0 < NB)
+                base[i0] = e0;
+            if (i0 + 1 < NB)
+                base[i0 + 1] = e0 + c0;
+            if (i0 + 2 < NB)
+                base[i0 + 2] = e0 + c0 + c1;
         }
         __syncthreads();
 
-        // (d) scatter (weight, source) records into per-cell lists
 #pragma unroll
-        for (int i = 0; i < kSamplesPerLane; ++i) {
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                const unsigned cidx = (cells[i][qd >> 1] >> ((qd & 1) * 16)) & 0xffffu;
-                if (cidx != 0xffffu) {
-                    const unsigned slot = base[cidx] + atomicAdd(&fill[cidx], 1u);
-                    rec[2 * slot] = __builtin_bit_cast(unsigned, wts[i][qd]);
-                    rec[2 * slot + 1] = (unsigned)srcs[i];
-                }
+        for (int k = 0; k < KMAX; ++k) {
+            if (slot[k] != 0xffffffffu) {
+                const unsigned idx = base[slot[k] >> 16] + (slot[k] & 0xffffu);
+                f32x4 r;
+                r[0] = fa[k];
+                r[1] = fb[k];
+                r[2] = msk[k];
+                r[3] = __builtin_bit_cast(float, (unsigned)tid);
+                rec[idx] = r;
             }
         }
         __syncthreads();
 
-        // (e) each cell sums its list
+        // each cell sums the samples whose corners reach it: bins a0-1, a0
+        // (same row) are one run of the sorted list, bins a1-1, a1 another
         if (my_cell) {
-            const unsigned r0 = base[tid], r1 = r0 + cnt[tid];
-            for (unsigned r = r0; r < r1; ++r) {
-                const float w = __builtin_bit_cast(float, rec[2 * r]);
-                const int s = (int)rec[2 * r + 1];
+            const unsigned s1 = base[a0 - 1], b1 = base[a0], n1 = b1 - s1 + cnt[a0];
+            const unsigned s2 = base[a1 - 1], b2 = base[a1], n2 = b2 - s2 + cnt[a1];
+            const unsigned ntot = n1 + n2;
+            for (unsigned r = 0; r < ntot; ++r) {
+                const bool same_row = r < n1;
+                const unsigned idx = same_row ? s1 + r : s2 + (r - n1);
+                const bool from_left = idx < (same_row ? b1 : b2);
+                const f32x4 rv = rec[idx];
+                const unsigned src = __builtin_bit_cast(u32x4, rv)[3];   // whole-vector cast, then index
+                const float wy = same_row ? 1.0f - rv[0] : rv[0];
+                const float wx = from_left ? rv[1] : 1.0f - rv[1];
+                const float w = rv[2] * (wy * wx);
+                const u32x4 *gp = reinterpret_cast<const u32x4 *>(g_s + src * (unsigned)(a.gps * 16));
 #pragma unroll
                 for (int v = 0; v < NVG; ++v) {
-                    const f32x4 gv = __builtin_bit_cast(f32x4, g_s[s * NVG + (v ^ ((s >> a.swz_shift) & a.swz_mask))]);
-                    for (int e2 = 0; e2 < 4; ++e2)
-                        acc[4 * v + e2] = __builtin_fmaf(w, gv[e2], acc[4 * v + e2]);
+                    const f32x4 gv = __builtin_bit_cast(f32x4, gp[v]);
+                    for (int e = 0; e < 4; ++e)
+                        acc[4 * v + e] = __builtin_fmaf(w, gv[e], acc[4 * v + e]);
                 }
             }
         }
         __syncthreads();
     }
 
+    const int my_cy = cy0 + ly, my_cx = cx0 + lx;
     if (my_cell && my_cy < geo.H && my_cx < geo.W) {
         const __amdgpu_buffer_rsrc_t gvr = rsrc(a.gvalue, a.value_bytes);
         const unsigned off = (unsigned)((n * geo.H + my_cy) * geo.W + my_cx) * cs + (unsigned)(g * CG * 4);
 #pragma unroll
         for (int v = 0; v < NVG; ++v) {
             f32x4 o;
-            for (int e2 = 0; e2 < 4; ++e2)
-                o[e2] = acc[4 * v + e2];
+            for (int e = 0; e < 4; ++e)
+                o[e] = acc[4 * v + e];
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), gvr, off + 16 * v, 0, 0);
         }
     }
@@ -682,7 +896,7 @@ unsigned magic_for(int d)
 {
     // ceil(2^32 / d): mulhi(e, magic) == e / d for 0 <= e < 2^32 / d;
     // d == 1 is encoded as 0 (see divm)
-    if (d == 1)
+    if (d <= 1)
         return 0u;
     return (unsigned)((((unsigned long long)1 << 32) + (unsigned)d - 1) / (unsigned)d);
 }
@@ -703,6 +917,8 @@ TArgs make_targs(const Problem &p, const TilePlan &tp)
     a.Cg = p.Cg;
     a.K = p.K;
     a.P = p.P;
+    a.kh_magic = magic_for(p.kh);
+    a.k3_magic = magic_for(3 * p.K);
     a.th = tp.th;
     a.tw = tp.tw;
     a.tiles_y = tp.tiles_y;
@@ -711,22 +927,31 @@ TArgs make_targs(const Problem &p, const TilePlan &tp)
     a.R = tp.R;
     a.rh = tp.rh;
     a.rw = tp.rw;
-    a.nvp_shift = log2i(tp.nvp);
-    a.swz_mask = tp.swz_mask;
-    a.swz_shift = tp.swz_shift;
-    a.om_lds_vecs = tp.om_lds_bytes / 16;
+    a.ps = tp.ps;
+    a.nvp = tp.nvp;
+    a.ps_magic = magic_for(tp.ps);
     a.om_dw = tp.om_dw;
-    a.k3_magic = magic_for(3 * p.K);
+    a.om_dw_magic = magic_for(tp.om_dw);
     a.tw_magic = magic_for(tp.tw);
-    a.omdw_magic = magic_for(tp.om_dw);
-    a.rw_magic = magic_for(tp.rw);
+    a.om_lds_bytes = tp.om_lds_bytes;
     a.ch = tp.ch;
     a.cw = tp.cw;
     a.ctiles_y = tp.ctiles_y;
     a.ctiles_x = tp.ctiles_x;
-    a.src_batch = tp.src_batch;
-    a.k_magic = magic_for(p.K);
+    a.src_cap = tp.src_cap;
+    a.gps = tp.gps;
+    a.gps_magic = magic_for(tp.gps);
+    a.rec_offset = tp.rec_offset;
+    a.gs_offset = tp.gs_offset;
     return a;
+}
+
+// Shapes every tiled launch relies on (the planner only produces these).
+bool out_tiles_ok(const Problem &p, const TilePlan &tp)
+{
+    return tp.threads % 64 == 0 && tp.threads <= kMaxTileThreads && tp.threads >= tp.th * tp.tw * tp.lanes &&
+           tp.rw * tp.ps <= 64 * kMaxRowChunks && tp.tw * tp.om_dw <= 64 * kMaxRowChunks && p.K <= 32 &&
+           tp.ps >= tp.nvp && tp.om_lds_bytes % 16 == 0;
 }
 
 }  // namespace
@@ -734,7 +959,7 @@ TArgs make_targs(const Problem &p, const TilePlan &tp)
 hipError_t launch_forward_tiled(const Problem &p, const TilePlan &tp, const void *value, const void *offset_mask,
                                 void *output, hipStream_t stream)
 {
-    if (tp.threads % 64 != 0 || tp.threads > 256 || tp.threads < tp.th * tp.tw * tp.lanes)
+    if (!out_tiles_ok(p, tp))
         return hipErrorInvalidConfiguration;
     TArgs a = make_targs(p, tp);
     a.value = value;
@@ -786,7 +1011,11 @@ hipError_t launch_backward_tiled(const Problem &p, const TilePlan &tp, const voi
                                  const void *grad_output, void *grad_value, void *grad_offset_mask,
                                  hipStream_t stream)
 {
-    if (tp.threads % 64 != 0 || tp.threads > 256 || tp.threads < tp.th * tp.tw * tp.lanes)
+    if (!out_tiles_ok(p, tp) || p.K > 25 || tp.ch * tp.cw > 256 || (tp.ch + 1) * (tp.cw + 1) > kMaxBins ||
+        tp.src_cap < 1 || tp.src_cap > 256 || tp.gps * 4 < p.Cg || tp.rec_offset < (2 * kMaxBins + 8) * 4 ||
+        tp.rec_offset % 16 != 0 || tp.gs_offset < tp.rec_offset + tp.src_cap * p.K * 16 ||
+        tp.splat_lds_bytes < tp.gs_offset + tp.src_cap * tp.gps * 16 ||
+        (tp.cw + 2 * tp.R + (p.kw - 1) * p.dw + 1) / p.sw + 2 > tp.src_cap)   // source window width
         return hipErrorInvalidConfiguration;
     TArgs a = make_targs(p, tp);
     a.value = value;
@@ -802,18 +1031,19 @@ hipError_t launch_backward_tiled(const Problem &p, const TilePlan &tp, const voi
         const int blocks = p.N * tp.ctiles_y * tp.ctiles_x * p.G;
         const dim3 grid(blocks), block(256);
         void (*kern)(TArgs) = nullptr;
+        const bool small_k = p.K <= 9;
         switch (p.Cg) {
         case 4:
-            kern = dcnv4_bwd_values_tiled<4>;
+            kern = small_k ? dcnv4_bwd_values_tiled<4, 9> : dcnv4_bwd_values_tiled<4, 25>;
             break;
         case 8:
-            kern = dcnv4_bwd_values_tiled<8>;
+            kern = small_k ? dcnv4_bwd_values_tiled<8, 9> : dcnv4_bwd_values_tiled<8, 25>;
             break;
         case 16:
-            kern = dcnv4_bwd_values_tiled<16>;
+            kern = small_k ? dcnv4_bwd_values_tiled<16, 9> : dcnv4_bwd_values_tiled<16, 25>;
             break;
         case 32:
-            kern = dcnv4_bwd_values_tiled<32>;
+            kern = small_k ? dcnv4_bwd_values_tiled<32, 9> : dcnv4_bwd_values_tiled<32, 25>;
             break;
         default:
             return hipErrorInvalidValue;

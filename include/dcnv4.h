@@ -50,7 +50,9 @@
  *     the null stream) and the call returns without waiting; results are
  *     valid once the stream has completed the work.
  *   - Outputs must not overlap inputs or each other.
- *   - Reentrant; the only process state is a cached device-property query.
+ *   - Reentrant.  Process state: a per-thread copy of the last HIP error
+ *     message, and a record of the kernels whose dynamic-LDS limit has
+ *     been raised (hipFuncSetAttribute, once per kernel, under a lock).
  *
  * Errors: every entry point returns DCNV4_OK (0) or a negative status.  All
  * argument checks run before any HIP call, so a rejected call has no side
