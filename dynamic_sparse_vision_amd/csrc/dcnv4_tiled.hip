@@ -53,6 +53,10 @@ constexpr int kMaxRowChunks = 8;      // a staged row spans at most 8 x 64 slots
 constexpr int kMaxTileThreads = 512;  // threads of an output-tile block
 constexpr int kMaxBins = 768;         // corner-cell bins of a cell tile (3 per thread)
 constexpr unsigned kOutOfRange = 0x80000000u;   // >= any buffer size used here
+// s_waitcnt immediate: vector memory count 0, export and LDS/scalar counts
+// left at their maxima (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
+// lgkmcnt [11:8])
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 struct TArgs {
     Geom geo;
@@ -72,6 +76,7 @@ struct TArgs {
     unsigned ps_magic;
     int om_dw;                   // staged dwords per pixel
     unsigned om_dw_magic, tw_magic;
+    unsigned npad_magic;         // ceil(2^32 / (P - 3GK)), padding entries per pixel
     int om_lds_bytes;
     // cell tiles (backward grad_value)
     int ch, cw, ctiles_y, ctiles_x;
@@ -178,30 +183,41 @@ __device__ __forceinline__ void staging_done()
 // start one element into it).  Value rows of group g for the tile plus the
 // halo: region pixel (rr, cc) is image pixel (ry0 + rr, rx0 + cc) and starts
 // at 16-byte slot (rr*rw + cc)*ps; zeros outside the image.
+// Per-lane byte offsets, within an image row of offset_mask (pixel stride
+// pix_bytes), of the slots of a tile row that holds `w` dwords per pixel from
+// byte `first` of each pixel: slot j = c*64 + lane is dword j % w of tile
+// column j / w; kOutOfRange past the tile or the image.
+__device__ __forceinline__ void pixel_row_offsets(const TArgs &a, const Tile &t, int w, unsigned w_magic,
+                                                  unsigned pix_bytes, unsigned first, unsigned (&lo)[kMaxRowChunks])
+{
+    const int lane = threadIdx.x & 63;
+    const int row_slots = a.tw * w;
+#pragma unroll
+    for (int c = 0; c < kMaxRowChunks; ++c) {
+        lo[c] = kOutOfRange;
+        if (c * 64 < row_slots) {
+            const int j = c * 64 + lane;
+            const int px = (int)divm((unsigned)j, w_magic);
+            const int d = j - px * w;
+            const int ox = t.ox0 + px;
+            if (px < a.tw && ox < a.geo.Wo)
+                lo[c] = (unsigned)ox * pix_bytes + first + 4u * (unsigned)d;
+        }
+    }
+}
+
 __device__ __forceinline__ void stage_tile(const TArgs &a, const Tile &t, char *om_s, char *val_s, int es)
 {
     const Geom &geo = a.geo;
     const int lane = threadIdx.x & 63;
     {
         unsigned lo[kMaxRowChunks];
-        const int row_slots = a.tw * a.om_dw;
-        const unsigned gofs = (unsigned)((t.g * 3 * a.K * es) & ~3);
-#pragma unroll
-        for (int c = 0; c < kMaxRowChunks; ++c) {
-            lo[c] = kOutOfRange;
-            if (c * 64 < row_slots) {
-                const int j = c * 64 + lane;
-                const int px = (int)divm((unsigned)j, a.om_dw_magic);
-                const int d = j - px * a.om_dw;
-                const int ox = t.ox0 + px;
-                if (px < a.tw && ox < geo.Wo)
-                    lo[c] = (unsigned)(ox * a.P * es) + gofs + 4u * (unsigned)d;
-            }
-        }
+        pixel_row_offsets(a, t, a.om_dw, a.om_dw_magic, (unsigned)(a.P * es),
+                          (unsigned)((t.g * 3 * a.K * es) & ~3), lo);
         const unsigned row_bytes = (unsigned)(geo.Wo * a.P * es);
         const int row0 = t.n * geo.Ho + t.oy0;
         const int rows_in = geo.Ho - t.oy0;
-        stage_rows<4>(rsrc(a.om, a.om_bytes), om_s, a.th, row_slots, lo, [&](int rr) {
+        stage_rows<4>(rsrc(a.om, a.om_bytes), om_s, a.th, a.tw * a.om_dw, lo, [&](int rr) {
             return rr < rows_in ? (unsigned)(row0 + rr) * row_bytes : kOutOfRange;
         });
     }
@@ -282,6 +298,22 @@ __device__ __forceinline__ bool live_loc(const Geom &g, float lh, float lw)
     return lh >= -1.0f && lh < (float)g.H && lw >= -1.0f && lw < (float)g.W;
 }
 
+// Corners of a far sample from global memory: loads only (the caller uses
+// the registers later, so the loads overlap other work).
+template <int NV>
+__device__ __forceinline__ void far_corner_loads(__amdgpu_buffer_rsrc_t vr, unsigned off, unsigned cs, unsigned rs,
+                                                 u32x4 (&v00)[NV], u32x4 (&v01)[NV], u32x4 (&v10)[NV],
+                                                 u32x4 (&v11)[NV])
+{
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        v00[v] = load16(vr, off + 16 * v);
+        v01[v] = load16(vr, off + cs + 16 * v);
+        v10[v] = load16(vr, off + rs + 16 * v);
+        v11[v] = load16(vr, off + rs + cs + 16 * v);
+    }
+}
+
 // ---- forward ---------------------------------------------------------------
 
 template <typename T, int DP>
@@ -315,7 +347,17 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_fwd_tiled(TArgs a)
     for (int c = 0; c < DP; ++c)
         acc[c] = 0.0f;
 
+    // the first far sample's corners are loaded as soon as it is found, so
+    // the loads overlap the rest of the near loop; later ones wait (rare)
+    const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
+    const int chan_off = (t.g * a.Cg + chunk * DP) * es;
+    const unsigned cs = (unsigned)(geo.C * es), rs = (unsigned)geo.W * cs;
     unsigned farbits = 0;
+    int pk = -1;
+    u32x4 p00[NV], p01[NV], p10[NV], p11[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+        p00[v] = p01[v] = p10[v] = p11[v] = u32x4{0u, 0u, 0u, 0u};
     for (int k = 0; k < a.K; ++k) {
         int gi, gj;
         grid_point(geo, k, gi, gj);
@@ -324,24 +366,34 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_fwd_tiled(TArgs a)
         const float m = Store<T>::scalar(om[2 * a.K + k]);
         const float bh = nf.bh0 + (float)(gj * geo.dh), bw = nf.bw0 + (float)(gi * geo.dw);
         const NearSample s = near_sample(nf, geo.scale, bh, bw, dx, dy);
-        farbits |= (!s.nr && live_loc(geo, s.lh, s.lw)) ? (1u << k) : 0u;
+        if (!s.nr && live_loc(geo, s.lh, s.lw)) {
+            if (pk < 0) {
+                pk = k;
+                Footprint f;
+                f.h0 = (int)s.fh;
+                f.w0 = (int)s.fw;
+                far_corner_loads<NV>(vr, corner_offset(geo, t.n, f, es, chan_off), cs, rs, p00, p01, p10, p11);
+            } else {
+                farbits |= 1u << k;
+            }
+        }
         // a sample that is not near gets zero weights (its reads hit slot 0)
         const float ah = s.nr ? s.lh - s.fh : 0.0f, aw = s.nr ? s.lw - s.fw : 0.0f;
         const float mm = s.nr ? m : 0.0f;
         const float mh = __builtin_fmaf(-mm, ah, mm), ml = mm * ah;
         const float w00 = __builtin_fmaf(-mh, aw, mh), w01 = mh * aw;
         const float w10 = __builtin_fmaf(-ml, aw, ml), w11 = ml * aw;
-        const u32x4 *p00 = reinterpret_cast<const u32x4 *>(vb + s.addr);
-        const u32x4 *p01 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.colb);
-        const u32x4 *p10 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.rowb);
-        const u32x4 *p11 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.rowb + nf.colb);
+        const u32x4 *q00 = reinterpret_cast<const u32x4 *>(vb + s.addr);
+        const u32x4 *q01 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.colb);
+        const u32x4 *q10 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.rowb);
+        const u32x4 *q11 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.rowb + nf.colb);
         u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            v00[v] = p00[v];
-            v01[v] = p01[v];
-            v10[v] = p10[v];
-            v11[v] = p11[v];
+            v00[v] = q00[v];
+            v01[v] = q01[v];
+            v10[v] = q10[v];
+            v11[v] = q11[v];
         }
 #pragma unroll
         for (int c = 0; c < DP; ++c) {
@@ -354,41 +406,36 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_fwd_tiled(TArgs a)
         }
     }
 
-    if (farbits) {
-        // far samples: corners from global memory; corners outside the image
-        // get weight 0 (the buffer range check zero-fills reads past the end)
-        const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
-        const int chan_off = (t.g * a.Cg + chunk * DP) * es;
-        const unsigned cs = (unsigned)(geo.C * es), rs = (unsigned)geo.W * cs;
-        do {
-            const int k = __builtin_ctz(farbits);
+    // far samples: corners outside the image get weight 0 (the buffer range
+    // check zero-fills reads past the end)
+    while (pk >= 0 || farbits) {
+        int k;
+        const bool pre = pk >= 0;
+        if (pre) {
+            k = pk;
+            pk = -1;
+        } else {
+            k = __builtin_ctz(farbits);
             farbits &= farbits - 1;
-            const float dx = Store<T>::scalar(om[2 * k]);
-            const float dy = Store<T>::scalar(om[2 * k + 1]);
-            const float m = Store<T>::scalar(om[2 * a.K + k]);
-            const Loc l = locate_lane(a, oy, ox, k, dx, dy);
-            const Footprint f = footprint(geo, l);
-            float w00, w01, w10, w11;
-            masked_weights(f, m, w00, w01, w10, w11);
-            const unsigned off = corner_offset(geo, t.n, f, es, chan_off);
-            u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
+        }
+        const float dx = Store<T>::scalar(om[2 * k]);
+        const float dy = Store<T>::scalar(om[2 * k + 1]);
+        const float m = Store<T>::scalar(om[2 * a.K + k]);
+        const Loc l = locate_lane(a, oy, ox, k, dx, dy);
+        const Footprint f = footprint(geo, l);
+        float w00, w01, w10, w11;
+        masked_weights(f, m, w00, w01, w10, w11);
+        if (!pre)
+            far_corner_loads<NV>(vr, corner_offset(geo, t.n, f, es, chan_off), cs, rs, p00, p01, p10, p11);
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                v00[v] = load16(vr, off + 16 * v);
-                v01[v] = load16(vr, off + cs + 16 * v);
-                v10[v] = load16(vr, off + rs + 16 * v);
-                v11[v] = load16(vr, off + rs + cs + 16 * v);
-            }
-#pragma unroll
-            for (int c = 0; c < DP; ++c) {
-                float x = acc[c];
-                x = __builtin_fmaf(w00, Store<T>::get(v00, c), x);
-                x = __builtin_fmaf(w01, Store<T>::get(v01, c), x);
-                x = __builtin_fmaf(w10, Store<T>::get(v10, c), x);
-                x = __builtin_fmaf(w11, Store<T>::get(v11, c), x);
-                acc[c] = x;
-            }
-        } while (farbits);
+        for (int c = 0; c < DP; ++c) {
+            float x = acc[c];
+            x = __builtin_fmaf(w00, Store<T>::get(p00, c), x);
+            x = __builtin_fmaf(w01, Store<T>::get(p01, c), x);
+            x = __builtin_fmaf(w10, Store<T>::get(p10, c), x);
+            x = __builtin_fmaf(w11, Store<T>::get(p11, c), x);
+            acc[c] = x;
+        }
     }
 
     u32x4 res[NV];
@@ -444,6 +491,7 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
     const unsigned cs = (unsigned)(geo.C * 4), rs = (unsigned)geo.W * cs;
     const char *vb = val_s + chunk * NV * 16;
     const unsigned pix_off = ((unsigned)((t.n * geo.Ho + oy) * geo.Wo + ox)) * cs + (unsigned)chan_off;
+    const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
 
     float go[DP];
     {
@@ -454,9 +502,19 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
             for (int e = 0; e < 4; ++e)
                 go[4 * v + e] = r[e];
         }
+        // wait for grad_out here: inside the loop the compiler cannot tell
+        // these loads from the far-sample prefetch and would drain both
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
 
+    // the first far sample's corners are loaded as soon as it is found, so
+    // the loads overlap the rest of the near loop; later ones wait (rare)
     unsigned farbits = 0;
+    int pk = -1;
+    u32x4 p00[NV], p01[NV], p10[NV], p11[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+        p00[v] = p01[v] = p10[v] = p11[v] = u32x4{0u, 0u, 0u, 0u};
     for (int k = 0; k < a.K; ++k) {
         int gi, gj;
         grid_point(geo, k, gi, gj);
@@ -466,18 +524,28 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
         const bool nr = s.nr && valid;
         const int addr = nr ? s.addr : 0;
         const bool far = valid && !s.nr && live_loc(geo, s.lh, s.lw);
-        farbits |= far ? (1u << k) : 0u;
-        const u32x4 *p00 = reinterpret_cast<const u32x4 *>(vb + addr);
-        const u32x4 *p01 = reinterpret_cast<const u32x4 *>(vb + addr + nf.colb);
-        const u32x4 *p10 = reinterpret_cast<const u32x4 *>(vb + addr + nf.rowb);
-        const u32x4 *p11 = reinterpret_cast<const u32x4 *>(vb + addr + nf.rowb + nf.colb);
+        if (far) {
+            if (pk < 0) {
+                pk = k;
+                Footprint f;
+                f.h0 = (int)s.fh;
+                f.w0 = (int)s.fw;
+                far_corner_loads<NV>(vr, corner_offset(geo, t.n, f, 4, chan_off), cs, rs, p00, p01, p10, p11);
+            } else {
+                farbits |= 1u << k;
+            }
+        }
+        const u32x4 *q00 = reinterpret_cast<const u32x4 *>(vb + addr);
+        const u32x4 *q01 = reinterpret_cast<const u32x4 *>(vb + addr + nf.colb);
+        const u32x4 *q10 = reinterpret_cast<const u32x4 *>(vb + addr + nf.rowb);
+        const u32x4 *q11 = reinterpret_cast<const u32x4 *>(vb + addr + nf.rowb + nf.colb);
         u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            v00[v] = p00[v];
-            v01[v] = p01[v];
-            v10[v] = p10[v];
-            v11[v] = p11[v];
+            v00[v] = q00[v];
+            v01[v] = q01[v];
+            v10[v] = q10[v];
+            v11[v] = q11[v];
         }
         float t00 = 0.0f, t01 = 0.0f, t10 = 0.0f, t11 = 0.0f;
 #pragma unroll
@@ -507,10 +575,9 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
         }
     }
 
-    // far samples, one per lane and iteration; the whole wave stays in the
-    // loop for the grad_value atomics
+    // far samples, one per lane and iteration (the prefetched one first); the
+    // whole wave stays in the loop for the grad_value atomics
     {
-        const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
         const __amdgpu_buffer_rsrc_t gr = rsrc(a.gvalue, a.value_bytes);
         // this lane's part of a far sample's grad_value update: corner
         // lane / DP, channel lane % DP of the owner's DP channels
@@ -518,35 +585,35 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
         const int my_corner = lane / DP, my_c = lane % DP;
         const unsigned my_corner_off =
             (unsigned)(my_corner & 1) * cs + (unsigned)(my_corner >> 1) * rs + 4u * (unsigned)my_c;
-        while (__ballot(farbits != 0)) {
-            const bool has = farbits != 0;
+        while (__ballot(pk >= 0 || farbits != 0)) {
+            const bool has = pk >= 0 || farbits != 0;
             int k = 0;
             float gm = 0.0f, gw = 0.0f, gh = 0.0f, m = 0.0f;
             unsigned off = 0;
             float w00 = 0.0f, w01 = 0.0f, w10 = 0.0f, w11 = 0.0f;
             if (has) {
-                k = __builtin_ctz(farbits);
-                farbits &= farbits - 1;
+                const bool pre = pk >= 0;
+                if (pre) {
+                    k = pk;
+                    pk = -1;
+                } else {
+                    k = __builtin_ctz(farbits);
+                    farbits &= farbits - 1;
+                }
                 const float dx = om[2 * k], dy = om[2 * k + 1];
                 m = om[2 * a.K + k];
                 const Loc l = locate_lane(a, oy, ox, k, dx, dy);
                 const Footprint f = footprint(geo, l);
                 off = corner_offset(geo, t.n, f, 4, chan_off);
-                u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
-#pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    v00[v] = load16(vr, off + 16 * v);
-                    v01[v] = load16(vr, off + cs + 16 * v);
-                    v10[v] = load16(vr, off + rs + 16 * v);
-                    v11[v] = load16(vr, off + rs + cs + 16 * v);
-                }
+                if (!pre)
+                    far_corner_loads<NV>(vr, off, cs, rs, p00, p01, p10, p11);
                 float t00 = 0.0f, t01 = 0.0f, t10 = 0.0f, t11 = 0.0f;
 #pragma unroll
                 for (int c = 0; c < DP; ++c) {
-                    t00 = __builtin_fmaf(go[c], Store<float>::get(v00, c), t00);
-                    t01 = __builtin_fmaf(go[c], Store<float>::get(v01, c), t01);
-                    t10 = __builtin_fmaf(go[c], Store<float>::get(v10, c), t10);
-                    t11 = __builtin_fmaf(go[c], Store<float>::get(v11, c), t11);
+                    t00 = __builtin_fmaf(go[c], Store<float>::get(p00, c), t00);
+                    t01 = __builtin_fmaf(go[c], Store<float>::get(p01, c), t01);
+                    t10 = __builtin_fmaf(go[c], Store<float>::get(p10, c), t10);
+                    t11 = __builtin_fmaf(go[c], Store<float>::get(p11, c), t11);
                 }
                 // zero-extended image: dots of corners outside are 0
                 t00 = (f.r0 && f.c0) ? t00 : 0.0f;
@@ -594,36 +661,39 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
     }
     __syncthreads();
 
-    // write the group's gradient entries of the tile; group 0 also zeroes
-    // the padding channels
+    // write the group's gradient rows of the tile back, slot for slot as they
+    // were staged; group 0 also zeroes the padding channels
     {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-        const int row_elems = a.tw * K3;
         const __amdgpu_buffer_rsrc_t r = rsrc(a.gom, a.om_bytes);
-        const int pad0 = a.G * K3, npad = a.P - pad0;
-        for (int py2 = wave; py2 < a.th; py2 += nwaves) {
-            const int oy2 = t.oy0 + py2;
-            if (oy2 >= geo.Ho)
-                break;
-            for (int e = lane; e < row_elems; e += 64) {
-                const int px2 = (int)divm((unsigned)e, a.k3_magic);
-                const int j = e - px2 * K3;
-                const int ox2 = t.ox0 + px2;
-                if (ox2 < geo.Wo) {
-                    const unsigned idx = (unsigned)(((t.n * geo.Ho + oy2) * geo.Wo + ox2) * a.P + t.g * K3 + j);
-                    __builtin_amdgcn_raw_buffer_store_b32(
-                        __builtin_bit_cast(unsigned, om_s[(py2 * a.tw + px2) * a.om_dw + j]), r, idx * 4u, 0, 0);
+        const unsigned row_bytes = (unsigned)(geo.Wo * a.P * 4);
+        const int row0 = t.n * geo.Ho + t.oy0;
+        const int rows = min(a.th, geo.Ho - t.oy0);
+        {
+            unsigned lo[kMaxRowChunks];
+            pixel_row_offsets(a, t, a.om_dw, a.om_dw_magic, (unsigned)(a.P * 4), (unsigned)(t.g * K3 * 4), lo);
+            const int row_slots = a.tw * a.om_dw;
+            for (int rr = wave; rr < rows; rr += nwaves) {
+                const unsigned base = (unsigned)(row0 + rr) * row_bytes;
+                const unsigned *src = reinterpret_cast<const unsigned *>(om_s) + rr * row_slots;
+#pragma unroll
+                for (int c = 0; c < kMaxRowChunks; ++c) {
+                    if (c * 64 < row_slots && c * 64 + lane < row_slots && lo[c] != kOutOfRange)
+                        __builtin_amdgcn_raw_buffer_store_b32(src[c * 64 + lane], r, base + lo[c], 0, 0);
                 }
             }
-            if (t.g == 0 && npad > 0) {
-                for (int e = lane; e < a.tw * npad; e += 64) {
-                    const int px2 = e / npad;
-                    const int j = e - px2 * npad;
-                    const int ox2 = t.ox0 + px2;
-                    if (ox2 < geo.Wo) {
-                        const unsigned idx = (unsigned)(((t.n * geo.Ho + oy2) * geo.Wo + ox2) * a.P + pad0 + j);
-                        __builtin_amdgcn_raw_buffer_store_b32(0u, r, idx * 4u, 0, 0);
-                    }
+        }
+        const int npad = a.P - a.G * K3;
+        if (t.g == 0 && npad > 0) {
+            unsigned lo[kMaxRowChunks];
+            pixel_row_offsets(a, t, npad, a.npad_magic, (unsigned)(a.P * 4), (unsigned)(a.G * K3 * 4), lo);
+            const int row_slots = a.tw * npad;
+            for (int rr = wave; rr < rows; rr += nwaves) {
+                const unsigned base = (unsigned)(row0 + rr) * row_bytes;
+#pragma unroll
+                for (int c = 0; c < kMaxRowChunks; ++c) {
+                    if (c * 64 < row_slots && c * 64 + lane < row_slots && lo[c] != kOutOfRange)
+                        __builtin_amdgcn_raw_buffer_store_b32(0u, r, base + lo[c], 0, 0);
                 }
             }
         }
@@ -932,6 +1002,7 @@ TArgs make_targs(const Problem &p, const TilePlan &tp)
     a.ps_magic = magic_for(tp.ps);
     a.om_dw = tp.om_dw;
     a.om_dw_magic = magic_for(tp.om_dw);
+    a.npad_magic = magic_for(p.P - 3 * p.G * p.K);
     a.tw_magic = magic_for(tp.tw);
     a.om_lds_bytes = tp.om_lds_bytes;
     a.ch = tp.ch;
@@ -1011,7 +1082,7 @@ hipError_t launch_backward_tiled(const Problem &p, const TilePlan &tp, const voi
                                  const void *grad_output, void *grad_value, void *grad_offset_mask,
                                  hipStream_t stream)
 {
-    if (!out_tiles_ok(p, tp) || p.K > 25 || tp.ch * tp.cw > 256 || (tp.ch + 1) * (tp.cw + 1) > kMaxBins ||
+    if (!out_tiles_ok(p, tp) || p.K > 25 || tp.tw * (p.P - 3 * p.G * p.K) > 64 * kMaxRowChunks || tp.ch * tp.cw > 256 || (tp.ch + 1) * (tp.cw + 1) > kMaxBins ||
         tp.src_cap < 1 || tp.src_cap > 256 || tp.gps * 4 < p.Cg || tp.rec_offset < (2 * kMaxBins + 8) * 4 ||
         tp.rec_offset % 16 != 0 || tp.gs_offset < tp.rec_offset + tp.src_cap * p.K * 16 ||
         tp.splat_lds_bytes < tp.gs_offset + tp.src_cap * tp.gps * 16 ||
