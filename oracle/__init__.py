@@ -8,7 +8,9 @@ arrays into it.  It shares no code with the HIP path.
 
 Every function here follows the definition cited in ``dcnv4_oracle.c``
 ("Efficient Deformable ConvNets", DCNv3 recap equation with the softmax
-removed, bilinear sampling with zero padding).
+removed, bilinear sampling with zero padding).  ``softmax=True`` selects the
+DCNv3 form, with the masks of each (pixel, group) normalised by a softmax
+over the K points.
 """
 from __future__ import annotations
 
@@ -48,10 +50,15 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     i, f, p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
     geo = [i] * 11 + [i, i, f, i, i, i]  # N H W kh kw sh sw ph pw dh dw | G Cg | scale | rc P nthreads
+    geo_ex = geo[:-1] + [i, i]   # ... rc P softmax nthreads
     lib.dcnv4o_forward.argtypes = [p, p, p] + geo
     lib.dcnv4o_forward.restype = i
     lib.dcnv4o_backward.argtypes = [p, p, p, p, p] + geo
     lib.dcnv4o_backward.restype = i
+    lib.dcnv4o_forward_ex.argtypes = [p, p, p] + geo_ex
+    lib.dcnv4o_forward_ex.restype = i
+    lib.dcnv4o_backward_ex.argtypes = [p, p, p, p, p] + geo_ex
+    lib.dcnv4o_backward_ex.restype = i
     lib.dcnv4o_output_size.argtypes = [i, i, i, i, i]
     lib.dcnv4o_output_size.restype = i
     lib.dcnv4o_grid.argtypes = [i, i, i, p, p]
@@ -95,7 +102,7 @@ def _geom(value, offset_mask, kernel_h, kernel_w, stride_h, stride_w, pad_h, pad
 
 def forward(value, offset_mask, kernel_h=3, kernel_w=3, stride_h=1, stride_w=1,
             pad_h=1, pad_w=1, dilation_h=1, dilation_w=1, group=1, group_channels=None,
-            offset_scale=1.0, remove_center=False, nthreads=0, lib=None):
+            offset_scale=1.0, remove_center=False, softmax=False, nthreads=0, lib=None):
     """y (N,Ho,Wo,C) float64 from value (N,H,W,C) and offset_mask (N,Ho,Wo,P).
 
     Inputs are converted to float32 (exact for fp16/bf16 storage values).
@@ -113,8 +120,8 @@ def forward(value, offset_mask, kernel_h=3, kernel_w=3, stride_h=1, stride_w=1,
     if offset_mask.shape[:3] != (N, Ho, Wo):
         raise ValueError(f"offset_mask shape {offset_mask.shape} != {(N, Ho, Wo)}+(P,)")
     out = np.zeros((N, Ho, Wo, group * group_channels), np.float64)
-    K = lib.dcnv4o_forward(value.ctypes.data, offset_mask.ctypes.data, out.ctypes.data,
-                           *g, int(nthreads))
+    K = lib.dcnv4o_forward_ex(value.ctypes.data, offset_mask.ctypes.data, out.ctypes.data,
+                              *g, int(bool(softmax)), int(nthreads))
     if K < 0:
         raise ValueError("oracle rejected the geometry")
     return out
@@ -122,8 +129,8 @@ def forward(value, offset_mask, kernel_h=3, kernel_w=3, stride_h=1, stride_w=1,
 
 def backward(value, offset_mask, grad_output, kernel_h=3, kernel_w=3, stride_h=1,
              stride_w=1, pad_h=1, pad_w=1, dilation_h=1, dilation_w=1, group=1,
-             group_channels=None, offset_scale=1.0, remove_center=False, nthreads=0,
-             lib=None):
+             group_channels=None, offset_scale=1.0, remove_center=False, softmax=False,
+             nthreads=0, lib=None):
     """(grad_value (N,H,W,C), grad_offset_mask (N,Ho,Wo,P)), both float64."""
     lib = lib or load()
     value = _f32(value)
@@ -140,8 +147,8 @@ def backward(value, offset_mask, grad_output, kernel_h=3, kernel_w=3, stride_h=1
         raise ValueError("shape mismatch")
     gv = np.zeros(value.shape, np.float64)
     gom = np.zeros(offset_mask.shape, np.float64)
-    K = lib.dcnv4o_backward(value.ctypes.data, offset_mask.ctypes.data, grad_output.ctypes.data,
-                            gv.ctypes.data, gom.ctypes.data, *g, int(nthreads))
+    K = lib.dcnv4o_backward_ex(value.ctypes.data, offset_mask.ctypes.data, grad_output.ctypes.data,
+                               gv.ctypes.data, gom.ctypes.data, *g, int(bool(softmax)), int(nthreads))
     if K < 0:
         raise ValueError("oracle rejected the geometry")
     return gv, gom

@@ -14,7 +14,11 @@
  *     C' = C / G channels: "Efficient Deformable ConvNets" as summarised in the
  *     CSDN walkthrough "DCNv4论文解析", section 1.2 (DCNv3 recap equation).
  *   - No softmax over K: m is an unnormalised, signed scalar (same walkthrough,
- *     section 2.1, "增强动态特性").
+ *     section 2.1, "增强动态特性").  The _ex entry points also offer the
+ *     DCNv3 form that section 2.1 contrasts it with (the recap equation of
+ *     section 1.2 with m normalised by a softmax over the K points of each
+ *     pixel and group): with softmax != 0, m_gk is replaced by
+ *     p_gk = exp(m_gk) / sum_j exp(m_gj), computed in double.
  *   - The scalar offset_scale, stride, pad, dilation and remove_center
  *     arguments: the dcnv4_cuda_forward / DCNv4Function.forward argument lists
  *     quoted in the blog "DCNv4架构解析", sections "内存访问优化策略" and
@@ -46,6 +50,11 @@
  *
  * Weights are formed in fp32 exactly as written below (one rounding per
  * product); everything after the weights is accumulated in double.
+ *
+ *   R-softmax the softmax runs over all K points of a (pixel, group), live or
+ *             not (a point outside the image keeps its share of the weight
+ *             and samples zeros); its gradient is the softmax Jacobian:
+ *             dL/dm_k = p_k * (dL/dp_k - sum_j p_j * dL/dp_j).
  *
  * Pins (tests that tie this oracle to something other than itself): identity
  * and stride-2 subsampling with a one-hot centre mask, grouped depthwise
@@ -119,6 +128,22 @@ static footprint bilinear_footprint(float loc_h, float loc_w, int H, int W)
     return f;
 }
 
+/* Softmax of the K masks of one (pixel, group) in double (R-softmax). */
+static void softmax_masks(const float *m, int K, double *p)
+{
+    double mx = (double)m[0];
+    for (int k = 1; k < K; ++k)
+        if ((double)m[k] > mx)
+            mx = (double)m[k];
+    double sum = 0.0;
+    for (int k = 0; k < K; ++k) {
+        p[k] = exp((double)m[k] - mx);
+        sum += p[k];
+    }
+    for (int k = 0; k < K; ++k)
+        p[k] /= sum;
+}
+
 /* Value of the zero-extended image x[n][r][c][ch] (channel-last). */
 static double xval(const float *value, int n, int r, int c, int ch, int H, int W, int C)
 {
@@ -133,11 +158,11 @@ static double xval(const float *value, int n, int r, int c, int ch, int H, int W
  * exactly to fp32 by the caller.  nthreads <= 0 means the OpenMP default.
  * Returns K, or -1 on bad geometry.
  */
-int dcnv4o_forward(const float *value, const float *offset_mask, double *out,
-                   int N, int H, int W, int kernel_h, int kernel_w,
-                   int stride_h, int stride_w, int pad_h, int pad_w,
-                   int dil_h, int dil_w, int G, int Cg, float offset_scale,
-                   int remove_center, int P, int nthreads)
+int dcnv4o_forward_ex(const float *value, const float *offset_mask, double *out,
+                      int N, int H, int W, int kernel_h, int kernel_w,
+                      int stride_h, int stride_w, int pad_h, int pad_w,
+                      int dil_h, int dil_w, int G, int Cg, float offset_scale,
+                      int remove_center, int P, int softmax, int nthreads)
 {
     int gi[ORACLE_MAX_K], gj[ORACLE_MAX_K];
     if ((size_t)kernel_h * kernel_w > ORACLE_MAX_K)
@@ -157,6 +182,7 @@ int dcnv4o_forward(const float *value, const float *offset_mask, double *out,
         int n = (int)(row / Ho);
         int ho = (int)(row % Ho);
         double *acc = (double *)malloc(sizeof(double) * (size_t)(Cg > 0 ? Cg : 1));
+        double *pk = (double *)malloc(sizeof(double) * (size_t)K);
         for (int wo = 0; wo < Wo; ++wo) {
             const float *om = offset_mask + (((size_t)n * Ho + ho) * Wo + wo) * P;
             double *y = out + (((size_t)n * Ho + ho) * Wo + wo) * C;
@@ -164,10 +190,12 @@ int dcnv4o_forward(const float *value, const float *offset_mask, double *out,
                 const float *omg = om + (size_t)g * 3 * K;
                 for (int c = 0; c < Cg; ++c)
                     acc[c] = 0.0;
+                if (softmax)
+                    softmax_masks(omg + 2 * K, K, pk);
                 for (int k = 0; k < K; ++k) {
                     float dx = omg[2 * k];
                     float dy = omg[2 * k + 1];
-                    float m = omg[2 * K + k];
+                    double m = softmax ? pk[k] : (double)omg[2 * K + k];
                     float loc_w = fmaf(offset_scale, dx, (float)(wo * stride_w - pad_w + gi[k] * dil_w));
                     float loc_h = fmaf(offset_scale, dy, (float)(ho * stride_h - pad_h + gj[k] * dil_h));
                     footprint f = bilinear_footprint(loc_h, loc_w, H, W);
@@ -179,16 +207,27 @@ int dcnv4o_forward(const float *value, const float *offset_mask, double *out,
                                  + (double)f.wt[1] * xval(value, n, f.h0, f.w0 + 1, ch, H, W, C)
                                  + (double)f.wt[2] * xval(value, n, f.h0 + 1, f.w0, ch, H, W, C)
                                  + (double)f.wt[3] * xval(value, n, f.h0 + 1, f.w0 + 1, ch, H, W, C);
-                        acc[c] += (double)m * s;
+                        acc[c] += m * s;
                     }
                 }
                 for (int c = 0; c < Cg; ++c)
                     y[g * Cg + c] = acc[c];
             }
         }
+        free(pk);
         free(acc);
     }
     return K;
+}
+
+int dcnv4o_forward(const float *value, const float *offset_mask, double *out,
+                   int N, int H, int W, int kernel_h, int kernel_w,
+                   int stride_h, int stride_w, int pad_h, int pad_w,
+                   int dil_h, int dil_w, int G, int Cg, float offset_scale,
+                   int remove_center, int P, int nthreads)
+{
+    return dcnv4o_forward_ex(value, offset_mask, out, N, H, W, kernel_h, kernel_w, stride_h, stride_w,
+                             pad_h, pad_w, dil_h, dil_w, G, Cg, offset_scale, remove_center, P, 0, nthreads);
 }
 
 /*
@@ -207,12 +246,12 @@ int dcnv4o_forward(const float *value, const float *offset_mask, double *out,
  * disjoint, so each image is accumulated serially and the result is
  * deterministic.  Returns K, or -1 on bad geometry.
  */
-int dcnv4o_backward(const float *value, const float *offset_mask, const float *grad_out,
-                    double *grad_value, double *grad_offset_mask,
-                    int N, int H, int W, int kernel_h, int kernel_w,
-                    int stride_h, int stride_w, int pad_h, int pad_w,
-                    int dil_h, int dil_w, int G, int Cg, float offset_scale,
-                    int remove_center, int P, int nthreads)
+int dcnv4o_backward_ex(const float *value, const float *offset_mask, const float *grad_out,
+                       double *grad_value, double *grad_offset_mask,
+                       int N, int H, int W, int kernel_h, int kernel_w,
+                       int stride_h, int stride_w, int pad_h, int pad_w,
+                       int dil_h, int dil_w, int G, int Cg, float offset_scale,
+                       int remove_center, int P, int softmax, int nthreads)
 {
     int gi[ORACLE_MAX_K], gj[ORACLE_MAX_K];
     if ((size_t)kernel_h * kernel_w > ORACLE_MAX_K)
@@ -231,6 +270,7 @@ int dcnv4o_backward(const float *value, const float *offset_mask, const float *g
 #endif
     for (int n = 0; n < N; ++n) {
         double *gv = grad_value + (size_t)n * H * W * C;
+        double *pk = (double *)malloc(sizeof(double) * (size_t)K);
         for (int ho = 0; ho < Ho; ++ho) {
             for (int wo = 0; wo < Wo; ++wo) {
                 size_t pix = ((size_t)n * Ho + ho) * Wo + wo;
@@ -240,10 +280,12 @@ int dcnv4o_backward(const float *value, const float *offset_mask, const float *g
                 for (int g = 0; g < G; ++g) {
                     const float *omg = om + (size_t)g * 3 * K;
                     double *gomg = gom + (size_t)g * 3 * K;
+                    if (softmax)
+                        softmax_masks(omg + 2 * K, K, pk);
                     for (int k = 0; k < K; ++k) {
                         float dx = omg[2 * k];
                         float dy = omg[2 * k + 1];
-                        float m = omg[2 * K + k];
+                        double m = softmax ? pk[k] : (double)omg[2 * K + k];
                         float loc_w = fmaf(offset_scale, dx, (float)(wo * stride_w - pad_w + gi[k] * dil_w));
                         float loc_h = fmaf(offset_scale, dy, (float)(ho * stride_h - pad_h + gj[k] * dil_h));
                         footprint f = bilinear_footprint(loc_h, loc_w, H, W);
@@ -266,16 +308,37 @@ int dcnv4o_backward(const float *value, const float *offset_mask, const float *g
                             for (int q = 0; q < 4; ++q) {
                                 if (rr[q] < 0 || rr[q] >= H || cc[q] < 0 || cc[q] >= W)
                                     continue;
-                                gv[((size_t)rr[q] * W + cc[q]) * C + ch] += (double)m * (double)f.wt[q] * go;
+                                gv[((size_t)rr[q] * W + cc[q]) * C + ch] += m * (double)f.wt[q] * go;
                             }
                         }
-                        gomg[2 * k] = (double)offset_scale * (double)m * gw;
-                        gomg[2 * k + 1] = (double)offset_scale * (double)m * gh;
+                        gomg[2 * k] = (double)offset_scale * m * gw;
+                        gomg[2 * k + 1] = (double)offset_scale * m * gh;
                         gomg[2 * K + k] = gm;
+                    }
+                    if (softmax) {
+                        /* dL/dm_k = p_k * (dL/dp_k - sum_j p_j dL/dp_j) (R-softmax) */
+                        double s = 0.0;
+                        for (int k = 0; k < K; ++k)
+                            s += pk[k] * gomg[2 * K + k];
+                        for (int k = 0; k < K; ++k)
+                            gomg[2 * K + k] = pk[k] * (gomg[2 * K + k] - s);
                     }
                 }
             }
         }
+        free(pk);
     }
     return K;
+}
+
+int dcnv4o_backward(const float *value, const float *offset_mask, const float *grad_out,
+                    double *grad_value, double *grad_offset_mask,
+                    int N, int H, int W, int kernel_h, int kernel_w,
+                    int stride_h, int stride_w, int pad_h, int pad_w,
+                    int dil_h, int dil_w, int G, int Cg, float offset_scale,
+                    int remove_center, int P, int nthreads)
+{
+    return dcnv4o_backward_ex(value, offset_mask, grad_out, grad_value, grad_offset_mask, N, H, W, kernel_h,
+                              kernel_w, stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, G, Cg, offset_scale,
+                              remove_center, P, 0, nthreads);
 }

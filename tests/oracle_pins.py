@@ -518,6 +518,83 @@ def pin_remove_center(lib):
     _close(c8.fwd(lib), c9.fwd(lib), 1e-12, 1e-12, "remove_center forward")
 
 
+# ---- DCNv3 softmax mode ------------------------------------------------------
+
+
+def _dyadic(a, bits=10):
+    return (np.round(a * 2.0 ** bits) / 2.0 ** bits).astype(np.float32)
+
+
+def pin_softmax_plain_reduction(lib):
+    """softmax mode = the plain operator with masks replaced by
+    scipy.special.softmax over the K points (a library routine), forward and
+    backward; its mask gradient is the softmax Jacobian applied to the plain
+    mask gradient."""
+    from scipy.special import softmax as sp_softmax
+
+    c = Case(seed=21, N=2, H=6, W=7, G=2, Cg=3, off_sigma=2.0)
+    p = sp_softmax(c.m.astype(np.float64), axis=-1)
+    om_l = c.om
+    om_p = make_om(c.dx, c.dy, p.astype(np.float32))
+    kw = c.kw_()
+    _close(oracle.forward(c.x, om_l, softmax=True, lib=lib, **kw),
+           oracle.forward(c.x, om_p, lib=lib, **kw), 1e-6, 1e-6, "softmax forward")
+    gv_s, gom_s = oracle.backward(c.x, om_l, c.g, softmax=True, lib=lib, **kw)
+    gv_p, gom_p = oracle.backward(c.x, om_p, c.g, lib=lib, **kw)
+    _close(gv_s, gv_p, 1e-6, 1e-6, "softmax grad_value")
+    dx_s, dy_s, gl = unpack_om(gom_s, c.G, c.K)
+    dx_p, dy_p, gp = unpack_om(gom_p, c.G, c.K)
+    _close(dx_s, dx_p, 1e-6, 1e-6, "softmax grad dx")
+    _close(dy_s, dy_p, 1e-6, 1e-6, "softmax grad dy")
+    # chain rule through the softmax, written with the Jacobian matrix
+    jac = np.einsum("...k,kj->...kj", p, np.eye(c.K)) - np.einsum("...k,...j->...kj", p, p)
+    _close(gl, np.einsum("...kj,...k->...j", jac, gp), 1e-6, 1e-6, "softmax Jacobian")
+
+
+def pin_softmax_invariants(lib):
+    """Shifting all K logits of a (pixel, group) by one constant changes
+    nothing; the logit gradients sum to 0 over K; a dominant centre logit
+    with zero offsets reproduces the input (identity)."""
+    c = Case(seed=22, N=1, H=5, W=6, G=2, Cg=3, off_sigma=1.5)
+    c.m = _dyadic(c.m)
+    kw = c.kw_()
+    shift = np.random.default_rng(220).integers(-3, 4, c.m.shape[:-1] + (1,)).astype(np.float32)
+    om_shift = make_om(c.dx, c.dy, (c.m + shift).astype(np.float32))
+    y0 = oracle.forward(c.x, c.om, softmax=True, lib=lib, **kw)
+    y1 = oracle.forward(c.x, om_shift, softmax=True, lib=lib, **kw)
+    _close(y1, y0, 1e-12, 1e-12, "softmax shift invariance")
+    gv, gom = oracle.backward(c.x, c.om, c.g, softmax=True, lib=lib, **kw)
+    _, _, gl = unpack_om(gom, c.G, c.K)
+    assert np.abs(gl.sum(axis=-1)).max() < 1e-12, "logit gradients must sum to 0"
+    ci = Case(seed=23, N=1, H=5, W=6, G=2, Cg=3, off_kind="zero")
+    kc = ci.pairs.index((1, 1))
+    ci.m[:] = 0
+    ci.m[..., kc] = 100.0
+    _close(oracle.forward(ci.x, ci.om, softmax=True, lib=lib, **ci.kw_()), ci.x, 1e-12, 1e-12,
+           "dominant centre logit = identity")
+
+
+def pin_softmax_finite_differences(lib):
+    """Logit gradients against central differences of <f, g> (the softmax is
+    smooth; dyadic logits and a 2^-12 step are exact in fp32)."""
+    c = Case(seed=24, N=1, H=4, W=5, G=2, Cg=2, off_sigma=1.5)
+    c.m = _dyadic(c.m)
+    kw = c.kw_()
+    _, gom = oracle.backward(c.x, c.om, c.g, softmax=True, lib=lib, **kw)
+    _, _, gl = unpack_om(gom, c.G, c.K)
+    h = np.float32(2.0 ** -12)
+    rng = np.random.default_rng(240)
+    idx = [tuple(int(v) for v in i) for i in np.argwhere(np.ones(c.m.shape, bool))]
+    for p in [idx[i] for i in rng.choice(len(idx), 30, replace=False)]:
+        mp, mm = c.m.copy(), c.m.copy()
+        mp[p] += h
+        mm[p] -= h
+        fp_ = float(np.sum(oracle.forward(c.x, make_om(c.dx, c.dy, mp), softmax=True, lib=lib, **kw) * c.g))
+        fm_ = float(np.sum(oracle.forward(c.x, make_om(c.dx, c.dy, mm), softmax=True, lib=lib, **kw) * c.g))
+        _close(gl[p], (fp_ - fm_) / (2 * float(h)), 1e-6, 1e-6, f"FD logit at {p}")
+
+
 PINS = [pin_identity, pin_stride2, pin_depthwise_conv, pin_integer_gather, pin_half_integer,
         pin_padded_bruteforce, pin_affine_image, pin_grid_sample, pin_linearity, pin_adjoint,
-        pin_finite_differences, pin_dense_jacobian, pin_padding_and_nan, pin_remove_center]
+        pin_finite_differences, pin_dense_jacobian, pin_padding_and_nan, pin_remove_center,
+        pin_softmax_plain_reduction, pin_softmax_invariants, pin_softmax_finite_differences]

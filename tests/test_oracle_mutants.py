@@ -18,7 +18,7 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "dcnv4_oracle.c")
 MUTANTS = {
     "dx_dy_swapped": [("float dx = omg[2 * k];", "float dx = omg[2 * k + 1];"),
                       ("float dy = omg[2 * k + 1];", "float dy = omg[2 * k];")],
-    "mask_interleaved_layout": [("float m = omg[2 * K + k];", "float m = omg[3 * k + 2];")],
+    "mask_interleaved_layout": [("(double)omg[2 * K + k];", "(double)omg[3 * k + 2];")],
     "grid_transposed": [("gi[K] = i;\n            gj[K] = j;", "gi[K] = j;\n            gj[K] = i;")],
     "offset_scale_dropped": [("fmaf(offset_scale, dx,", "fmaf(1.0f, dx,"),
                              ("fmaf(offset_scale, dy,", "fmaf(1.0f, dy,")],
@@ -34,19 +34,27 @@ MUTANTS = {
     "corner_swapped_in_forward": [("(double)f.wt[1] * xval(value, n, f.h0, f.w0 + 1, ch, H, W, C)",
                                    "(double)f.wt[1] * xval(value, n, f.h0 + 1, f.w0, ch, H, W, C)")],
     "output_channels_interleaved": [("y[g * Cg + c] = acc[c];", "y[c * G + g] = acc[c];")],
-    "mask_not_applied": [("acc[c] += (double)m * s;", "acc[c] += s;")],
+    "mask_not_applied": [("acc[c] += m * s;", "acc[c] += s;")],
     "grad_w_sign": [("(double)f.hh * (v[1] - v[0])", "(double)f.hh * (v[0] - v[1])")],
     "grad_h_wrong_weight": [("(double)f.hw * (v[2] - v[0])", "(double)f.hh * (v[2] - v[0])")],
-    "grad_offset_missing_m": [("(double)offset_scale * (double)m * gw", "(double)offset_scale * gw")],
-    "grad_offset_missing_scale": [("(double)offset_scale * (double)m * gh", "(double)m * gh")],
-    "grad_value_missing_m": [("+= (double)m * (double)f.wt[q] * go;", "+= (double)f.wt[q] * go;")],
+    "grad_offset_missing_m": [("(double)offset_scale * m * gw", "(double)offset_scale * gw")],
+    "grad_offset_missing_scale": [("(double)offset_scale * m * gh", "m * gh")],
+    "grad_value_missing_m": [("+= m * (double)f.wt[q] * go;", "+= (double)f.wt[q] * go;")],
     "grad_mask_corner_only": [("gm += go * s;", "gm += go * v[0];")],
-    "grad_dx_dy_slots_swapped": [("gomg[2 * k] = (double)offset_scale * (double)m * gw;",
-                                  "gomg[2 * k] = (double)offset_scale * (double)m * gh;"),
-                                 ("gomg[2 * k + 1] = (double)offset_scale * (double)m * gh;",
-                                  "gomg[2 * k + 1] = (double)offset_scale * (double)m * gw;")],
+    "grad_dx_dy_slots_swapped": [("gomg[2 * k] = (double)offset_scale * m * gw;",
+                                  "gomg[2 * k] = (double)offset_scale * m * gh;"),
+                                 ("gomg[2 * k + 1] = (double)offset_scale * m * gh;",
+                                  "gomg[2 * k + 1] = (double)offset_scale * m * gw;")],
     "grad_value_wrong_corner": [("int cc[4] = {f.w0, f.w0 + 1, f.w0, f.w0 + 1};",
                                  "int cc[4] = {f.w0, f.w0, f.w0 + 1, f.w0 + 1};")],
+    # DCNv3 softmax mode
+    "softmax_not_normalised": [("p[k] /= sum;", "p[k] /= 1.0;")],
+    "softmax_jacobian_missing_sum": [("gomg[2 * K + k] = pk[k] * (gomg[2 * K + k] - s);",
+                                      "gomg[2 * K + k] = pk[k] * gomg[2 * K + k];")],
+    "softmax_jacobian_missing_p": [("gomg[2 * K + k] = pk[k] * (gomg[2 * K + k] - s);",
+                                    "gomg[2 * K + k] = gomg[2 * K + k] - s;")],
+    "softmax_backward_slice_off_by_one": [("                        softmax_masks(omg + 2 * K, K, pk);",
+                                           "                        softmax_masks(omg + 2 * K - 1, K, pk);")],
 }
 
 
