@@ -127,15 +127,21 @@ def time_configs(path, steps, warmup):
     dev = torch.device("cuda")
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     lines = []
-    for name, w in WORKLOADS.items():
+    # (label, workload, direction, softmax): every workload in its own
+    # direction, plus the DCNv3 softmax mode on the fp32 benchmark shape
+    cases = [(name, w, w.direction, False) for name, w in WORKLOADS.items()]
+    c2 = WORKLOADS["c2_fwd_fp32_56x56_b64"]
+    cases += [("c2_softmax_fwd_fp32_56x56_b64", c2, "fwd", True),
+              ("c2_softmax_bwd_fp32_56x56_b64", c2, "bwd", True)]
+    for name, w, direction, softmax in cases:
         sets, _ = make_sets(w, 1, dev)
         s = sets[0]
-        kw = w.kwargs()
-        if w.direction == "fwd":
-            call = lambda: dcnv4.dcnv4_forward(s["v"], s["om"], s["out"], **kw)  # noqa: E731
+        kw = dict(w.kwargs(), softmax=softmax)
+        if direction == "fwd":
+            call = lambda: dcnv4.dcnv4_forward_ex(s["v"], s["om"], s["out"], **kw)  # noqa: E731
             nbytes = w.fwd_bytes()
         else:
-            call = lambda: dcnv4.dcnv4_backward(s["v"], s["om"], s["g"], s["gv"], s["gom"], **kw)  # noqa: E731
+            call = lambda: dcnv4.dcnv4_backward_ex(s["v"], s["om"], s["g"], s["gv"], s["gom"], **kw)  # noqa: E731
             nbytes = w.bwd_bytes()
         times = []
         for i in range(warmup + steps):
@@ -148,7 +154,7 @@ def time_configs(path, steps, warmup):
             if i >= warmup:
                 times.append(e0.elapsed_time(e1))
         ms = statistics.median(times)
-        line = {"workload": name, "direction": w.direction, "dtype": w.dtype, "ms": ms,
+        line = {"workload": name, "direction": direction, "softmax": softmax, "dtype": w.dtype, "ms": ms,
                 "points_per_s": w.points / (ms * 1e-3), "compulsory_bytes": nbytes,
                 "gbps": nbytes / (ms * 1e-3) / 1e9,
                 "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}

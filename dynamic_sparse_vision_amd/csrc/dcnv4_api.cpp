@@ -117,6 +117,7 @@ int describe(int N, int H, int W, int kh, int kw, int sh, int sw, int ph, int pw
     p->dtype = dtype;
     p->elem = es;
     p->offset_scale = offset_scale;
+    p->softmax = 0;
     return DCNV4_OK;
 }
 
@@ -223,6 +224,13 @@ int staged_om_dwords(const Problem &p, int elem)
     return elem == 4 ? 3 * p.K : (3 * p.K + 2) / 2;
 }
 
+// LDS dwords per pixel of the backward's offset/mask rows: the staged
+// entries, plus K for the softmax probabilities in softmax mode.
+int backward_om_dwords(const Problem &p)
+{
+    return 3 * p.K + (p.softmax ? p.K : 0);
+}
+
 int region_rows(const Problem &p, int th, int R)
 {
     return (th - 1) * p.sh + (p.kh - 1) * p.dh + 2 * R + 2;
@@ -310,19 +318,19 @@ bool choose_cell_tile(const Problem &p, int R, int src_cap, int gps, int *ch, in
 }
 
 // Fill the LDS geometry for halo radius R; returns total LDS bytes.
-int tile_lds(const Problem &p, TilePlan *tp, int R, int elem)
+int tile_lds(const Problem &p, TilePlan *tp, int R, int om_dw)
 {
     tp->R = R;
     tp->rh = region_rows(p, tp->th, R);
     tp->rw = region_cols(p, tp->tw, R);
-    tp->om_dw = staged_om_dwords(p, elem);
+    tp->om_dw = om_dw;
     const int om = tp->th * tp->tw * tp->om_dw * 4;
     tp->om_lds_bytes = (om + 15) / 16 * 16;
     tp->lds_bytes = tp->om_lds_bytes + tp->rh * tp->rw * tp->ps * 16;
     return tp->lds_bytes;
 }
 
-int plan_tiled_common(const Problem &p, int elem, int r_max, int lds_budget, TilePlan *tp)
+int plan_tiled_common(const Problem &p, int elem, int om_dw, int r_max, int lds_budget, TilePlan *tp)
 {
     if ((p.Cg * elem) % 16 != 0 || p.K > kMaxTiledK)
         return DCNV4_ERR_UNSUPPORTED;
@@ -346,12 +354,11 @@ int plan_tiled_common(const Problem &p, int elem, int r_max, int lds_budget, Til
     tp->lanes = p.Cg / dp;
     if (!pow2(tp->lanes) || tp->lanes > 64)
         return DCNV4_ERR_UNSUPPORTED;
-    const int om_dw = staged_om_dwords(p, elem);
     // the largest halo radius that has a tile within the LDS budget
     for (int R = r_max; R >= 1; --R) {
         if (!choose_out_tile(p, tp->lanes, dp, tp->ps, om_dw, R, lds_budget, elem, &tp->th, &tp->tw))
             continue;
-        tile_lds(p, tp, R, elem);
+        tile_lds(p, tp, R, om_dw);
         // whole waves: the staging loops take rows per wave
         tp->threads = (tp->th * tp->tw * tp->lanes + 63) / 64 * 64;
         tp->tiles_y = (p.Ho + tp->th - 1) / tp->th;
@@ -367,7 +374,7 @@ int plan_tiled_common(const Problem &p, int elem, int r_max, int lds_budget, Til
 int plan_forward_tiled(const Problem &p, TilePlan *tp)
 {
     *tp = TilePlan{};
-    const int st = plan_tiled_common(p, p.elem, 5, kTiledMaxLds, tp);
+    const int st = plan_tiled_common(p, p.elem, staged_om_dwords(p, p.elem), 5, kTiledMaxLds, tp);
     if (st != DCNV4_OK)
         return st;
     tp->images_per_launch = (int)(kMaxBytesPerLaunch / image_bytes_max(p, false));
@@ -381,7 +388,7 @@ int plan_backward_tiled(const Problem &p, TilePlan *tp)
         return DCNV4_ERR_UNSUPPORTED;
     if (p.Cg != 4 && p.Cg != 8 && p.Cg != 16 && p.Cg != 32)
         return DCNV4_ERR_UNSUPPORTED;
-    int st = plan_tiled_common(p, 4, 5, kTiledMaxLds, tp);
+    int st = plan_tiled_common(p, 4, backward_om_dwords(p), 5, kTiledMaxLds, tp);
     if (st != DCNV4_OK)
         return st;
     // cell tiles for grad_value: LDS holds the bins, up to src_cap*K sorted
@@ -483,21 +490,26 @@ int dcnv4_om_channels(int group, int kernel_h, int kernel_w, int remove_center)
     return (int)P;
 }
 
-int dcnv4_forward(const void *value, const void *offset_mask, void *output, int N, int H, int W, int kernel_h,
-                  int kernel_w, int stride_h, int stride_w, int pad_h, int pad_w, int dilation_h, int dilation_w,
-                  int group, int group_channels, float offset_scale, int remove_center, int om_channels, int dtype,
-                  void *stream)
+int dcnv4_forward_ex(const void *value, const void *offset_mask, void *output, int N, int H, int W, int kernel_h,
+                     int kernel_w, int stride_h, int stride_w, int pad_h, int pad_w, int dilation_h, int dilation_w,
+                     int group, int group_channels, float offset_scale, int remove_center, int om_channels,
+                     int softmax, int dtype, void *stream)
 {
     g_last_hip_error[0] = '\0';
+    if (softmax != 0 && softmax != 1)
+        return DCNV4_ERR_PARAM;
     Problem p;
     int st = describe(N, H, W, kernel_h, kernel_w, stride_h, stride_w, pad_h, pad_w, dilation_h, dilation_w, group,
                       group_channels, offset_scale, remove_center, om_channels, dtype, &p);
     if (st != DCNV4_OK)
         return st;
+    p.softmax = softmax;
     Plan plan;
     TilePlan tp;
     const bool tiled = plan_forward_tiled(p, &tp) == DCNV4_OK;
     st = plan_forward(p, &plan);
+    if (softmax && !tiled)
+        return DCNV4_ERR_UNSUPPORTED;   // the softmax mode exists in the tiled kernels only
     if (st != DCNV4_OK && !tiled)
         return st;
     if (N == 0)
@@ -527,22 +539,37 @@ int dcnv4_forward(const void *value, const void *offset_mask, void *output, int 
     return DCNV4_OK;
 }
 
-int dcnv4_backward(const void *value, const void *offset_mask, const void *grad_output, void *grad_value,
-                   void *grad_offset_mask, int N, int H, int W, int kernel_h, int kernel_w, int stride_h,
-                   int stride_w, int pad_h, int pad_w, int dilation_h, int dilation_w, int group,
-                   int group_channels, float offset_scale, int remove_center, int om_channels, int dtype,
-                   void *stream)
+int dcnv4_forward(const void *value, const void *offset_mask, void *output, int N, int H, int W, int kernel_h,
+                  int kernel_w, int stride_h, int stride_w, int pad_h, int pad_w, int dilation_h, int dilation_w,
+                  int group, int group_channels, float offset_scale, int remove_center, int om_channels, int dtype,
+                  void *stream)
+{
+    return dcnv4_forward_ex(value, offset_mask, output, N, H, W, kernel_h, kernel_w, stride_h, stride_w, pad_h, pad_w,
+                            dilation_h, dilation_w, group, group_channels, offset_scale, remove_center, om_channels, 0,
+                            dtype, stream);
+}
+
+int dcnv4_backward_ex(const void *value, const void *offset_mask, const void *grad_output, void *grad_value,
+                      void *grad_offset_mask, int N, int H, int W, int kernel_h, int kernel_w, int stride_h,
+                      int stride_w, int pad_h, int pad_w, int dilation_h, int dilation_w, int group,
+                      int group_channels, float offset_scale, int remove_center, int om_channels, int softmax,
+                      int dtype, void *stream)
 {
     g_last_hip_error[0] = '\0';
+    if (softmax != 0 && softmax != 1)
+        return DCNV4_ERR_PARAM;
     Problem p;
     int st = describe(N, H, W, kernel_h, kernel_w, stride_h, stride_w, pad_h, pad_w, dilation_h, dilation_w, group,
                       group_channels, offset_scale, remove_center, om_channels, dtype, &p);
     if (st != DCNV4_OK)
         return st;
+    p.softmax = softmax;
     Plan plan;
     TilePlan tp;
     const bool tiled = plan_backward_tiled(p, &tp) == DCNV4_OK;
     st = plan_backward(p, &plan);
+    if (softmax && !tiled)
+        return DCNV4_ERR_UNSUPPORTED;   // the softmax mode exists in the tiled kernels only
     if (st != DCNV4_OK && !tiled)
         return st;
     if (N == 0)
@@ -579,6 +606,17 @@ int dcnv4_backward(const void *value, const void *offset_mask, const void *grad_
             return hip_status(e);
     }
     return DCNV4_OK;
+}
+
+int dcnv4_backward(const void *value, const void *offset_mask, const void *grad_output, void *grad_value,
+                   void *grad_offset_mask, int N, int H, int W, int kernel_h, int kernel_w, int stride_h,
+                   int stride_w, int pad_h, int pad_w, int dilation_h, int dilation_w, int group,
+                   int group_channels, float offset_scale, int remove_center, int om_channels, int dtype,
+                   void *stream)
+{
+    return dcnv4_backward_ex(value, offset_mask, grad_output, grad_value, grad_offset_mask, N, H, W, kernel_h,
+                             kernel_w, stride_h, stride_w, pad_h, pad_w, dilation_h, dilation_w, group,
+                             group_channels, offset_scale, remove_center, om_channels, 0, dtype, stream);
 }
 
 }  // extern "C"

@@ -21,6 +21,7 @@ struct Problem {
     int kh, kw, sh, sw, ph, pw, dh, dw;
     int G, Cg, C, K, P;
     int remove_center;
+    int softmax;       // 1: masks are logits normalised over the K points
     int dtype;         // enum dcnv4_dtype
     int elem;          // bytes per element of the storage dtype
     float offset_scale;
@@ -51,7 +52,8 @@ struct TilePlan {
     int rh, rw;          // LDS value region, pixels
     int nvp;             // 16-byte vectors per region pixel (Cg * elem / 16)
     int ps;              // LDS pixel stride, 16-byte slots (nvp rounded up to odd)
-    int om_dw;           // staged dwords per pixel: one group's 3K entries, dword-aligned
+    int om_dw;           // LDS dwords per pixel of the offset/mask rows (staged entries, + K
+                         // softmax probabilities in the backward's softmax mode)
     int om_lds_bytes;    // LDS for the staged offset/mask entries (16-byte multiple)
     int lds_bytes;       // total LDS of an output-tile block
     // cell tiles (backward grad_value): ch x cw input cells of one (image, group)

@@ -314,9 +314,23 @@ __device__ __forceinline__ void far_corner_loads(__amdgpu_buffer_rsrc_t vr, unsi
     }
 }
 
+// Softmax statistics of the K mask logits m[stride*k] of one (pixel, group):
+// the maximum and 1 / sum_k exp(m_k - max).
+template <typename T>
+__device__ __forceinline__ void softmax_stats(const T *m, int K, float &mx, float &inv)
+{
+    mx = Store<T>::scalar(m[0]);
+    for (int k = 1; k < K; ++k)
+        mx = fmaxf(mx, Store<T>::scalar(m[k]));
+    float sum = 0.0f;
+    for (int k = 0; k < K; ++k)
+        sum += expf(Store<T>::scalar(m[k]) - mx);
+    inv = 1.0f / sum;
+}
+
 // ---- forward ---------------------------------------------------------------
 
-template <typename T, int DP>
+template <typename T, int DP, bool SM>
 __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_fwd_tiled(TArgs a)
 {
     extern __shared__ u32x4 smem[];
@@ -341,6 +355,9 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_fwd_tiled(TArgs a)
     const T *om = reinterpret_cast<const T *>(om_s + q * a.om_dw * 4) + ((t.g * 3 * a.K) & (epd - 1));
     const NearFrame nf = near_frame(a, t, oy, ox);
     const char *vb = val_s + chunk * NV * 16;
+    float smx = 0.0f, sinv = 1.0f;
+    if (SM)
+        softmax_stats(om + 2 * a.K, a.K, smx, sinv);
 
     float acc[DP];
 #pragma unroll
@@ -363,7 +380,9 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_fwd_tiled(TArgs a)
         grid_point(geo, k, gi, gj);
         const float dx = Store<T>::scalar(om[2 * k]);
         const float dy = Store<T>::scalar(om[2 * k + 1]);
-        const float m = Store<T>::scalar(om[2 * a.K + k]);
+        float m = Store<T>::scalar(om[2 * a.K + k]);
+        if (SM)
+            m = expf(m - smx) * sinv;
         const float bh = nf.bh0 + (float)(gj * geo.dh), bw = nf.bw0 + (float)(gi * geo.dw);
         const NearSample s = near_sample(nf, geo.scale, bh, bw, dx, dy);
         if (!s.nr && live_loc(geo, s.lh, s.lw)) {
@@ -420,7 +439,9 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_fwd_tiled(TArgs a)
         }
         const float dx = Store<T>::scalar(om[2 * k]);
         const float dy = Store<T>::scalar(om[2 * k + 1]);
-        const float m = Store<T>::scalar(om[2 * a.K + k]);
+        float m = Store<T>::scalar(om[2 * a.K + k]);
+        if (SM)
+            m = expf(m - smx) * sinv;
         const Loc l = locate_lane(a, oy, ox, k, dx, dy);
         const Footprint f = footprint(geo, l);
         float w00, w01, w10, w11;
@@ -462,7 +483,7 @@ __device__ __forceinline__ void sample_grads(float ah, float aw, float t00, floa
     gh = hw * (t10 - t00) + aw * (t11 - t01);
 }
 
-template <int DP>
+template <int DP, bool SM>
 __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs a)
 {
     extern __shared__ u32x4 smem[];
@@ -492,6 +513,11 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
     const char *vb = val_s + chunk * NV * 16;
     const unsigned pix_off = ((unsigned)((t.n * geo.Ho + oy) * geo.Wo + ox)) * cs + (unsigned)chan_off;
     const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
+    // softmax mode: probabilities p_k are kept at om[3K + k] (the rows have
+    // K spare dwords) until the logit gradients are formed at the end
+    float smx = 0.0f, sinv = 1.0f;
+    if (SM)
+        softmax_stats(om + 2 * a.K, a.K, smx, sinv);
 
     float go[DP];
     {
@@ -518,7 +544,13 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
     for (int k = 0; k < a.K; ++k) {
         int gi, gj;
         grid_point(geo, k, gi, gj);
-        const float dx = om[2 * k], dy = om[2 * k + 1], m = om[2 * a.K + k];
+        const float dx = om[2 * k], dy = om[2 * k + 1];
+        float m = om[2 * a.K + k];
+        if (SM) {
+            m = expf(m - smx) * sinv;
+            if (valid && chunk == 0)
+                om[K3 + k] = m;
+        }
         const float bh = nf.bh0 + (float)(gj * geo.dh), bw = nf.bw0 + (float)(gi * geo.dw);
         const NearSample s = near_sample(nf, geo.scale, bh, bw, dx, dy);
         const bool nr = s.nr && valid;
@@ -601,7 +633,7 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
                     farbits &= farbits - 1;
                 }
                 const float dx = om[2 * k], dy = om[2 * k + 1];
-                m = om[2 * a.K + k];
+                m = SM ? om[K3 + k] : om[2 * a.K + k];
                 const Loc l = locate_lane(a, oy, ox, k, dx, dy);
                 const Footprint f = footprint(geo, l);
                 off = corner_offset(geo, t.n, f, 4, chan_off);
@@ -659,6 +691,15 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
             }
         }
     }
+    if (SM && valid && chunk == 0) {
+        // gradients with respect to the logits: p_k * (g_k - sum_j p_j g_j),
+        // with g_k = dL/dp_k now at om[2K + k]
+        float sdot = 0.0f;
+        for (int k = 0; k < a.K; ++k)
+            sdot = __builtin_fmaf(om[K3 + k], om[2 * a.K + k], sdot);
+        for (int k = 0; k < a.K; ++k)
+            om[2 * a.K + k] = om[K3 + k] * (om[2 * a.K + k] - sdot);
+    }
     __syncthreads();
 
     // write the group's gradient rows of the tile back, slot for slot as they
@@ -670,16 +711,25 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
         const int row0 = t.n * geo.Ho + t.oy0;
         const int rows = min(a.th, geo.Ho - t.oy0);
         {
+            // slot j of a row: entry j % 3K of tile column j / 3K, at LDS dword
+            // (j / 3K) * om_dw + j % 3K of the row
             unsigned lo[kMaxRowChunks];
-            pixel_row_offsets(a, t, a.om_dw, a.om_dw_magic, (unsigned)(a.P * 4), (unsigned)(t.g * K3 * 4), lo);
-            const int row_slots = a.tw * a.om_dw;
+            int li[kMaxRowChunks];
+            pixel_row_offsets(a, t, K3, a.k3_magic, (unsigned)(a.P * 4), (unsigned)(t.g * K3 * 4), lo);
+#pragma unroll
+            for (int c = 0; c < kMaxRowChunks; ++c) {
+                const int j = c * 64 + lane;
+                const int px2 = (int)divm((unsigned)j, a.k3_magic);
+                li[c] = px2 * a.om_dw + (j - px2 * K3);
+            }
+            const int row_slots = a.tw * K3;
             for (int rr = wave; rr < rows; rr += nwaves) {
                 const unsigned base = (unsigned)(row0 + rr) * row_bytes;
-                const unsigned *src = reinterpret_cast<const unsigned *>(om_s) + rr * row_slots;
+                const unsigned *src = reinterpret_cast<const unsigned *>(om_s) + rr * a.tw * a.om_dw;
 #pragma unroll
                 for (int c = 0; c < kMaxRowChunks; ++c) {
                     if (c * 64 < row_slots && c * 64 + lane < row_slots && lo[c] != kOutOfRange)
-                        __builtin_amdgcn_raw_buffer_store_b32(src[c * 64 + lane], r, base + lo[c], 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(src[li[c]], r, base + lo[c], 0, 0);
                 }
             }
         }
@@ -735,7 +785,7 @@ __device__ __forceinline__ void shifted_entries(const u32x4 (&v)[NVEC], int mis,
         out[e] = __builtin_bit_cast(float, t[e] ^ ((t[e] ^ t[e + 2]) & m2));
 }
 
-template <int CG, int KMAX>
+template <int CG, int KMAX, bool SM>
 __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
 {
     extern __shared__ u32x4 smem[];
@@ -832,6 +882,22 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
         float offs[2 * KMAX], msk[KMAX];
         shifted_entries(vov, mis_o, offs);
         shifted_entries(vmv, mis_m, msk);
+        if (SM) {
+            float mx = msk[0];
+#pragma unroll
+            for (int k = 1; k < KMAX; ++k)
+                mx = k < a.K ? fmaxf(mx, msk[k]) : mx;
+            float sum = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                msk[k] = k < a.K ? expf(msk[k] - mx) : 0.0f;
+                sum += msk[k];
+            }
+            const float inv = 1.0f / sum;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k)
+                msk[k] *= inv;
+        }
         const float bh0 = (float)(oy * geo.sh - geo.ph), bw0 = (float)(ox * geo.sw - geo.pw);
         unsigned slot[KMAX];
         float fa[KMAX], fb[KMAX];
@@ -1022,6 +1088,7 @@ bool out_tiles_ok(const Problem &p, const TilePlan &tp)
 {
     return tp.threads % 64 == 0 && tp.threads <= kMaxTileThreads && tp.threads >= tp.th * tp.tw * tp.lanes &&
            tp.rw * tp.ps <= 64 * kMaxRowChunks && tp.tw * tp.om_dw <= 64 * kMaxRowChunks && p.K <= 32 &&
+           tp.om_dw >= 3 * p.K * p.elem / 4 &&
            tp.ps >= tp.nvp && tp.om_lds_bytes % 16 == 0;
 }
 
@@ -1043,10 +1110,11 @@ hipError_t launch_forward_tiled(const Problem &p, const TilePlan &tp, const void
     const dim3 grid(blocks), block(tp.threads);
 #define DCNV4_FWD(T, D)                                                                              \
     do {                                                                                             \
-        const hipError_t e_ = allow_lds(reinterpret_cast<const void *>(&dcnv4_fwd_tiled<T, D>), tp.lds_bytes); \
+        void (*k_)(TArgs) = p.softmax ? dcnv4_fwd_tiled<T, D, true> : dcnv4_fwd_tiled<T, D, false>;  \
+        const hipError_t e_ = allow_lds(reinterpret_cast<const void *>(k_), tp.lds_bytes);           \
         if (e_ != hipSuccess)                                                                        \
             return e_;                                                                               \
-        hipLaunchKernelGGL((dcnv4_fwd_tiled<T, D>), grid, block, tp.lds_bytes, stream, a);           \
+        hipLaunchKernelGGL(k_, grid, block, tp.lds_bytes, stream, a);                                \
     } while (0)
     if (p.dtype == 0) {
         if (tp.dp == 16)
@@ -1102,23 +1170,27 @@ hipError_t launch_backward_tiled(const Problem &p, const TilePlan &tp, const voi
         const int blocks = p.N * tp.ctiles_y * tp.ctiles_x * p.G;
         const dim3 grid(blocks), block(256);
         void (*kern)(TArgs) = nullptr;
-        const bool small_k = p.K <= 9;
+        const bool small_k = p.K <= 9, sm = p.softmax != 0;
+#define DCNV4_VALUES(CG)                                                                     \
+    kern = small_k ? (sm ? dcnv4_bwd_values_tiled<CG, 9, true> : dcnv4_bwd_values_tiled<CG, 9, false>) \
+                   : (sm ? dcnv4_bwd_values_tiled<CG, 25, true> : dcnv4_bwd_values_tiled<CG, 25, false>)
         switch (p.Cg) {
         case 4:
-            kern = small_k ? dcnv4_bwd_values_tiled<4, 9> : dcnv4_bwd_values_tiled<4, 25>;
+            DCNV4_VALUES(4);
             break;
         case 8:
-            kern = small_k ? dcnv4_bwd_values_tiled<8, 9> : dcnv4_bwd_values_tiled<8, 25>;
+            DCNV4_VALUES(8);
             break;
         case 16:
-            kern = small_k ? dcnv4_bwd_values_tiled<16, 9> : dcnv4_bwd_values_tiled<16, 25>;
+            DCNV4_VALUES(16);
             break;
         case 32:
-            kern = small_k ? dcnv4_bwd_values_tiled<32, 9> : dcnv4_bwd_values_tiled<32, 25>;
+            DCNV4_VALUES(32);
             break;
         default:
             return hipErrorInvalidValue;
         }
+#undef DCNV4_VALUES
         hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), tp.splat_lds_bytes);
         if (e != hipSuccess)
             return e;
@@ -1132,15 +1204,16 @@ hipError_t launch_backward_tiled(const Problem &p, const TilePlan &tp, const voi
         const int blocks = p.N * tp.tiles_y * tp.tiles_x * p.G;
         const dim3 grid(blocks), block(tp.threads);
         void (*kern)(TArgs) = nullptr;
+        const bool sm = p.softmax != 0;
         switch (tp.dp) {
         case 16:
-            kern = dcnv4_bwd_offsets_tiled<16>;
+            kern = sm ? dcnv4_bwd_offsets_tiled<16, true> : dcnv4_bwd_offsets_tiled<16, false>;
             break;
         case 8:
-            kern = dcnv4_bwd_offsets_tiled<8>;
+            kern = sm ? dcnv4_bwd_offsets_tiled<8, true> : dcnv4_bwd_offsets_tiled<8, false>;
             break;
         case 4:
-            kern = dcnv4_bwd_offsets_tiled<4>;
+            kern = sm ? dcnv4_bwd_offsets_tiled<4, true> : dcnv4_bwd_offsets_tiled<4, false>;
             break;
         default:
             return hipErrorInvalidValue;

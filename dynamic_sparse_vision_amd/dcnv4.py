@@ -44,10 +44,15 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     i, f, p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
     geo = [i] * 13 + [f, i, i, i, p]  # N H W kh kw sh sw ph pw dh dw G Cg | scale | rc P dtype | stream
+    geo_ex = geo[:-2] + [i, i, p]  # ... rc P softmax dtype | stream
     lib.dcnv4_forward.argtypes = [p, p, p] + geo
     lib.dcnv4_forward.restype = i
     lib.dcnv4_backward.argtypes = [p, p, p, p, p] + geo
     lib.dcnv4_backward.restype = i
+    lib.dcnv4_forward_ex.argtypes = [p, p, p] + geo_ex
+    lib.dcnv4_forward_ex.restype = i
+    lib.dcnv4_backward_ex.argtypes = [p, p, p, p, p] + geo_ex
+    lib.dcnv4_backward_ex.restype = i
     lib.dcnv4_output_size.argtypes = [i] * 10 + [ctypes.POINTER(i), ctypes.POINTER(i)]
     lib.dcnv4_output_size.restype = i
     lib.dcnv4_om_channels.argtypes = [i, i, i, i]
@@ -120,18 +125,34 @@ def dcnv4_forward(value, offset_mask, output, *, kernel_h=3, kernel_w=3, stride_
     """value (N,H,W,C), offset_mask (N,Ho,Wo,P), output (N,Ho,Wo,C): device
     tensors of one dtype.  Enqueues the forward on ``stream`` (default: torch's
     current stream)."""
+    dcnv4_forward_ex(value, offset_mask, output, kernel_h=kernel_h, kernel_w=kernel_w,
+                     stride_h=stride_h, stride_w=stride_w, pad_h=pad_h, pad_w=pad_w,
+                     dilation_h=dilation_h, dilation_w=dilation_w, group=group,
+                     group_channels=group_channels, offset_scale=offset_scale,
+                     remove_center=remove_center, softmax=False, stream=stream, _name="dcnv4_forward")
+
+
+def dcnv4_forward_ex(value, offset_mask, output, *, kernel_h=3, kernel_w=3, stride_h=1, stride_w=1,
+                     pad_h=1, pad_w=1, dilation_h=1, dilation_w=1, group, group_channels,
+                     offset_scale=1.0, remove_center=False, softmax=False, stream=None,
+                     _name="dcnv4_forward_ex") -> None:
+    """dcnv4_forward with the DCNv3 softmax over the K masks when ``softmax``."""
     for t, nm in ((value, "value"), (offset_mask, "offset_mask"), (output, "output")):
         _check(t, nm)
         if t.dtype != value.dtype:
             raise TypeError(f"{nm} dtype {t.dtype} != value dtype {value.dtype}")
     N, H, W, C = value.shape
-    st = load().dcnv4_forward(
-        ctypes.c_void_p(value.data_ptr()), ctypes.c_void_p(offset_mask.data_ptr()),
-        ctypes.c_void_p(output.data_ptr()), N, H, W, kernel_h, kernel_w, stride_h, stride_w,
-        pad_h, pad_w, dilation_h, dilation_w, group, group_channels, float(offset_scale),
-        int(bool(remove_center)), offset_mask.shape[-1], _dtype_code(value), _stream_ptr(stream))
+    lib = load()
+    args = (ctypes.c_void_p(value.data_ptr()), ctypes.c_void_p(offset_mask.data_ptr()),
+            ctypes.c_void_p(output.data_ptr()), N, H, W, kernel_h, kernel_w, stride_h, stride_w,
+            pad_h, pad_w, dilation_h, dilation_w, group, group_channels, float(offset_scale),
+            int(bool(remove_center)), offset_mask.shape[-1])
+    if _name == "dcnv4_forward":
+        st = lib.dcnv4_forward(*args, _dtype_code(value), _stream_ptr(stream))
+    else:
+        st = lib.dcnv4_forward_ex(*args, int(bool(softmax)), _dtype_code(value), _stream_ptr(stream))
     if st != DCNV4_OK:
-        raise Dcnv4Error(st, "dcnv4_forward")
+        raise Dcnv4Error(st, _name)
 
 
 def dcnv4_backward(value, offset_mask, grad_output, grad_value, grad_offset_mask, *, kernel_h=3,
@@ -140,25 +161,43 @@ def dcnv4_backward(value, offset_mask, grad_output, grad_value, grad_offset_mask
                    stream=None) -> None:
     """Backward into caller-allocated grad_value (N,H,W,C) and
     grad_offset_mask (N,Ho,Wo,P) (both overwritten)."""
+    dcnv4_backward_ex(value, offset_mask, grad_output, grad_value, grad_offset_mask,
+                      kernel_h=kernel_h, kernel_w=kernel_w, stride_h=stride_h, stride_w=stride_w,
+                      pad_h=pad_h, pad_w=pad_w, dilation_h=dilation_h, dilation_w=dilation_w,
+                      group=group, group_channels=group_channels, offset_scale=offset_scale,
+                      remove_center=remove_center, softmax=False, stream=stream,
+                      _name="dcnv4_backward")
+
+
+def dcnv4_backward_ex(value, offset_mask, grad_output, grad_value, grad_offset_mask, *, kernel_h=3,
+                      kernel_w=3, stride_h=1, stride_w=1, pad_h=1, pad_w=1, dilation_h=1,
+                      dilation_w=1, group, group_channels, offset_scale=1.0, remove_center=False,
+                      softmax=False, stream=None, _name="dcnv4_backward_ex") -> None:
+    """dcnv4_backward with the DCNv3 softmax over the K masks when ``softmax``
+    (the mask gradient is then taken with respect to the logits)."""
     for t, nm in ((value, "value"), (offset_mask, "offset_mask"), (grad_output, "grad_output"),
                   (grad_value, "grad_value"), (grad_offset_mask, "grad_offset_mask")):
         _check(t, nm)
         if t.dtype != value.dtype:
             raise TypeError(f"{nm} dtype {t.dtype} != value dtype {value.dtype}")
     N, H, W, C = value.shape
-    st = load().dcnv4_backward(
-        ctypes.c_void_p(value.data_ptr()), ctypes.c_void_p(offset_mask.data_ptr()),
-        ctypes.c_void_p(grad_output.data_ptr()), ctypes.c_void_p(grad_value.data_ptr()),
-        ctypes.c_void_p(grad_offset_mask.data_ptr()), N, H, W, kernel_h, kernel_w, stride_h,
-        stride_w, pad_h, pad_w, dilation_h, dilation_w, group, group_channels,
-        float(offset_scale), int(bool(remove_center)), offset_mask.shape[-1],
-        _dtype_code(value), _stream_ptr(stream))
+    lib = load()
+    args = (ctypes.c_void_p(value.data_ptr()), ctypes.c_void_p(offset_mask.data_ptr()),
+            ctypes.c_void_p(grad_output.data_ptr()), ctypes.c_void_p(grad_value.data_ptr()),
+            ctypes.c_void_p(grad_offset_mask.data_ptr()), N, H, W, kernel_h, kernel_w, stride_h,
+            stride_w, pad_h, pad_w, dilation_h, dilation_w, group, group_channels,
+            float(offset_scale), int(bool(remove_center)), offset_mask.shape[-1])
+    if _name == "dcnv4_backward":
+        st = lib.dcnv4_backward(*args, _dtype_code(value), _stream_ptr(stream))
+    else:
+        st = lib.dcnv4_backward_ex(*args, int(bool(softmax)), _dtype_code(value), _stream_ptr(stream))
     if st != DCNV4_OK:
-        raise Dcnv4Error(st, "dcnv4_backward")
+        raise Dcnv4Error(st, _name)
 
 
 def forward(value, offset_mask, **params):
-    """Allocate the output with torch and call dcnv4_forward."""
+    """Allocate the output with torch and call dcnv4_forward (dcnv4_forward_ex
+    when ``softmax=True`` is among the parameters)."""
     import torch
 
     N, H, W, C = value.shape
@@ -167,15 +206,24 @@ def forward(value, offset_mask, **params):
                                params.get("pad_h", 1), params.get("pad_w", 1),
                                params.get("dilation_h", 1), params.get("dilation_w", 1))
     out = torch.empty((N, Ho, Wo, C), dtype=value.dtype, device=value.device)
-    dcnv4_forward(value, offset_mask, out, **params)
+    if params.get("softmax"):
+        dcnv4_forward_ex(value, offset_mask, out, **params)
+    else:
+        params.pop("softmax", None)
+        dcnv4_forward(value, offset_mask, out, **params)
     return out
 
 
 def backward(value, offset_mask, grad_output, **params):
-    """Allocate grad_value / grad_offset_mask with torch and call dcnv4_backward."""
+    """Allocate grad_value / grad_offset_mask with torch and call dcnv4_backward
+    (dcnv4_backward_ex when ``softmax=True`` is among the parameters)."""
     import torch
 
     gv = torch.empty_like(value)
     gom = torch.empty_like(offset_mask)
-    dcnv4_backward(value, offset_mask, grad_output, gv, gom, **params)
+    if params.get("softmax"):
+        dcnv4_backward_ex(value, offset_mask, grad_output, gv, gom, **params)
+    else:
+        params.pop("softmax", None)
+        dcnv4_backward(value, offset_mask, grad_output, gv, gom, **params)
     return gv, gom

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define DCNV4_ABI_VERSION 1
+#define DCNV4_ABI_VERSION 2
 
 enum dcnv4_status {
     DCNV4_OK = 0,
@@ -153,12 +153,14 @@ DCNV4_API int dcnv4_forward(const void *value, const void *offset_mask, void *ou
  *   value, offset_mask       as for dcnv4_forward, read
  *   grad_output      (N, Ho, Wo, group*group_channels), read
  *   grad_value       (N, H, W, group*group_channels), written (overwritten,
- *                    not accumulated: the library zero-fills it first)
+ *                    not accumulated)
  *   grad_offset_mask (N, Ho, Wo, om_channels), written; padding entries 0
  *
  * dtype: DCNV4_FP32 only (others return DCNV4_ERR_UNSUPPORTED).
- * grad_value is summed with device atomics, so its last bits may differ
- * from run to run; grad_offset_mask is deterministic.
+ * grad_offset_mask is deterministic.  grad_value is deterministic except for
+ * the contributions of samples that land more than a few pixels from their
+ * grid position, which are added with device atomics after the rest (their
+ * last bits may then differ from run to run).
  * Errors: as dcnv4_forward.
  */
 DCNV4_API int dcnv4_backward(const void *value, const void *offset_mask, const void *grad_output,
@@ -168,6 +170,34 @@ DCNV4_API int dcnv4_backward(const void *value, const void *offset_mask, const v
                    int dilation_h, int dilation_w, int group, int group_channels,
                    float offset_scale, int remove_center, int om_channels,
                    int dtype, void *stream);
+
+/*
+ * DCNv3-compatible variants (walkthrough section 1.2 recap equation with the
+ * softmax that section 2.1 removes): with softmax = 1 each (pixel, group)'s
+ * K masks are logits, and the operation uses
+ *   p_gk = exp(m_gk) / sum_j exp(m_gj)      (over all K points)
+ * in place of m_gk.  The backward's mask gradient is then taken with respect
+ * to the logits: dL/dm_gk = p_gk * (dL/dp_gk - sum_j p_gj * dL/dp_gj).
+ * softmax = 0 is exactly dcnv4_forward / dcnv4_backward.  The masks must be
+ * finite.  Arguments, layouts, ownership and errors as for the plain calls;
+ * additionally PARAM if softmax is not 0 or 1, and UNSUPPORTED for softmax =
+ * 1 with a geometry the LDS-tiled kernels do not cover (group_channels *
+ * sizeof(dtype) a power-of-two multiple of 16 bytes, K <= 25).
+ */
+DCNV4_API int dcnv4_forward_ex(const void *value, const void *offset_mask, void *output,
+                     int N, int H, int W, int kernel_h, int kernel_w,
+                     int stride_h, int stride_w, int pad_h, int pad_w,
+                     int dilation_h, int dilation_w, int group, int group_channels,
+                     float offset_scale, int remove_center, int om_channels,
+                     int softmax, int dtype, void *stream);
+
+DCNV4_API int dcnv4_backward_ex(const void *value, const void *offset_mask, const void *grad_output,
+                      void *grad_value, void *grad_offset_mask,
+                      int N, int H, int W, int kernel_h, int kernel_w,
+                      int stride_h, int stride_w, int pad_h, int pad_w,
+                      int dilation_h, int dilation_w, int group, int group_channels,
+                      float offset_scale, int remove_center, int om_channels,
+                      int softmax, int dtype, void *stream);
 
 #ifdef __cplusplus
 }

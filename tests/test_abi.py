@@ -29,7 +29,8 @@ def declared_symbols():
 def test_header_declares_the_abi():
     assert declared_symbols() == sorted([
         "dcnv4_abi_version", "dcnv4_status_string", "dcnv4_last_hip_error",
-        "dcnv4_output_size", "dcnv4_om_channels", "dcnv4_forward", "dcnv4_backward"])
+        "dcnv4_output_size", "dcnv4_om_channels", "dcnv4_forward", "dcnv4_backward",
+        "dcnv4_forward_ex", "dcnv4_backward_ex"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -46,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = dcnv4.load()
-    assert lib.dcnv4_abi_version() == 1
+    assert lib.dcnv4_abi_version() == 2
     for st in (OK, NULL, SHAPE, PARAM, DTYPE, ALIGN, UNSUP, OVERFLOW, HIP):
         assert lib.dcnv4_status_string(st)
     assert lib.dcnv4_status_string(12345) == b"unknown status"
@@ -100,7 +101,24 @@ def bwd(ptrs=(A, B, Cp, D, E), **over):
                                        a["Cg"], a["scale"], a["rc"], a["P"], a["dtype"], None)
 
 
-@pytest.mark.parametrize("call", [fwd, bwd], ids=["forward", "backward"])
+def fwd_ex(ptrs=(A, B, Cp), softmax=1, **over):
+    a = dict(BASE, **over)
+    return dcnv4.load().dcnv4_forward_ex(*ptrs, a["N"], a["H"], a["W"], a["kh"], a["kw"], a["sh"],
+                                         a["sw"], a["ph"], a["pw"], a["dh"], a["dw"], a["G"],
+                                         a["Cg"], a["scale"], a["rc"], a["P"], softmax, a["dtype"],
+                                         None)
+
+
+def bwd_ex(ptrs=(A, B, Cp, D, E), softmax=1, **over):
+    a = dict(BASE, **over)
+    return dcnv4.load().dcnv4_backward_ex(*ptrs, a["N"], a["H"], a["W"], a["kh"], a["kw"],
+                                          a["sh"], a["sw"], a["ph"], a["pw"], a["dh"], a["dw"],
+                                          a["G"], a["Cg"], a["scale"], a["rc"], a["P"], softmax,
+                                          a["dtype"], None)
+
+
+@pytest.mark.parametrize("call", [fwd, bwd, fwd_ex, bwd_ex],
+                         ids=["forward", "backward", "forward_ex", "backward_ex"])
 @pytest.mark.parametrize("over,expect", [
     (dict(dtype=3), DTYPE),
     (dict(dtype=-1), DTYPE),
@@ -151,6 +169,18 @@ def test_backward_pointer_and_dtype_checks():
     assert bwd(ptrs=(A, B, Cp, D, ctypes.c_void_p(0x400000010))) == PARAM  # grad outputs overlap
     assert bwd(Cg=12) == UNSUP        # 3 lanes of 4 channels: not a power of two
     assert bwd(N=0, ptrs=(None,) * 5) == OK
+
+
+def test_softmax_flag_checks():
+    for call in (fwd_ex, bwd_ex):
+        assert call(softmax=2) == PARAM
+        assert call(softmax=-1) == PARAM
+        assert call(softmax=1, N=0, ptrs=(None,) * (3 if call is fwd_ex else 5)) == OK
+        # K = 49 > 25: only the general kernels could take it, and they have
+        # no softmax mode
+        assert call(softmax=1, kh=7, kw=7, ph=3, pw=3, P=592) == UNSUP
+    assert bwd_ex(softmax=1, dtype=1) == UNSUP
+    assert bwd_ex(softmax=0, dtype=2) == UNSUP
 
 
 def test_binding_refuses_host_tensors():
