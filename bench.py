@@ -73,7 +73,7 @@ def make_sets(w, nsets, dev):
     for i in range(nsets):
         s = {k: (t if i == 0 else t.clone()) for k, t in base.items()}
         s["out"] = torch.empty((w.N, w.Ho, w.Wo, w.C), dtype=s["v"].dtype, device=dev)
-        s["gv"] = torch.empty_like(s["v"])
+        s["gv"] = torch.empty(s["v"].shape, dtype=torch.float32, device=dev)   # fp32 for every dtype
         s["gom"] = torch.empty_like(s["om"])
         sets.append(s)
     return sets, (v32, om32, g32)
@@ -81,12 +81,12 @@ def make_sets(w, nsets, dev):
 
 def set_bytes_of(w):
     """Bytes of one buffer set: value, offset_mask, grad_output, output,
-    grad_value, grad_offset_mask (gradients fp32)."""
+    grad_offset_mask in the storage dtype, grad_value in fp32."""
     es = w.elem_bytes
     nv = w.N * w.H * w.W * w.C
     nom = w.N * w.Ho * w.Wo * w.P
     no = w.N * w.Ho * w.Wo * w.C
-    return es * (nv + nom + 2 * no) + 4 * (nv + nom)
+    return es * (nv + 2 * nom + 2 * no) + 4 * nv
 
 
 def cpu_baseline(w, arrays, seconds):
@@ -128,11 +128,14 @@ def time_configs(path, steps, warmup):
     flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     lines = []
     # (label, workload, direction, softmax): every workload in its own
-    # direction, plus the DCNv3 softmax mode on the fp32 benchmark shape
+    # direction, plus the DCNv3 softmax mode on the fp32 benchmark shape and
+    # the 16-bit backward
     cases = [(name, w, w.direction, False) for name, w in WORKLOADS.items()]
     c2 = WORKLOADS["c2_fwd_fp32_56x56_b64"]
     cases += [("c2_softmax_fwd_fp32_56x56_b64", c2, "fwd", True),
-              ("c2_softmax_bwd_fp32_56x56_b64", c2, "bwd", True)]
+              ("c2_softmax_bwd_fp32_56x56_b64", c2, "bwd", True),
+              ("c3a_bwd_fp16_56x56x64_g4", WORKLOADS["c3a_fwd_fp16_56x56x64_g4"], "bwd", False),
+              ("c4_bwd_bf16_270x480_k9", WORKLOADS["c4_fwd_bf16_270x480_k9"], "bwd", False)]
     for name, w, direction, softmax in cases:
         sets, _ = make_sets(w, 1, dev)
         s = sets[0]

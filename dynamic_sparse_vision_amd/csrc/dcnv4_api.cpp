@@ -225,10 +225,10 @@ int staged_om_dwords(const Problem &p, int elem)
 }
 
 // LDS dwords per pixel of the backward's offset/mask rows: the staged
-// entries, plus K for the softmax probabilities in softmax mode.
+// entries, plus 2K in softmax mode (fp32 probabilities and their gradients).
 int backward_om_dwords(const Problem &p)
 {
-    return 3 * p.K + (p.softmax ? p.K : 0);
+    return staged_om_dwords(p, p.elem) + (p.softmax ? 2 * p.K : 0);
 }
 
 int region_rows(const Problem &p, int th, int R)
@@ -242,16 +242,17 @@ int region_cols(const Problem &p, int tw, int R)
 }
 
 // Output tile for halo radius R: th x tw pixels with `lanes` threads per
-// pixel, at most kTileThreads threads, staged rows within the row limit.
+// pixel, at most kTileThreads threads, staged rows (om_dw dwords per pixel)
+// and written-back rows (row_elems entries per pixel) within the row limit.
 // Modelled time: per block, a lane-sample costs ~40 instructions plus one
 // FMA per channel and corner, a staged region slot ~8; blocks run
 // concurrently until 24 waves share a CU (fewer when LDS limits them).
-bool choose_out_tile(const Problem &p, int lanes, int dp, int ps, int om_dw, int R, int lds_budget, int elem,
+bool choose_out_tile(const Problem &p, int lanes, int dp, int ps, int om_dw, int R, int lds_budget, int row_elems,
                      int *th, int *tw)
 {
     double best = -1;
     for (int w = 1; w <= 64 && w <= p.Wo; ++w) {
-        if (w * om_dw > kRowSlots || region_cols(p, w, R) * ps > kRowSlots)
+        if (w * om_dw > kRowSlots || w * row_elems > kRowSlots || region_cols(p, w, R) * ps > kRowSlots)
             break;
         for (int h = 1; h <= 64 && h <= p.Ho; ++h) {
             const int threads = h * w * lanes;
@@ -330,7 +331,7 @@ int tile_lds(const Problem &p, TilePlan *tp, int R, int om_dw)
     return tp->lds_bytes;
 }
 
-int plan_tiled_common(const Problem &p, int elem, int om_dw, int r_max, int lds_budget, TilePlan *tp)
+int plan_tiled_common(const Problem &p, int elem, int om_dw, int row_elems, int r_max, int lds_budget, TilePlan *tp)
 {
     if ((p.Cg * elem) % 16 != 0 || p.K > kMaxTiledK)
         return DCNV4_ERR_UNSUPPORTED;
@@ -356,7 +357,7 @@ int plan_tiled_common(const Problem &p, int elem, int om_dw, int r_max, int lds_
         return DCNV4_ERR_UNSUPPORTED;
     // the largest halo radius that has a tile within the LDS budget
     for (int R = r_max; R >= 1; --R) {
-        if (!choose_out_tile(p, tp->lanes, dp, tp->ps, om_dw, R, lds_budget, elem, &tp->th, &tp->tw))
+        if (!choose_out_tile(p, tp->lanes, dp, tp->ps, om_dw, R, lds_budget, row_elems, &tp->th, &tp->tw))
             continue;
         tile_lds(p, tp, R, om_dw);
         // whole waves: the staging loops take rows per wave
@@ -374,7 +375,7 @@ int plan_tiled_common(const Problem &p, int elem, int om_dw, int r_max, int lds_
 int plan_forward_tiled(const Problem &p, TilePlan *tp)
 {
     *tp = TilePlan{};
-    const int st = plan_tiled_common(p, p.elem, staged_om_dwords(p, p.elem), 5, kTiledMaxLds, tp);
+    const int st = plan_tiled_common(p, p.elem, staged_om_dwords(p, p.elem), 0, 5, kTiledMaxLds, tp);
     if (st != DCNV4_OK)
         return st;
     tp->images_per_launch = (int)(kMaxBytesPerLaunch / image_bytes_max(p, false));
@@ -384,16 +385,17 @@ int plan_forward_tiled(const Problem &p, TilePlan *tp)
 int plan_backward_tiled(const Problem &p, TilePlan *tp)
 {
     *tp = TilePlan{};
-    if (p.dtype != DCNV4_FP32)
+    // grad_value cell tiles are instantiated for these channel counts
+    const bool cg_ok = p.Cg == 8 || p.Cg == 16 || p.Cg == 32 || (p.Cg == 4 && p.elem == 4);
+    if (!cg_ok)
         return DCNV4_ERR_UNSUPPORTED;
-    if (p.Cg != 4 && p.Cg != 8 && p.Cg != 16 && p.Cg != 32)
-        return DCNV4_ERR_UNSUPPORTED;
-    int st = plan_tiled_common(p, 4, backward_om_dwords(p), 5, kTiledMaxLds, tp);
+    // the gradient write-back stores the 3K entries of a tile row slot by slot
+    int st = plan_tiled_common(p, p.elem, backward_om_dwords(p), 3 * p.K, 5, kTiledMaxLds, tp);
     if (st != DCNV4_OK)
         return st;
     // cell tiles for grad_value: LDS holds the bins, up to src_cap*K sorted
     // samples of 16 bytes and src_cap staged grad_output pixels
-    tp->gps = (p.Cg / 4) | 1;
+    tp->gps = (p.Cg * p.elem / 16) | 1;
     tp->rec_offset = kCellBinBytes;
     tp->src_cap = std::min(256, (kCellTileLds - kCellBinBytes) / (16 * (p.K + tp->gps)));
     if (tp->src_cap < 1)
@@ -579,16 +581,19 @@ int dcnv4_backward_ex(const void *value, const void *offset_mask, const void *gr
     if (!aligned16(value) || !aligned16(offset_mask) || !aligned16(grad_output) || !aligned16(grad_value) ||
         !aligned16(grad_offset_mask))
         return DCNV4_ERR_ALIGN;
-    const int64_t img_v = (int64_t)p.H * p.W * p.C * 4, img_om = (int64_t)p.Ho * p.Wo * p.P * 4,
-                  img_o = (int64_t)p.Ho * p.Wo * p.C * 4;
-    const int64_t nv = img_v * N, nom = img_om * N, no = img_o * N;
+    const int64_t es = p.elem;
+    const int64_t img_v = (int64_t)p.H * p.W * p.C * es, img_om = (int64_t)p.Ho * p.Wo * p.P * es,
+                  img_o = (int64_t)p.Ho * p.Wo * p.C * es;
+    const int64_t img_gv = (int64_t)p.H * p.W * p.C * 4;   // grad_value is fp32 for every dtype
+    const int64_t nv = img_v * N, nom = img_om * N, no = img_o * N, ngv = img_gv * N;
     const void *ins[3] = {value, offset_mask, grad_output};
     const int64_t in_sz[3] = {nv, nom, no};
     for (int i = 0; i < 3; ++i) {
-        if (ranges_overlap(grad_value, nv, ins[i], in_sz[i]) || ranges_overlap(grad_offset_mask, nom, ins[i], in_sz[i]))
+        if (ranges_overlap(grad_value, ngv, ins[i], in_sz[i]) ||
+            ranges_overlap(grad_offset_mask, nom, ins[i], in_sz[i]))
             return DCNV4_ERR_PARAM;
     }
-    if (ranges_overlap(grad_value, nv, grad_offset_mask, nom))
+    if (ranges_overlap(grad_value, ngv, grad_offset_mask, nom))
         return DCNV4_ERR_PARAM;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int per_launch = tiled ? tp.images_per_launch : plan.images_per_launch;
@@ -598,7 +603,7 @@ int dcnv4_backward_ex(const void *value, const void *offset_mask, const void *gr
         const void *v = static_cast<const char *>(value) + img_v * n0;
         const void *om = static_cast<const char *>(offset_mask) + img_om * n0;
         const void *go = static_cast<const char *>(grad_output) + img_o * n0;
-        void *gv = static_cast<char *>(grad_value) + img_v * n0;
+        void *gv = static_cast<char *>(grad_value) + img_gv * n0;
         void *gom = static_cast<char *>(grad_offset_mask) + img_om * n0;
         hipError_t e = tiled ? launch_backward_tiled(q, tp, v, om, go, gv, gom, s)
                              : launch_backward_general(q, plan, v, om, go, gv, gom, s);

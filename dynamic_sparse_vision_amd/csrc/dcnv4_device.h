@@ -8,6 +8,7 @@
 __device__ float dcnv4_buffer_atomic_fadd(float v, __amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset,
                                           int aux) __asm("llvm.amdgcn.raw.ptr.buffer.atomic.fadd.f32");
 
+
 namespace dcnv4 {
 namespace dev {
 
@@ -60,6 +61,7 @@ struct Store;
 template <>
 struct Store<float> {
     __device__ static float scalar(float v) { return v; }
+    __device__ static float make(float v) { return v; }
     __device__ static float get(const u32x4 *r, int c)
     {
         const f32x4 f = __builtin_bit_cast(f32x4, r[c >> 2]);
@@ -79,6 +81,8 @@ struct Store<float> {
 template <>
 struct Store<_Float16> {
     __device__ static float scalar(_Float16 v) { return (float)v; }
+    __device__ static _Float16 make(float v) { return (_Float16)v; }   // round to nearest even
+    __device__ static float from_bits(unsigned b) { return (float)__builtin_bit_cast(_Float16, (unsigned short)b); }
     __device__ static float get(const u32x4 *r, int c)
     {
         const f16x8 h = __builtin_bit_cast(f16x8, r[c >> 3]);
@@ -98,6 +102,8 @@ struct Store<_Float16> {
 template <>
 struct Store<bf16_t> {
     __device__ static float scalar(bf16_t v) { return __builtin_bit_cast(float, (unsigned)v.bits << 16); }
+    __device__ static bf16_t make(float v) { return bf16_t{(unsigned short)bf16_round(v)}; }
+    __device__ static float from_bits(unsigned b) { return __builtin_bit_cast(float, (b & 0xffffu) << 16); }
     __device__ static float get(const u32x4 *r, int c)
     {
         const unsigned w = r[c >> 3][(c & 7) >> 1];

@@ -86,6 +86,7 @@ struct TArgs {
     int rec_offset, gs_offset;   // LDS byte offsets of the record list and the grad_output rows
     // buffer sizes of this launch, bytes
     int value_bytes, om_bytes, out_bytes, gout_bytes;
+    int gvalue_bytes;            // grad_value is fp32 for every storage dtype
 };
 
 // e / d for the small non-negative e used here: magic = ceil(2^32 / d), or
@@ -483,20 +484,22 @@ __device__ __forceinline__ void sample_grads(float ah, float aw, float t00, floa
     gh = hw * (t10 - t00) + aw * (t11 - t01);
 }
 
-template <int DP, bool SM>
+template <typename T, int DP, bool SM>
 __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs a)
 {
     extern __shared__ u32x4 smem[];
-    constexpr int NV = DP / 4;
+    constexpr int es = (int)sizeof(T);
+    constexpr int NV = DP * es / 16;
+    constexpr int epd = 4 / es;   // entries per staged dword
     const Geom &geo = a.geo;
     const Tile t = out_tile(a);
     char *om_b = reinterpret_cast<char *>(smem);
     char *val_s = om_b + a.om_lds_bytes;
-    stage_tile(a, t, om_b, val_s, 4);
+    stage_tile(a, t, om_b, val_s, es);
     staging_done();
-    float *om_s = reinterpret_cast<float *>(om_b);
 
     const int K3 = 3 * a.K;
+    const int par = (t.g * K3) & (epd - 1);   // element of entry 0 inside its staged dword
     const int q = threadIdx.x >> a.lanes_shift;
     const int chunk = threadIdx.x & ((1 << a.lanes_shift) - 1);
     const int lanes = 1 << a.lanes_shift;
@@ -506,15 +509,17 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
     // every thread stays to the end (far samples are written by whole
     // waves); threads past the tile or the image only take part in that
     const bool valid = py < a.th && oy < geo.Ho && ox < geo.Wo;
-    float *om = om_s + (valid ? q : 0) * a.om_dw;   // overwritten in place with the gradients
+    char *row = om_b + (valid ? q : 0) * a.om_dw * 4;
+    T *om = reinterpret_cast<T *>(row) + par;   // overwritten in place with the gradients
+    // softmax mode: the row's last 2K dwords hold p_k and dL/dp_k in fp32
+    // until the logit gradients are formed at the end
+    float *prob = reinterpret_cast<float *>(row) + (a.om_dw - 2 * a.K);
     const NearFrame nf = near_frame(a, t, oy, ox);
-    const int chan_off = (t.g * a.Cg + chunk * DP) * 4;
-    const unsigned cs = (unsigned)(geo.C * 4), rs = (unsigned)geo.W * cs;
+    const int chan_off = (t.g * a.Cg + chunk * DP) * es;
+    const unsigned cs = (unsigned)(geo.C * es), rs = (unsigned)geo.W * cs;
     const char *vb = val_s + chunk * NV * 16;
     const unsigned pix_off = ((unsigned)((t.n * geo.Ho + oy) * geo.Wo + ox)) * cs + (unsigned)chan_off;
     const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
-    // softmax mode: probabilities p_k are kept at om[3K + k] (the rows have
-    // K spare dwords) until the logit gradients are formed at the end
     float smx = 0.0f, sinv = 1.0f;
     if (SM)
         softmax_stats(om + 2 * a.K, a.K, smx, sinv);
@@ -522,12 +527,13 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
     float go[DP];
     {
         const __amdgpu_buffer_rsrc_t gor = rsrc(a.gout, a.gout_bytes);
+        u32x4 gv[NV];
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const f32x4 r = __builtin_bit_cast(f32x4, load16(gor, valid ? pix_off + 16 * v : kOutOfRange));
-            for (int e = 0; e < 4; ++e)
-                go[4 * v + e] = r[e];
-        }
+        for (int v = 0; v < NV; ++v)
+            gv[v] = load16(gor, valid ? pix_off + 16 * v : kOutOfRange);
+#pragma unroll
+        for (int c = 0; c < DP; ++c)
+            go[c] = Store<T>::get(gv, c);
         // wait for grad_out here: inside the loop the compiler cannot tell
         // these loads from the far-sample prefetch and would drain both
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -544,12 +550,12 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
     for (int k = 0; k < a.K; ++k) {
         int gi, gj;
         grid_point(geo, k, gi, gj);
-        const float dx = om[2 * k], dy = om[2 * k + 1];
-        float m = om[2 * a.K + k];
+        const float dx = Store<T>::scalar(om[2 * k]), dy = Store<T>::scalar(om[2 * k + 1]);
+        float m = Store<T>::scalar(om[2 * a.K + k]);
         if (SM) {
             m = expf(m - smx) * sinv;
             if (valid && chunk == 0)
-                om[K3 + k] = m;
+                prob[k] = m;
         }
         const float bh = nf.bh0 + (float)(gj * geo.dh), bw = nf.bw0 + (float)(gi * geo.dw);
         const NearSample s = near_sample(nf, geo.scale, bh, bw, dx, dy);
@@ -562,7 +568,7 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
                 Footprint f;
                 f.h0 = (int)s.fh;
                 f.w0 = (int)s.fw;
-                far_corner_loads<NV>(vr, corner_offset(geo, t.n, f, 4, chan_off), cs, rs, p00, p01, p10, p11);
+                far_corner_loads<NV>(vr, corner_offset(geo, t.n, f, es, chan_off), cs, rs, p00, p01, p10, p11);
             } else {
                 farbits |= 1u << k;
             }
@@ -582,10 +588,10 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
         float t00 = 0.0f, t01 = 0.0f, t10 = 0.0f, t11 = 0.0f;
 #pragma unroll
         for (int c = 0; c < DP; ++c) {
-            t00 = __builtin_fmaf(go[c], Store<float>::get(v00, c), t00);
-            t01 = __builtin_fmaf(go[c], Store<float>::get(v01, c), t01);
-            t10 = __builtin_fmaf(go[c], Store<float>::get(v10, c), t10);
-            t11 = __builtin_fmaf(go[c], Store<float>::get(v11, c), t11);
+            t00 = __builtin_fmaf(go[c], Store<T>::get(v00, c), t00);
+            t01 = __builtin_fmaf(go[c], Store<T>::get(v01, c), t01);
+            t10 = __builtin_fmaf(go[c], Store<T>::get(v10, c), t10);
+            t11 = __builtin_fmaf(go[c], Store<T>::get(v11, c), t11);
         }
         float gm, gw, gh;
         sample_grads(s.lh - s.fh, s.lw - s.fw, t00, t01, t10, t11, gm, gw, gh);
@@ -599,24 +605,28 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
         }
         if (valid && chunk == 0 && !far) {
             // the lanes of this pixel have read entry k already; far entries
-            // are still needed by the loop below
+            // are still needed by the loop below.  In softmax mode the mask
+            // slot holds dL/dp_k in fp32 until the final pass (kept exact).
             const float sm = geo.scale * m;
-            om[2 * k] = sm * gw;
-            om[2 * k + 1] = sm * gh;
-            om[2 * a.K + k] = gm;
+            om[2 * k] = Store<T>::make(sm * gw);
+            om[2 * k + 1] = Store<T>::make(sm * gh);
+            if (SM)
+                prob[a.K + k] = gm;
+            else
+                om[2 * a.K + k] = Store<T>::make(gm);
         }
     }
 
     // far samples, one per lane and iteration (the prefetched one first); the
     // whole wave stays in the loop for the grad_value atomics
     {
-        const __amdgpu_buffer_rsrc_t gr = rsrc(a.gvalue, a.value_bytes);
-        // this lane's part of a far sample's grad_value update: corner
-        // lane / DP, channel lane % DP of the owner's DP channels
+        const __amdgpu_buffer_rsrc_t gr = rsrc(a.gvalue, a.gvalue_bytes);
+        // this lane's part of a far sample's grad_value update (fp32 for
+        // every storage dtype): corner lane / DP, channel lane % DP
         const int lane = threadIdx.x & 63;
         const int my_corner = lane / DP, my_c = lane % DP;
-        const unsigned my_corner_off =
-            (unsigned)(my_corner & 1) * cs + (unsigned)(my_corner >> 1) * rs + 4u * (unsigned)my_c;
+        const unsigned gcs = (unsigned)(geo.C * 4), grs = (unsigned)geo.W * gcs;
+        const unsigned my_corner_off = (unsigned)(my_corner & 1) * gcs + (unsigned)(my_corner >> 1) * grs + 4u * (unsigned)my_c;
         while (__ballot(pk >= 0 || farbits != 0)) {
             const bool has = pk >= 0 || farbits != 0;
             int k = 0;
@@ -632,20 +642,20 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
                     k = __builtin_ctz(farbits);
                     farbits &= farbits - 1;
                 }
-                const float dx = om[2 * k], dy = om[2 * k + 1];
-                m = SM ? om[K3 + k] : om[2 * a.K + k];
+                const float dx = Store<T>::scalar(om[2 * k]), dy = Store<T>::scalar(om[2 * k + 1]);
+                m = SM ? prob[k] : Store<T>::scalar(om[2 * a.K + k]);
                 const Loc l = locate_lane(a, oy, ox, k, dx, dy);
                 const Footprint f = footprint(geo, l);
-                off = corner_offset(geo, t.n, f, 4, chan_off);
+                off = corner_offset(geo, t.n, f, es, chan_off);
                 if (!pre)
                     far_corner_loads<NV>(vr, off, cs, rs, p00, p01, p10, p11);
                 float t00 = 0.0f, t01 = 0.0f, t10 = 0.0f, t11 = 0.0f;
 #pragma unroll
                 for (int c = 0; c < DP; ++c) {
-                    t00 = __builtin_fmaf(go[c], Store<float>::get(p00, c), t00);
-                    t01 = __builtin_fmaf(go[c], Store<float>::get(p01, c), t01);
-                    t10 = __builtin_fmaf(go[c], Store<float>::get(p10, c), t10);
-                    t11 = __builtin_fmaf(go[c], Store<float>::get(p11, c), t11);
+                    t00 = __builtin_fmaf(go[c], Store<T>::get(p00, c), t00);
+                    t01 = __builtin_fmaf(go[c], Store<T>::get(p01, c), t01);
+                    t10 = __builtin_fmaf(go[c], Store<T>::get(p10, c), t10);
+                    t11 = __builtin_fmaf(go[c], Store<T>::get(p11, c), t11);
                 }
                 // zero-extended image: dots of corners outside are 0
                 t00 = (f.r0 && f.c0) ? t00 : 0.0f;
@@ -662,18 +672,23 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
             }
             if (has && chunk == 0) {
                 const float sm = geo.scale * m;
-                om[2 * k] = sm * gw;
-                om[2 * k + 1] = sm * gh;
-                om[2 * a.K + k] = gm;
+                om[2 * k] = Store<T>::make(sm * gw);
+                om[2 * k + 1] = Store<T>::make(sm * gh);
+                if (SM)
+                    prob[a.K + k] = gm;
+                else
+                    om[2 * a.K + k] = Store<T>::make(gm);
             }
-            // grad_value: one device atomic per corner and channel, issued by
-            // the whole wave for one (sample, lane) at a time so that each
-            // instruction covers four contiguous corner rows
+            // grad_value: one device atomic per corner and channel (pair),
+            // issued by the whole wave for one (sample, lane) at a time so
+            // that each instruction covers four contiguous corner rows
             unsigned long long fm = __ballot(has);
             while (fm) {
                 const int src = __builtin_ctzll(fm);
                 fm &= fm - 1;
-                const unsigned so = (unsigned)__builtin_amdgcn_readlane((int)off, src);
+                // byte offset of the corner in grad_value (fp32) from the
+                // value offset (storage dtype; corner_offset wraps consistently)
+                const unsigned so = (unsigned)__builtin_amdgcn_readlane((int)off, src) * (4u / (unsigned)es);
                 const float s00 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w00), src));
                 const float s01 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w01), src));
                 const float s10 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w10), src));
@@ -693,57 +708,77 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
     }
     if (SM && valid && chunk == 0) {
         // gradients with respect to the logits: p_k * (g_k - sum_j p_j g_j),
-        // with g_k = dL/dp_k now at om[2K + k]
+        // with g_k = dL/dp_k
         float sdot = 0.0f;
         for (int k = 0; k < a.K; ++k)
-            sdot = __builtin_fmaf(om[K3 + k], om[2 * a.K + k], sdot);
+            sdot = __builtin_fmaf(prob[k], prob[a.K + k], sdot);
         for (int k = 0; k < a.K; ++k)
-            om[2 * a.K + k] = om[K3 + k] * (om[2 * a.K + k] - sdot);
+            om[2 * a.K + k] = Store<T>::make(prob[k] * (prob[a.K + k] - sdot));
     }
     __syncthreads();
 
-    // write the group's gradient rows of the tile back, slot for slot as they
-    // were staged; group 0 also zeroes the padding channels
+    // write the group's gradient entries of the tile back, element for
+    // element (2-byte entries of neighbouring groups may share a dword);
+    // group 0 also zeroes the padding channels
     {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
         const __amdgpu_buffer_rsrc_t r = rsrc(a.gom, a.om_bytes);
-        const unsigned row_bytes = (unsigned)(geo.Wo * a.P * 4);
+        const unsigned row_bytes = (unsigned)(geo.Wo * a.P * es);
         const int row0 = t.n * geo.Ho + t.oy0;
         const int rows = min(a.th, geo.Ho - t.oy0);
+        const int row_elems = a.om_dw * epd;   // LDS elements per pixel row
         {
-            // slot j of a row: entry j % 3K of tile column j / 3K, at LDS dword
-            // (j / 3K) * om_dw + j % 3K of the row
+            // slot j of a row: entry j % 3K of tile column j / 3K
             unsigned lo[kMaxRowChunks];
             int li[kMaxRowChunks];
-            pixel_row_offsets(a, t, K3, a.k3_magic, (unsigned)(a.P * 4), (unsigned)(t.g * K3 * 4), lo);
+            const int row_slots = a.tw * K3;
 #pragma unroll
             for (int c = 0; c < kMaxRowChunks; ++c) {
                 const int j = c * 64 + lane;
                 const int px2 = (int)divm((unsigned)j, a.k3_magic);
-                li[c] = px2 * a.om_dw + (j - px2 * K3);
+                const int d = j - px2 * K3;
+                const int ox2 = t.ox0 + px2;
+                li[c] = px2 * row_elems + par + d;
+                lo[c] = (px2 < a.tw && ox2 < geo.Wo) ? (unsigned)((ox2 * a.P + t.g * K3 + d) * es) : kOutOfRange;
             }
-            const int row_slots = a.tw * K3;
             for (int rr = wave; rr < rows; rr += nwaves) {
                 const unsigned base = (unsigned)(row0 + rr) * row_bytes;
-                const unsigned *src = reinterpret_cast<const unsigned *>(om_s) + rr * a.tw * a.om_dw;
+                const T *src = reinterpret_cast<const T *>(om_b + rr * a.tw * a.om_dw * 4);
 #pragma unroll
                 for (int c = 0; c < kMaxRowChunks; ++c) {
-                    if (c * 64 < row_slots && c * 64 + lane < row_slots && lo[c] != kOutOfRange)
-                        __builtin_amdgcn_raw_buffer_store_b32(src[li[c]], r, base + lo[c], 0, 0);
+                    if (c * 64 < row_slots && c * 64 + lane < row_slots && lo[c] != kOutOfRange) {
+                        if constexpr (es == 4)
+                            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, src[li[c]]), r,
+                                                                  base + lo[c], 0, 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, src[li[c]]), r,
+                                                                  base + lo[c], 0, 0);
+                    }
                 }
             }
         }
         const int npad = a.P - a.G * K3;
         if (t.g == 0 && npad > 0) {
             unsigned lo[kMaxRowChunks];
-            pixel_row_offsets(a, t, npad, a.npad_magic, (unsigned)(a.P * 4), (unsigned)(a.G * K3 * 4), lo);
             const int row_slots = a.tw * npad;
+#pragma unroll
+            for (int c = 0; c < kMaxRowChunks; ++c) {
+                const int j = c * 64 + lane;
+                const int px2 = (int)divm((unsigned)j, a.npad_magic);
+                const int d = j - px2 * npad;
+                const int ox2 = t.ox0 + px2;
+                lo[c] = (px2 < a.tw && ox2 < geo.Wo) ? (unsigned)((ox2 * a.P + a.G * K3 + d) * es) : kOutOfRange;
+            }
             for (int rr = wave; rr < rows; rr += nwaves) {
                 const unsigned base = (unsigned)(row0 + rr) * row_bytes;
 #pragma unroll
                 for (int c = 0; c < kMaxRowChunks; ++c) {
-                    if (c * 64 < row_slots && c * 64 + lane < row_slots && lo[c] != kOutOfRange)
-                        __builtin_amdgcn_raw_buffer_store_b32(0u, r, base + lo[c], 0, 0);
+                    if (c * 64 < row_slots && c * 64 + lane < row_slots && lo[c] != kOutOfRange) {
+                        if constexpr (es == 4)
+                            __builtin_amdgcn_raw_buffer_store_b32(0u, r, base + lo[c], 0, 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)0, r, base + lo[c], 0, 0);
+                    }
                 }
             }
         }
@@ -785,13 +820,55 @@ __device__ __forceinline__ void shifted_entries(const u32x4 (&v)[NVEC], int mis,
         out[e] = __builtin_bit_cast(float, t[e] ^ ((t[e] ^ t[e + 2]) & m2));
 }
 
-template <int CG, int KMAX, bool SM>
+// 2-byte entries e = 0..NOUT-1 of a slice that starts `mis` (0..7, the same
+// for the whole block) elements into the 16-byte vectors v, as floats: a
+// dword shift by mis / 2, then a half-word select by mis % 2, all with bit
+// masks.
+template <typename T, int NVEC, int NOUT>
+__device__ __forceinline__ void shifted_entries16(const u32x4 (&v)[NVEC], int mis, float (&out)[NOUT])
+{
+    static_assert(NOUT + 7 <= 8 * NVEC, "vectors too short");
+    unsigned w[4 * NVEC];
+#pragma unroll
+    for (int i = 0; i < NVEC; ++i)
+        for (int e = 0; e < 4; ++e)
+            w[4 * i + e] = v[i][e];
+    const int sh = mis >> 1;
+    const unsigned m1 = 0u - (unsigned)(sh & 1), m2 = 0u - (unsigned)((sh >> 1) & 1);
+    unsigned t1[4 * NVEC - 1], W[4 * NVEC - 3];
+#pragma unroll
+    for (int i = 0; i < 4 * NVEC - 1; ++i)
+        t1[i] = w[i] ^ ((w[i] ^ w[i + 1]) & m1);
+#pragma unroll
+    for (int i = 0; i < 4 * NVEC - 3; ++i)
+        W[i] = t1[i] ^ ((t1[i] ^ t1[i + 2]) & m2);
+    const unsigned mp = 0u - (unsigned)(mis & 1);
+#pragma unroll
+    for (int e = 0; e < NOUT; ++e) {
+        const unsigned even = (e & 1) ? (W[e >> 1] >> 16) : (W[e >> 1] & 0xffffu);
+        const unsigned odd = (e & 1) ? (W[(e + 1) >> 1] & 0xffffu) : (W[e >> 1] >> 16);
+        out[e] = Store<T>::from_bits(even ^ ((even ^ odd) & mp));
+    }
+}
+
+template <typename T, int NVEC, int NOUT>
+__device__ __forceinline__ void entries_of(const u32x4 (&v)[NVEC], int mis, float (&out)[NOUT])
+{
+    if constexpr (sizeof(T) == 4)
+        shifted_entries(v, mis, out);
+    else
+        shifted_entries16<T>(v, mis, out);
+}
+
+template <typename T, int CG, int KMAX, bool SM>
 __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
 {
     extern __shared__ u32x4 smem[];
-    constexpr int NVG = CG / 4;                  // 16-byte vectors of one source pixel's grad_out
-    constexpr int NVO = (2 * KMAX + 3 + 3) / 4;  // vectors holding the 2K offsets after a shift
-    constexpr int NVM = (KMAX + 3 + 3) / 4;      // vectors holding the K masks after a shift
+    constexpr int es = (int)sizeof(T);
+    constexpr int EPV = 16 / es;                           // entries per 16-byte vector
+    constexpr int NVG = CG * es / 16;                      // vectors of one source pixel's grad_out
+    constexpr int NVO = (2 * KMAX + 2 * (EPV - 1)) / EPV;  // vectors holding the 2K offsets after a shift
+    constexpr int NVM = (KMAX + 2 * (EPV - 1)) / EPV;      // vectors holding the K masks after a shift
     const Geom &geo = a.geo;
     char *lds = reinterpret_cast<char *>(smem);
     unsigned *cnt = reinterpret_cast<unsigned *>(lds);   // [kMaxBins] samples per corner cell
@@ -830,7 +907,7 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
     const bool my_cell = tid < a.ch * a.cw;
     const int a0 = (ly + 1) * AW + lx + 1, a1 = a0 - AW;
 
-    const unsigned cs = (unsigned)(geo.C * 4);
+    const unsigned cs = (unsigned)(geo.C * es);
     const __amdgpu_buffer_rsrc_t omr = rsrc(a.om, a.om_bytes);
     const __amdgpu_buffer_rsrc_t gor = rsrc(a.gout, a.gout_bytes);
     // grad_out rows: slot j of a row is vector j % gps of source column j / gps
@@ -844,14 +921,14 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
             const int s = (int)divm((unsigned)j, a.gps_magic);
             const int v = j - s * a.gps;
             if (s < SW && v < NVG)
-                glo[c] = (unsigned)(sx0 + s) * cs + (unsigned)(g * CG * 4 + 16 * v);
+                glo[c] = (unsigned)(sx0 + s) * cs + (unsigned)(g * CG * es + 16 * v);
         }
     }
     // a source's offsets and masks: 16-byte aligned vectors from the one that
-    // holds the first entry (pixel rows are 32-byte multiples)
+    // holds the first entry (pixel rows are 16-byte multiples)
     const int eo = g * 3 * a.K, em = eo + 2 * a.K;
-    const int mis_o = eo & 3, mis_m = em & 3;
-    const unsigned vo = (unsigned)(eo - mis_o) * 4u, vm = (unsigned)(em - mis_m) * 4u;
+    const int mis_o = eo & (EPV - 1), mis_m = em & (EPV - 1);
+    const unsigned vo = (unsigned)((eo - mis_o) * es), vm = (unsigned)((em - mis_m) * es);
     const float Rf = (float)a.R, chf = (float)a.ch, cwf = (float)a.cw;
     const float ylo = (float)(cy0 - 1), xlo = (float)(cx0 - 1);
 
@@ -869,7 +946,7 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
                        [&](int rr) { return (unsigned)(n * geo.Ho + r0 + rr) * row_bytes; });
         const bool src_ok = srow < nrows;
         const int oy = r0 + srow, ox = sx0 + scol;
-        const unsigned pix = (unsigned)((n * geo.Ho + oy) * geo.Wo + ox) * (unsigned)(a.P * 4);
+        const unsigned pix = (unsigned)((n * geo.Ho + oy) * geo.Wo + ox) * (unsigned)(a.P * es);
         u32x4 vov[NVO], vmv[NVM];
 #pragma unroll
         for (int j = 0; j < NVO; ++j)
@@ -880,8 +957,8 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
         staging_done();   // also orders the counter reset before the counting
 
         float offs[2 * KMAX], msk[KMAX];
-        shifted_entries(vov, mis_o, offs);
-        shifted_entries(vmv, mis_m, msk);
+        entries_of<T>(vov, mis_o, offs);
+        entries_of<T>(vmv, mis_m, msk);
         if (SM) {
             float mx = msk[0];
 #pragma unroll
@@ -985,12 +1062,13 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
                 const float wx = from_left ? rv[1] : 1.0f - rv[1];
                 const float w = rv[2] * (wy * wx);
                 const u32x4 *gp = reinterpret_cast<const u32x4 *>(g_s + src * (unsigned)(a.gps * 16));
+                u32x4 gv[NVG];
 #pragma unroll
-                for (int v = 0; v < NVG; ++v) {
-                    const f32x4 gv = __builtin_bit_cast(f32x4, gp[v]);
-                    for (int e = 0; e < 4; ++e)
-                        acc[4 * v + e] = __builtin_fmaf(w, gv[e], acc[4 * v + e]);
-                }
+                for (int v = 0; v < NVG; ++v)
+                    gv[v] = gp[v];
+#pragma unroll
+                for (int c = 0; c < CG; ++c)
+                    acc[c] = __builtin_fmaf(w, Store<T>::get(gv, c), acc[c]);
             }
         }
         __syncthreads();
@@ -998,15 +1076,14 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
 
     const int my_cy = cy0 + ly, my_cx = cx0 + lx;
     if (my_cell && my_cy < geo.H && my_cx < geo.W) {
-        const __amdgpu_buffer_rsrc_t gvr = rsrc(a.gvalue, a.value_bytes);
-        const unsigned off = (unsigned)((n * geo.H + my_cy) * geo.W + my_cx) * cs + (unsigned)(g * CG * 4);
+        // grad_value is fp32 for every storage dtype
+        const __amdgpu_buffer_rsrc_t gvr = rsrc(a.gvalue, a.gvalue_bytes);
+        const unsigned off = ((unsigned)((n * geo.H + my_cy) * geo.W + my_cx) * (unsigned)geo.C + (unsigned)(g * CG)) * 4u;
+        u32x4 o[CG / 4];
+        Store<float>::pack(acc, o, CG / 4);
 #pragma unroll
-        for (int v = 0; v < NVG; ++v) {
-            f32x4 o;
-            for (int e = 0; e < 4; ++e)
-                o[e] = acc[4 * v + e];
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), gvr, off + 16 * v, 0, 0);
-        }
+        for (int v = 0; v < CG / 4; ++v)
+            __builtin_amdgcn_raw_buffer_store_b128(o[v], gvr, off + 16 * v, 0, 0);
     }
 }
 
@@ -1146,15 +1223,68 @@ hipError_t launch_forward_tiled(const Problem &p, const TilePlan &tp, const void
     return hipGetLastError();
 }
 
+namespace {
+
+typedef void (*Kernel)(TArgs);
+
+template <typename T, int CG>
+Kernel values_kernel(bool small_k, bool sm)
+{
+    if (small_k)
+        return sm ? dcnv4_bwd_values_tiled<T, CG, 9, true> : dcnv4_bwd_values_tiled<T, CG, 9, false>;
+    return sm ? dcnv4_bwd_values_tiled<T, CG, 25, true> : dcnv4_bwd_values_tiled<T, CG, 25, false>;
+}
+
+template <typename T>
+Kernel values_kernel_for(int Cg, bool small_k, bool sm)
+{
+    switch (Cg) {
+    case 4:
+        if constexpr (sizeof(T) == 4)
+            return values_kernel<T, 4>(small_k, sm);
+        return nullptr;
+    case 8:
+        return values_kernel<T, 8>(small_k, sm);
+    case 16:
+        return values_kernel<T, 16>(small_k, sm);
+    case 32:
+        return values_kernel<T, 32>(small_k, sm);
+    default:
+        return nullptr;
+    }
+}
+
+template <typename T>
+Kernel offsets_kernel_for(int dp, bool sm)
+{
+    switch (dp) {
+    case 4:
+        if constexpr (sizeof(T) == 4)
+            return sm ? dcnv4_bwd_offsets_tiled<T, 4, true> : dcnv4_bwd_offsets_tiled<T, 4, false>;
+        return nullptr;
+    case 8:
+        return sm ? dcnv4_bwd_offsets_tiled<T, 8, true> : dcnv4_bwd_offsets_tiled<T, 8, false>;
+    case 16:
+        return sm ? dcnv4_bwd_offsets_tiled<T, 16, true> : dcnv4_bwd_offsets_tiled<T, 16, false>;
+    default:
+        return nullptr;
+    }
+}
+
+}  // namespace
+
 hipError_t launch_backward_tiled(const Problem &p, const TilePlan &tp, const void *value, const void *offset_mask,
                                  const void *grad_output, void *grad_value, void *grad_offset_mask,
                                  hipStream_t stream)
 {
-    if (!out_tiles_ok(p, tp) || p.K > 25 || tp.tw * (p.P - 3 * p.G * p.K) > 64 * kMaxRowChunks || tp.ch * tp.cw > 256 || (tp.ch + 1) * (tp.cw + 1) > kMaxBins ||
-        tp.src_cap < 1 || tp.src_cap > 256 || tp.gps * 4 < p.Cg || tp.rec_offset < (2 * kMaxBins + 8) * 4 ||
+    const int es = p.elem;
+    if (!out_tiles_ok(p, tp) || p.K > 25 || tp.tw * (p.P - 3 * p.G * p.K) > 64 * kMaxRowChunks ||
+        tp.tw * 3 * p.K > 64 * kMaxRowChunks || tp.ch * tp.cw > 256 || (tp.ch + 1) * (tp.cw + 1) > kMaxBins ||
+        tp.src_cap < 1 || tp.src_cap > 256 || tp.gps * 16 < p.Cg * es || tp.rec_offset < (2 * kMaxBins + 8) * 4 ||
         tp.rec_offset % 16 != 0 || tp.gs_offset < tp.rec_offset + tp.src_cap * p.K * 16 ||
         tp.splat_lds_bytes < tp.gs_offset + tp.src_cap * tp.gps * 16 ||
-        (tp.cw + 2 * tp.R + (p.kw - 1) * p.dw + 1) / p.sw + 2 > tp.src_cap)   // source window width
+        (tp.cw + 2 * tp.R + (p.kw - 1) * p.dw + 1) / p.sw + 2 > tp.src_cap ||   // source window width
+        tp.om_dw < (3 * p.K * es + 3) / 4 + (p.softmax ? 2 * p.K : 0))
         return hipErrorInvalidConfiguration;
     TArgs a = make_targs(p, tp);
     a.value = value;
@@ -1162,39 +1292,31 @@ hipError_t launch_backward_tiled(const Problem &p, const TilePlan &tp, const voi
     a.gout = static_cast<const float *>(grad_output);
     a.gvalue = static_cast<float *>(grad_value);
     a.gom = static_cast<float *>(grad_offset_mask);
-    a.value_bytes = p.N * p.H * p.W * p.C * 4;
-    a.om_bytes = p.N * p.Ho * p.Wo * p.P * 4;
-    a.gout_bytes = p.N * p.Ho * p.Wo * p.C * 4;
+    a.value_bytes = p.N * p.H * p.W * p.C * es;
+    a.om_bytes = p.N * p.Ho * p.Wo * p.P * es;
+    a.gout_bytes = p.N * p.Ho * p.Wo * p.C * es;
+    a.gvalue_bytes = p.N * p.H * p.W * p.C * 4;
+    const bool small_k = p.K <= 9, sm = p.softmax != 0;
+    Kernel values = nullptr, offsets = nullptr;
+    if (p.dtype == 0) {
+        values = values_kernel_for<float>(p.Cg, small_k, sm);
+        offsets = offsets_kernel_for<float>(tp.dp, sm);
+    } else if (p.dtype == 1) {
+        values = values_kernel_for<_Float16>(p.Cg, small_k, sm);
+        offsets = offsets_kernel_for<_Float16>(tp.dp, sm);
+    } else if (p.dtype == 2) {
+        values = values_kernel_for<bf16_t>(p.Cg, small_k, sm);
+        offsets = offsets_kernel_for<bf16_t>(tp.dp, sm);
+    }
+    if (!values || !offsets)
+        return hipErrorInvalidValue;
     // 1) grad_value of near samples: every cell written once, plain stores
     {
         const int blocks = p.N * tp.ctiles_y * tp.ctiles_x * p.G;
-        const dim3 grid(blocks), block(256);
-        void (*kern)(TArgs) = nullptr;
-        const bool small_k = p.K <= 9, sm = p.softmax != 0;
-#define DCNV4_VALUES(CG)                                                                     \
-    kern = small_k ? (sm ? dcnv4_bwd_values_tiled<CG, 9, true> : dcnv4_bwd_values_tiled<CG, 9, false>) \
-                   : (sm ? dcnv4_bwd_values_tiled<CG, 25, true> : dcnv4_bwd_values_tiled<CG, 25, false>)
-        switch (p.Cg) {
-        case 4:
-            DCNV4_VALUES(4);
-            break;
-        case 8:
-            DCNV4_VALUES(8);
-            break;
-        case 16:
-            DCNV4_VALUES(16);
-            break;
-        case 32:
-            DCNV4_VALUES(32);
-            break;
-        default:
-            return hipErrorInvalidValue;
-        }
-#undef DCNV4_VALUES
-        hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), tp.splat_lds_bytes);
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(values), tp.splat_lds_bytes);
         if (e != hipSuccess)
             return e;
-        hipLaunchKernelGGL(kern, grid, block, tp.splat_lds_bytes, stream, a);
+        hipLaunchKernelGGL(values, dim3(blocks), dim3(256), tp.splat_lds_bytes, stream, a);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -1202,26 +1324,10 @@ hipError_t launch_backward_tiled(const Problem &p, const TilePlan &tp, const voi
     // 2) grad_offset_mask, plus far samples' grad_value by device atomics
     {
         const int blocks = p.N * tp.tiles_y * tp.tiles_x * p.G;
-        const dim3 grid(blocks), block(tp.threads);
-        void (*kern)(TArgs) = nullptr;
-        const bool sm = p.softmax != 0;
-        switch (tp.dp) {
-        case 16:
-            kern = sm ? dcnv4_bwd_offsets_tiled<16, true> : dcnv4_bwd_offsets_tiled<16, false>;
-            break;
-        case 8:
-            kern = sm ? dcnv4_bwd_offsets_tiled<8, true> : dcnv4_bwd_offsets_tiled<8, false>;
-            break;
-        case 4:
-            kern = sm ? dcnv4_bwd_offsets_tiled<4, true> : dcnv4_bwd_offsets_tiled<4, false>;
-            break;
-        default:
-            return hipErrorInvalidValue;
-        }
-        const hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), tp.lds_bytes);
+        const hipError_t e = allow_lds(reinterpret_cast<const void *>(offsets), tp.lds_bytes);
         if (e != hipSuccess)
             return e;
-        hipLaunchKernelGGL(kern, grid, block, tp.lds_bytes, stream, a);
+        hipLaunchKernelGGL(offsets, dim3(blocks), dim3(tp.threads), tp.lds_bytes, stream, a);
     }
     return hipGetLastError();
 }

@@ -159,8 +159,8 @@ def dcnv4_backward(value, offset_mask, grad_output, grad_value, grad_offset_mask
                    kernel_w=3, stride_h=1, stride_w=1, pad_h=1, pad_w=1, dilation_h=1,
                    dilation_w=1, group, group_channels, offset_scale=1.0, remove_center=False,
                    stream=None) -> None:
-    """Backward into caller-allocated grad_value (N,H,W,C) and
-    grad_offset_mask (N,Ho,Wo,P) (both overwritten)."""
+    """Backward into caller-allocated grad_value (N,H,W,C) float32 and
+    grad_offset_mask (N,Ho,Wo,P) in the inputs' dtype (both overwritten)."""
     dcnv4_backward_ex(value, offset_mask, grad_output, grad_value, grad_offset_mask,
                       kernel_h=kernel_h, kernel_w=kernel_w, stride_h=stride_h, stride_w=stride_w,
                       pad_h=pad_h, pad_w=pad_w, dilation_h=dilation_h, dilation_w=dilation_w,
@@ -175,11 +175,14 @@ def dcnv4_backward_ex(value, offset_mask, grad_output, grad_value, grad_offset_m
                       softmax=False, stream=None, _name="dcnv4_backward_ex") -> None:
     """dcnv4_backward with the DCNv3 softmax over the K masks when ``softmax``
     (the mask gradient is then taken with respect to the logits)."""
+    import torch
+
     for t, nm in ((value, "value"), (offset_mask, "offset_mask"), (grad_output, "grad_output"),
                   (grad_value, "grad_value"), (grad_offset_mask, "grad_offset_mask")):
         _check(t, nm)
-        if t.dtype != value.dtype:
-            raise TypeError(f"{nm} dtype {t.dtype} != value dtype {value.dtype}")
+        want = torch.float32 if nm == "grad_value" else value.dtype
+        if t.dtype != want:
+            raise TypeError(f"{nm} dtype {t.dtype} != {want}")
     N, H, W, C = value.shape
     lib = load()
     args = (ctypes.c_void_p(value.data_ptr()), ctypes.c_void_p(offset_mask.data_ptr()),
@@ -219,7 +222,7 @@ def backward(value, offset_mask, grad_output, **params):
     (dcnv4_backward_ex when ``softmax=True`` is among the parameters)."""
     import torch
 
-    gv = torch.empty_like(value)
+    gv = torch.empty(value.shape, dtype=torch.float32, device=value.device)
     gom = torch.empty_like(offset_mask)
     if params.get("softmax"):
         dcnv4_backward_ex(value, offset_mask, grad_output, gv, gom, **params)

@@ -75,12 +75,13 @@ class Workload:
         return s * (self.N * self.H * self.W * self.C + self.N * self.Ho * self.Wo * (self.P + self.C))
 
     def bwd_bytes(self) -> int:
-        """Compulsory backward bytes: read value, offset_mask, grad_output;
-        write grad_value, grad_offset_mask (all fp32)."""
+        """Compulsory backward bytes: read value, offset_mask, grad_output
+        and write grad_offset_mask in the storage dtype; write grad_value in
+        fp32."""
         s = self.elem_bytes
         nv = self.N * self.H * self.W * self.C
         no = self.N * self.Ho * self.Wo
-        return s * (2 * nv + no * (2 * self.P + self.C))
+        return s * (nv + no * (2 * self.P + self.C)) + 4 * nv
 
     def kwargs(self) -> dict:
         return dict(kernel_h=self.kernel[0], kernel_w=self.kernel[1],

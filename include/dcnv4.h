@@ -152,11 +152,17 @@ DCNV4_API int dcnv4_forward(const void *value, const void *offset_mask, void *ou
  *
  *   value, offset_mask       as for dcnv4_forward, read
  *   grad_output      (N, Ho, Wo, group*group_channels), read
- *   grad_value       (N, H, W, group*group_channels), written (overwritten,
- *                    not accumulated)
+ *   grad_value       (N, H, W, group*group_channels) fp32 for every dtype,
+ *                    written (overwritten, not accumulated)
  *   grad_offset_mask (N, Ho, Wo, om_channels), written; padding entries 0
  *
- * dtype: DCNV4_FP32 only (others return DCNV4_ERR_UNSUPPORTED).
+ * dtype: of value, offset_mask, grad_output and grad_offset_mask (grad_value
+ * is always fp32, so that the many contributions to one element are summed
+ * and rounded once; a caller that wants it in 16 bits rounds it once).  fp32
+ * for every geometry dcnv4_forward accepts; fp16 and bf16 (fp32 arithmetic,
+ * grad_offset_mask rounded to nearest-even into the storage dtype) when the
+ * LDS-tiled kernels cover the geometry: group_channels in {8, 16, 32} and
+ * K <= 25, otherwise DCNV4_ERR_UNSUPPORTED.
  * grad_offset_mask is deterministic.  grad_value is deterministic except for
  * the contributions of samples that land more than a few pixels from their
  * grid position, which are added with device atomics after the rest (their

@@ -158,8 +158,8 @@ def test_forward_pointer_and_layout_checks():
 
 
 def test_backward_pointer_and_dtype_checks():
-    assert bwd(dtype=1) == UNSUP
-    assert bwd(dtype=2) == UNSUP
+    assert bwd(dtype=1, Cg=4) == UNSUP   # 8 bytes of fp16 per group pixel
+    assert bwd(dtype=2, Cg=4) == UNSUP
     for i in range(5):
         ptrs = [A, B, Cp, D, E]
         ptrs[i] = None
@@ -179,8 +179,8 @@ def test_softmax_flag_checks():
         # K = 49 > 25: only the general kernels could take it, and they have
         # no softmax mode
         assert call(softmax=1, kh=7, kw=7, ph=3, pw=3, P=592) == UNSUP
-    assert bwd_ex(softmax=1, dtype=1) == UNSUP
-    assert bwd_ex(softmax=0, dtype=2) == UNSUP
+    assert bwd_ex(softmax=1, dtype=1, Cg=4) == UNSUP
+    assert bwd_ex(softmax=0, dtype=2, kh=7, kw=7, ph=3, pw=3, P=592) == UNSUP   # 16-bit: tiled only
 
 
 def test_binding_refuses_host_tensors():
