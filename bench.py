@@ -165,10 +165,43 @@ def time_configs(path, steps, warmup):
         print(json.dumps(line), file=sys.stderr, flush=True)
         del sets, s
         torch.cuda.empty_cache()
+    lines.append(time_layer(flush, steps, warmup))
+    print(json.dumps(lines[-1]), file=sys.stderr, flush=True)
     os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
     with open(path, "w") as f:
         for line in lines:
             f.write(json.dumps(line) + "\n")
+
+
+def time_layer(flush, steps, warmup):
+    """The DCNv4 layer (projections through the vendor BLAS, the operator in
+    this library) forward + backward on the benchmark shape, random weights."""
+    import torch
+
+    from dynamic_sparse_vision_amd import layer
+    from dynamic_sparse_vision_amd.workloads import WORKLOADS
+
+    w = WORKLOADS["c2_fwd_fp32_56x56_b64"]
+    dev = torch.device("cuda")
+    cfg = layer.LayerConfig(channels=w.C, group=w.G)
+    weights = {k: v.requires_grad_(True) for k, v in layer.init_weights(cfg, dev, seed=1).items()}
+    x = torch.randn(w.N, w.H, w.W, w.C, device=dev, requires_grad=True)
+    d_out = torch.randn(w.N, w.Ho, w.Wo, w.C, device=dev)
+    times = []
+    for i in range(warmup + steps):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        out = layer.layer_forward(x, weights, cfg)
+        out.backward(d_out)
+        e1.record()
+        e1.synchronize()
+        if i >= warmup:
+            times.append(e0.elapsed_time(e1))
+    ms = statistics.median(times)
+    return {"workload": "c2_layer_fwd_bwd_fp32_56x56_b64", "direction": "fwd+bwd", "softmax": False,
+            "dtype": "fp32", "ms": ms, "points_per_s": w.points / (ms * 1e-3),
+            "note": "DCNv4 layer: value / offset-mask / output projections (vendor BLAS) + operator"}
 
 
 def main():
