@@ -213,9 +213,10 @@ constexpr int kMaxTiledK = 25;        // grid points of the tiled kernels
 constexpr int kTiledMaxLds = 80 * 1024;
 constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kTileThreads = 512;
-constexpr int kCellTileLds = 40 * 1024;   // four cell-tile blocks per CU
-constexpr int kMaxCellBins = 768;     // (ch + 1) * (cw + 1) corner-cell bins
-constexpr int kCellBinBytes = (2 * kMaxCellBins + 8) * 4;   // counters, prefix, scan scratch
+constexpr int kCellTileLds = 78 * 1024;   // two cell-tile blocks per CU
+constexpr int kCellThreads = 512;         // threads of a cell-tile block: one per vertical pair of cells
+constexpr int kCellBinSlots = 2048;       // bin counters: (ch + 1) * (cw + 1) < 2048
+constexpr int kCellBinBytes = kCellBinSlots * 4 + (kCellThreads / 64) * 4;   // counters, scan scratch
 
 // Staged offset/mask dwords per pixel: a group's 3K entries, widened to whole
 // dwords (2-byte entries of odd groups start mid-dword).
@@ -285,29 +286,57 @@ int window_cols(const Problem &p, int cw, int R)
     return (cw + 2 * R + (p.kw - 1) * p.dw + 1) / p.sw + 2;
 }
 
-int window_rows(const Problem &p, int ch, int R)
+int floor_div_h(int a, int b)
 {
-    return (ch + 2 * R + (p.kh - 1) * p.dh + 1) / p.sh + 2;
+    const int q = a / b;
+    return (a % b != 0 && ((a < 0) != (b < 0))) ? q - 1 : q;
 }
 
-// Cell tile of the grad_value kernel (one thread per cell, at most 256):
-// minimise the samples evaluated, i.e. blocks x window pixels x K, plus a
-// per-batch cost; the window's rows must fit a batch of src_cap sources and
-// the staged row limit.
+// Source range [s0, s1) of a cell range starting at c0, `len` cells long,
+// along one axis (the kernel's window: output pixels whose near samples can
+// put a top-left corner in [c0 - 1, c0 + len - 1]).
+void source_range(int c0, int len, int R, int pad, int kern, int dil, int stride, int out, int *s0, int *s1)
+{
+    *s0 = std::max(0, -floor_div_h(-(c0 - 1 - R + pad - (kern - 1) * dil), stride));
+    *s1 = std::min(out, floor_div_h(c0 + len - 1 + R + pad, stride) + 1);
+}
+
+// Cell tile of the grad_value kernel: ch x cw cells, ch even, one thread
+// per vertical pair.  Modelled cost, summed over the tiles of an image:
+// per batch, the sample evaluation of its source waves plus a fixed part
+// (staging, the scan, four barriers); per block, the three-run gathers of
+// its pair waves (about 10 instructions per record of a 9-point sample).
 bool choose_cell_tile(const Problem &p, int R, int src_cap, int gps, int *ch, int *cw)
 {
     double best = -1;
-    for (int w = 1; w <= 256 && w <= p.W; ++w) {
-        const int sw = window_cols(p, w, R);
-        if (sw > src_cap || sw * gps > kRowSlots)
+    const int hmax = std::min(128, (p.H + 1) / 2 * 2);
+    for (int w = 1; w <= 128 && w <= p.W; ++w) {
+        const int sw_max = window_cols(p, w, R);
+        if (sw_max > src_cap || sw_max * gps > kRowSlots)
             break;
-        for (int h = 1; h <= 256 && h <= p.H; ++h) {
-            if (h * w > 256 || (h + 1) * (w + 1) > kMaxCellBins)
+        for (int h = 2; h <= hmax; h += 2) {
+            if ((h / 2) * w > kCellThreads || (h + 1) * (w + 1) >= kCellBinSlots)
                 break;
-            const double blocks = (double)((p.H + h - 1) / h) * ((p.W + w - 1) / w);
-            const int sh = window_rows(p, h, R);
-            const double batches = std::ceil((double)sh / (src_cap / sw));
-            const double cost = blocks * ((double)sh * sw * p.K + 1024.0 * batches);
+            const int pair_waves = ((h / 2) * w + 63) / 64;
+            double cost = 0;
+            for (int y0 = 0; y0 < p.H; y0 += h) {
+                int r0, r1;
+                source_range(y0, h, R, p.ph, p.kh, p.dh, p.sh, p.Ho, &r0, &r1);
+                for (int x0 = 0; x0 < p.W; x0 += w) {
+                    int c0, c1;
+                    source_range(x0, w, R, p.pw, p.kw, p.dw, p.sw, p.Wo, &c0, &c1);
+                    const int sh = std::max(0, r1 - r0), sw = std::max(0, c1 - c0);
+                    double blk = 400.0 + pair_waves * 90.0 * 4 * p.K;
+                    if (sw > 0) {
+                        const int br = std::max(1, src_cap / sw);
+                        for (int r = 0; r < sh; r += br) {
+                            const int nsrc = std::min(br, sh - r) * sw;
+                            blk += 800.0 + ((nsrc + 63) / 64) * (40.0 * p.K + 60.0);
+                        }
+                    }
+                    cost += blk;
+                }
+            }
             if (best < 0 || cost < best) {
                 best = cost;
                 *ch = h;
@@ -397,7 +426,7 @@ int plan_backward_tiled(const Problem &p, TilePlan *tp)
     // samples of 16 bytes and src_cap staged grad_output pixels
     tp->gps = (p.Cg * p.elem / 16) | 1;
     tp->rec_offset = kCellBinBytes;
-    tp->src_cap = std::min(256, (kCellTileLds - kCellBinBytes) / (16 * (p.K + tp->gps)));
+    tp->src_cap = std::min(kCellThreads, (kCellTileLds - kCellBinBytes) / (16 * (p.K + tp->gps)));
     if (tp->src_cap < 1)
         return DCNV4_ERR_UNSUPPORTED;
     if (!choose_cell_tile(p, tp->R, tp->src_cap, tp->gps, &tp->ch, &tp->cw))

@@ -31,8 +31,9 @@
 // computed without float atomics: a block owns a tile of *input* cells,
 // evaluates the near samples of the output pixels that can reach it, sorts
 // them by their top-left corner cell (a counting sort with integer LDS
-// atomics), and every cell sums in registers the lists of the four corner
-// cells that reach it; the tile is then written with plain stores.
+// atomics), and every thread sums in registers, for a vertical pair of
+// cells, the lists of the corner cells that reach them; the tile is then
+// written with plain stores.
 // grad_offset_mask is forward-shaped; it also adds the contributions of far
 // samples to grad_value with device atomics (one 64-lane instruction per far
 // sample), after the cell-tile kernel has written every cell.
@@ -51,7 +52,8 @@ using namespace dev;
 
 constexpr int kMaxRowChunks = 8;      // a staged row spans at most 8 x 64 slots
 constexpr int kMaxTileThreads = 512;  // threads of an output-tile block
-constexpr int kMaxBins = 768;         // corner-cell bins of a cell tile (3 per thread)
+constexpr int kCellThreads = 512;     // threads of a cell-tile block
+constexpr int kCellBinSlots = 2048;   // bin counters of a cell tile: (ch + 1) * (cw + 1) < 2048, 4 per thread
 constexpr unsigned kOutOfRange = 0x80000000u;   // >= any buffer size used here
 // s_waitcnt immediate: vector memory count 0, export and LDS/scalar counts
 // left at their maxima (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
@@ -80,6 +82,7 @@ struct TArgs {
     int om_lds_bytes;
     // cell tiles (backward grad_value)
     int ch, cw, ctiles_y, ctiles_x;
+    unsigned cw_magic;           // ceil(2^32 / cw)
     int src_cap;                 // source pixels per batch
     int gps;                     // LDS stride of a staged grad_output pixel, 16-byte units
     unsigned gps_magic;
@@ -860,8 +863,22 @@ __device__ __forceinline__ void entries_of(const u32x4 (&v)[NVEC], int mis, floa
         shifted_entries16<T>(v, mis, out);
 }
 
+// A cell-tile block: ch x cw input cells of one (image, group), ch even;
+// thread t < (ch / 2) * cw owns the vertical pair of cells (2 * (t / cw),
+// t % cw) and the one below it.  The output pixels whose near samples can
+// reach the tile (its "sources") are taken in batches of whole rows; a batch
+// stages their grad_output rows, evaluates their samples (one source per
+// thread), and counting-sorts the near samples by top-left corner cell
+// ("bin"; bins span rows cy0-1 .. cy0+ch-1 and columns cx0-1 .. cx0+cw-1).
+// A sample's corners are the cells of bin rows by, by+1 and columns bx,
+// bx+1, so the pair sums three runs of the sorted list: bin row 2py (its
+// upper cell is the samples' lower corner row), 2py+1 (both cells) and 2py+2
+// (its lower cell is their upper row); each run is the two bins of columns
+// px and px+1, which are adjacent in the sorted order.  Every record adds
+// to exactly the cells that are its corners (non-finite inputs spread as in
+// the plain sum).
 template <typename T, int CG, int KMAX, bool SM>
-__global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
+__global__ __launch_bounds__(kCellThreads) __attribute__((amdgpu_waves_per_eu(4))) void dcnv4_bwd_values_tiled(TArgs a)
 {
     extern __shared__ u32x4 smem[];
     constexpr int es = (int)sizeof(T);
@@ -871,11 +888,12 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
     constexpr int NVM = (KMAX + 2 * (EPV - 1)) / EPV;      // vectors holding the K masks after a shift
     const Geom &geo = a.geo;
     char *lds = reinterpret_cast<char *>(smem);
-    unsigned *cnt = reinterpret_cast<unsigned *>(lds);   // [kMaxBins] samples per corner cell
-    unsigned *base = cnt + kMaxBins;                     // [kMaxBins] exclusive prefix of cnt
-    unsigned *wsum = base + kMaxBins;                    // [8]
-    f32x4 *rec = reinterpret_cast<f32x4 *>(lds + a.rec_offset);   // (frac h, frac w, m, source)
-    char *g_s = lds + a.gs_offset;                       // grad_out of the batch's sources
+    // [kCellBinSlots]: per-bin counts, then their exclusive prefix in place,
+    // then (after placing) the end of each bin
+    unsigned *bins = reinterpret_cast<unsigned *>(lds);
+    unsigned *wsum = bins + kCellBinSlots;               // [kCellThreads / 64] per-wave scan totals
+    // sorted records: (frac h, frac w, m, LDS byte offset of the source's grad_out)
+    f32x4 *rec = reinterpret_cast<f32x4 *>(lds + a.rec_offset);
 
     int b = xcd_tile(blockIdx.x, gridDim.x);
     const int g = b % a.G;
@@ -901,15 +919,15 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
     const int BR = SW > 0 ? max(1, a.src_cap / SW) : 1;
     const int srow = SW > 0 ? tid / SW : 0, scol = tid - srow * SW;
     const int sy_end = SW > 0 ? sy1 : sy0;   // no source column: no batch
-    // this thread's cell and the bins of the corner cells that reach it: the
-    // cell itself (corner 00), left (01), up (10), up-left (11)
-    const int ly = tid / a.cw, lx = tid - ly * a.cw;
-    const bool my_cell = tid < a.ch * a.cw;
-    const int a0 = (ly + 1) * AW + lx + 1, a1 = a0 - AW;
+    // this thread's pair of cells
+    const int py = (int)divm((unsigned)tid, a.cw_magic), px = tid - py * a.cw;
+    const bool my_pair = tid < (a.ch >> 1) * a.cw;
+    const int binA = 2 * py * AW + px;   // bin row 2py, column px
 
     const unsigned cs = (unsigned)(geo.C * es);
     const __amdgpu_buffer_rsrc_t omr = rsrc(a.om, a.om_bytes);
     const __amdgpu_buffer_rsrc_t gor = rsrc(a.gout, a.gout_bytes);
+    char *g_s = lds + a.gs_offset;   // grad_out of the batch's sources
     // grad_out rows: slot j of a row is vector j % gps of source column j / gps
     unsigned glo[kMaxRowChunks];
     const int grow_slots = SW * a.gps;
@@ -931,21 +949,29 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
     const unsigned vo = (unsigned)((eo - mis_o) * es), vm = (unsigned)((em - mis_m) * es);
     const float Rf = (float)a.R, chf = (float)a.ch, cwf = (float)a.cw;
     const float ylo = (float)(cy0 - 1), xlo = (float)(cx0 - 1);
+    // LDS byte offset of this thread's source in the staged grad_out
+    const unsigned my_gs = (unsigned)a.gs_offset + (unsigned)tid * (unsigned)(a.gps * 16);
 
-    float acc[CG];
+    float acc0[CG], acc1[CG];
 #pragma unroll
     for (int c = 0; c < CG; ++c)
-        acc[c] = 0.0f;
+        acc0[c] = acc1[c] = 0.0f;
 
-    for (int r0 = sy0; r0 < sy_end; r0 += BR) {
-        const int nrows = min(BR, sy1 - r0);
-        for (int i = tid; i < NB; i += 256)
-            cnt[i] = 0u;
+    // batch b takes source rows sy0 + b, sy0 + b + nb, ...: every batch
+    // spreads its samples over the whole tile, so the waves of a block get
+    // similar shares of each batch's gather
+    const int SH = sy_end - sy0;
+    const int nb = (SH + BR - 1) / BR;
+    for (int bt = 0; bt < nb; ++bt) {
+        const int r0 = sy0 + bt;
+        const int nrows = (SH - bt + nb - 1) / nb;
+        for (int i = 4 * tid; i <= NB; i += 4 * kCellThreads)
+            *reinterpret_cast<u32x4 *>(bins + i) = u32x4{0u, 0u, 0u, 0u};
         const unsigned row_bytes = (unsigned)geo.Wo * cs;
         stage_rows<16>(gor, g_s, nrows, grow_slots, glo,
-                       [&](int rr) { return (unsigned)(n * geo.Ho + r0 + rr) * row_bytes; });
+                       [&](int rr) { return (unsigned)(n * geo.Ho + r0 + rr * nb) * row_bytes; });
         const bool src_ok = srow < nrows;
-        const int oy = r0 + srow, ox = sx0 + scol;
+        const int oy = r0 + srow * nb, ox = sx0 + scol;
         const unsigned pix = (unsigned)((n * geo.Ho + oy) * geo.Wo + ox) * (unsigned)(a.P * es);
         u32x4 vov[NVO], vmv[NVM];
 #pragma unroll
@@ -954,7 +980,7 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
 #pragma unroll
         for (int j = 0; j < NVM; ++j)
             vmv[j] = load16(omr, src_ok ? pix + vm + 16u * j : kOutOfRange);
-        staging_done();   // also orders the counter reset before the counting
+        staging_done();   // also orders the bin reset before the counting
 
         float offs[2 * KMAX], msk[KMAX];
         entries_of<T>(vov, mis_o, offs);
@@ -976,40 +1002,45 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
                 msk[k] *= inv;
         }
         const float bh0 = (float)(oy * geo.sh - geo.ph), bw0 = (float)(ox * geo.sw - geo.pw);
-        unsigned slot[KMAX];
-        float fa[KMAX], fb[KMAX];
+        // The batch's near samples whose top-left corner cell is in the tile:
+        // their bin (relative to (cy0 - 1, cx0 - 1)) and fractional parts.
+        // Evaluated twice, to count and then to place, so that nothing but the
+        // offsets and masks stays live across the scan.
+        auto sample = [&](int k, unsigned &bin, float &fa, float &fb) {
+            int gi, gj;
+            grid_point(geo, k, gi, gj);
+            const float bh = bh0 + (float)(gj * geo.dh), bw = bw0 + (float)(gi * geo.dw);
+            const float lh = __builtin_fmaf(geo.scale, offs[2 * k + 1], bh);
+            const float lw = __builtin_fmaf(geo.scale, offs[2 * k], bw);
+            const float fh = __builtin_floorf(lh), fw = __builtin_floorf(lw);
+            const bool nr = __builtin_fabsf(fh - bh) <= Rf && __builtin_fabsf(fw - bw) <= Rf;
+            const float ay = fh - ylo, ax = fw - xlo;
+            fa = lh - fh;
+            fb = lw - fw;
+            const bool in = src_ok && nr && ay >= 0.0f && ay <= chf && ax >= 0.0f && ax <= cwf;
+            bin = in ? (unsigned)((int)ay * AW + (int)ax) : 0xffffffffu;
+        };
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-            slot[k] = 0xffffffffu;
-            fa[k] = fb[k] = 0.0f;
             if (k < a.K) {
-                int gi, gj;
-                grid_point(geo, k, gi, gj);
-                const float bh = bh0 + (float)(gj * geo.dh), bw = bw0 + (float)(gi * geo.dw);
-                const float lh = __builtin_fmaf(geo.scale, offs[2 * k + 1], bh);
-                const float lw = __builtin_fmaf(geo.scale, offs[2 * k], bw);
-                const float fh = __builtin_floorf(lh), fw = __builtin_floorf(lw);
-                const bool nr = __builtin_fabsf(fh - bh) <= Rf && __builtin_fabsf(fw - bw) <= Rf;
-                // top-left corner cell relative to (cy0 - 1, cx0 - 1)
-                const float ay = fh - ylo, ax = fw - xlo;
-                if (src_ok && nr && ay >= 0.0f && ay <= chf && ax >= 0.0f && ax <= cwf) {
-                    const unsigned bin = (unsigned)((int)ay * AW + (int)ax);
-                    const unsigned rank = atomicAdd(&cnt[bin], 1u);
-                    slot[k] = (bin << 16) | rank;
-                }
-                fa[k] = lh - fh;
-                fb[k] = lw - fw;
+                unsigned bin;
+                float fa, fb;
+                sample(k, bin, fa, fb);
+                if (bin != 0xffffffffu)
+                    __hip_atomic_fetch_add(&bins[bin], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
         }
         __syncthreads();
 
-        // exclusive prefix sum of the bins, three per thread
+        // exclusive prefix of the counts, in place, four bins per thread
+        // (entries past NB are not touched)
         {
-            const int i0 = 3 * tid;
-            const unsigned c0 = i0 < NB ? cnt[i0] : 0u;
-            const unsigned c1 = i0 + 1 < NB ? cnt[i0 + 1] : 0u;
-            const unsigned c2 = i0 + 2 < NB ? cnt[i0 + 2] : 0u;
-            const unsigned mine = c0 + c1 + c2;
+            const int i0 = 4 * tid;
+            u32x4 c = i0 <= NB ? *reinterpret_cast<const u32x4 *>(bins + i0) : u32x4{0u, 0u, 0u, 0u};
+            c[1] = i0 + 1 <= NB ? c[1] : 0u;
+            c[2] = i0 + 2 <= NB ? c[2] : 0u;
+            c[3] = i0 + 3 <= NB ? c[3] : 0u;
+            const unsigned mine = c[0] + c[1] + c[2] + c[3];
             unsigned x = mine;
             for (int d = 1; d < 64; d <<= 1) {
                 const unsigned y = __shfl_up(x, d);
@@ -1023,67 +1054,115 @@ __global__ __launch_bounds__(256) void dcnv4_bwd_values_tiled(TArgs a)
             for (int w = 0; w < wave; ++w)
                 off += wsum[w];
             const unsigned e0 = off + x - mine;
-            if (i0 < NB)
-                base[i0] = e0;
-            if (i0 + 1 < NB)
-                base[i0 + 1] = e0 + c0;
-            if (i0 + 2 < NB)
-                base[i0 + 2] = e0 + c0 + c1;
+            if (i0 <= NB)
+                bins[i0] = e0;
+            if (i0 + 1 <= NB)
+                bins[i0 + 1] = e0 + c[0];
+            if (i0 + 2 <= NB)
+                bins[i0 + 2] = e0 + c[0] + c[1];
+            if (i0 + 3 <= NB)
+                bins[i0 + 3] = e0 + c[0] + c[1] + c[2];
         }
         __syncthreads();
 
+        // place the records; afterwards bins[b] is the end of bin b (the
+        // start of bin b + 1).  The empty asm hides that the inputs are the
+        // same as in the counting pass, so the samples are evaluated again
+        // instead of being kept in registers across the scan.
+#pragma unroll
+        for (int k = 0; k < 2 * KMAX; ++k)
+            asm volatile("" : "+v"(offs[k]));
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-            if (slot[k] != 0xffffffffu) {
-                const unsigned idx = base[slot[k] >> 16] + (slot[k] & 0xffffu);
-                f32x4 r;
-                r[0] = fa[k];
-                r[1] = fb[k];
-                r[2] = msk[k];
-                r[3] = __builtin_bit_cast(float, (unsigned)tid);
-                rec[idx] = r;
+            if (k < a.K) {
+                unsigned bin;
+                float fa, fb;
+                sample(k, bin, fa, fb);
+                if (bin != 0xffffffffu) {
+                    const unsigned idx = atomicAdd(&bins[bin], 1u);
+                    f32x4 r;
+                    r[0] = fa;
+                    r[1] = fb;
+                    r[2] = msk[k];
+                    r[3] = __builtin_bit_cast(float, my_gs);
+                    rec[idx] = r;
+                }
             }
         }
         __syncthreads();
 
-        // each cell sums the samples whose corners reach it: bins a0-1, a0
-        // (same row) are one run of the sorted list, bins a1-1, a1 another
-        if (my_cell) {
-            const unsigned s1 = base[a0 - 1], b1 = base[a0], n1 = b1 - s1 + cnt[a0];
-            const unsigned s2 = base[a1 - 1], b2 = base[a1], n2 = b2 - s2 + cnt[a1];
-            const unsigned ntot = n1 + n2;
-            for (unsigned r = 0; r < ntot; ++r) {
-                const bool same_row = r < n1;
-                const unsigned idx = same_row ? s1 + r : s2 + (r - n1);
-                const bool from_left = idx < (same_row ? b1 : b2);
-                const f32x4 rv = rec[idx];
-                const unsigned src = __builtin_bit_cast(u32x4, rv)[3];   // whole-vector cast, then index
-                const float wy = same_row ? 1.0f - rv[0] : rv[0];
-                const float wx = from_left ? rv[1] : 1.0f - rv[1];
-                const float w = rv[2] * (wy * wx);
-                const u32x4 *gp = reinterpret_cast<const u32x4 *>(g_s + src * (unsigned)(a.gps * 16));
-                u32x4 gv[NVG];
+        if (my_pair) {
+            // one record ahead: the next record's read overlaps this one's
+            // grad_out reads (the read past the end stays inside the LDS
+            // allocation and is not used)
+            auto gather = [&](int bin, auto &&add) {
+                const unsigned s = bin > 0 ? bins[bin - 1] : 0u, mid = bins[bin], e = bins[bin + 1];
+                f32x4 rv = rec[s];
+                for (unsigned idx = s; idx < e; ++idx) {
+                    const f32x4 cur = rv;
+                    // LDS byte offset of the source's grad_out (whole-vector cast, then index)
+                    const unsigned src = __builtin_bit_cast(u32x4, cur)[3];
+                    const u32x4 *gp = reinterpret_cast<const u32x4 *>(lds + src);
+                    u32x4 gv[NVG];
 #pragma unroll
-                for (int v = 0; v < NVG; ++v)
-                    gv[v] = gp[v];
+                    for (int v = 0; v < NVG; ++v)
+                        gv[v] = gp[v];
+                    rv = rec[idx + 1];
+                    // column px of the bin pair: this cell is the samples' right column
+                    const float wx = idx < mid ? cur[1] : 1.0f - cur[1];
+                    add(cur[0], wx, cur[2], gv);
+                }
+            };
+            // bin row 2py: the upper cell is the samples' lower row
+            gather(binA, [&](float fy, float wx, float m, const u32x4(&gv)[NVG]) {
+                const float w = m * (fy * wx);
 #pragma unroll
                 for (int c = 0; c < CG; ++c)
-                    acc[c] = __builtin_fmaf(w, Store<T>::get(gv, c), acc[c]);
-            }
+                    acc0[c] = __builtin_fmaf(w, Store<T>::get(gv, c), acc0[c]);
+            });
+            // bin row 2py+1: upper row of the upper cell, lower row of the lower
+            gather(binA + AW, [&](float fy, float wx, float m, const u32x4(&gv)[NVG]) {
+                const float w0 = m * ((1.0f - fy) * wx);
+                const float w1 = m * (fy * wx);
+#pragma unroll
+                for (int c = 0; c < CG; ++c) {
+                    const float gc = Store<T>::get(gv, c);
+                    acc0[c] = __builtin_fmaf(w0, gc, acc0[c]);
+                    acc1[c] = __builtin_fmaf(w1, gc, acc1[c]);
+                }
+            });
+            // bin row 2py+2: the lower cell is the samples' upper row
+            gather(binA + 2 * AW, [&](float fy, float wx, float m, const u32x4(&gv)[NVG]) {
+                const float w = m * ((1.0f - fy) * wx);
+#pragma unroll
+                for (int c = 0; c < CG; ++c)
+                    acc1[c] = __builtin_fmaf(w, Store<T>::get(gv, c), acc1[c]);
+            });
         }
         __syncthreads();
     }
 
-    const int my_cy = cy0 + ly, my_cx = cx0 + lx;
-    if (my_cell && my_cy < geo.H && my_cx < geo.W) {
+    if (my_pair) {
         // grad_value is fp32 for every storage dtype
         const __amdgpu_buffer_rsrc_t gvr = rsrc(a.gvalue, a.gvalue_bytes);
-        const unsigned off = ((unsigned)((n * geo.H + my_cy) * geo.W + my_cx) * (unsigned)geo.C + (unsigned)(g * CG)) * 4u;
-        u32x4 o[CG / 4];
-        Store<float>::pack(acc, o, CG / 4);
+        const int my_cy = cy0 + 2 * py, my_cx = cx0 + px;
+        if (my_cx < geo.W) {
+            const unsigned off = ((unsigned)((n * geo.H + my_cy) * geo.W + my_cx) * (unsigned)geo.C + (unsigned)(g * CG)) * 4u;
+            const unsigned down = (unsigned)geo.W * (unsigned)geo.C * 4u;
+            u32x4 o0[CG / 4], o1[CG / 4];
+            Store<float>::pack(acc0, o0, CG / 4);
+            Store<float>::pack(acc1, o1, CG / 4);
+            if (my_cy < geo.H) {
 #pragma unroll
-        for (int v = 0; v < CG / 4; ++v)
-            __builtin_amdgcn_raw_buffer_store_b128(o[v], gvr, off + 16 * v, 0, 0);
+                for (int v = 0; v < CG / 4; ++v)
+                    __builtin_amdgcn_raw_buffer_store_b128(o0[v], gvr, off + 16 * v, 0, 0);
+            }
+            if (my_cy + 1 < geo.H) {
+#pragma unroll
+                for (int v = 0; v < CG / 4; ++v)
+                    __builtin_amdgcn_raw_buffer_store_b128(o1[v], gvr, off + down + 16 * v, 0, 0);
+            }
+        }
     }
 }
 
@@ -1152,6 +1231,7 @@ TArgs make_targs(const Problem &p, const TilePlan &tp)
     a.cw = tp.cw;
     a.ctiles_y = tp.ctiles_y;
     a.ctiles_x = tp.ctiles_x;
+    a.cw_magic = magic_for(tp.cw);
     a.src_cap = tp.src_cap;
     a.gps = tp.gps;
     a.gps_magic = magic_for(tp.gps);
@@ -1279,11 +1359,15 @@ hipError_t launch_backward_tiled(const Problem &p, const TilePlan &tp, const voi
 {
     const int es = p.elem;
     if (!out_tiles_ok(p, tp) || p.K > 25 || tp.tw * (p.P - 3 * p.G * p.K) > 64 * kMaxRowChunks ||
-        tp.tw * 3 * p.K > 64 * kMaxRowChunks || tp.ch * tp.cw > 256 || (tp.ch + 1) * (tp.cw + 1) > kMaxBins ||
-        tp.src_cap < 1 || tp.src_cap > 256 || tp.gps * 16 < p.Cg * es || tp.rec_offset < (2 * kMaxBins + 8) * 4 ||
-        tp.rec_offset % 16 != 0 || tp.gs_offset < tp.rec_offset + tp.src_cap * p.K * 16 ||
+        tp.tw * 3 * p.K > 64 * kMaxRowChunks || tp.ch < 2 || tp.ch % 2 != 0 || tp.cw < 1 ||
+        (tp.ch / 2) * tp.cw > kCellThreads || (tp.ch + 1) * (tp.cw + 1) >= kCellBinSlots || tp.src_cap < 1 ||
+        tp.src_cap > kCellThreads || tp.gps * 16 < p.Cg * es ||
+        tp.rec_offset < (kCellBinSlots + kCellThreads / 64) * 4 || tp.rec_offset % 16 != 0 ||
+        tp.gs_offset < tp.rec_offset + tp.src_cap * p.K * 16 || tp.gs_offset % 16 != 0 ||
         tp.splat_lds_bytes < tp.gs_offset + tp.src_cap * tp.gps * 16 ||
-        (tp.cw + 2 * tp.R + (p.kw - 1) * p.dw + 1) / p.sw + 2 > tp.src_cap ||   // source window width
+        // source window width: within a batch and within a staged row
+        (tp.cw + 2 * tp.R + (p.kw - 1) * p.dw + 1) / p.sw + 2 > tp.src_cap ||
+        ((tp.cw + 2 * tp.R + (p.kw - 1) * p.dw + 1) / p.sw + 2) * tp.gps > 64 * kMaxRowChunks ||
         tp.om_dw < (3 * p.K * es + 3) / 4 + (p.softmax ? 2 * p.K : 0))
         return hipErrorInvalidConfiguration;
     TArgs a = make_targs(p, tp);
@@ -1316,7 +1400,7 @@ hipError_t launch_backward_tiled(const Problem &p, const TilePlan &tp, const voi
         hipError_t e = allow_lds(reinterpret_cast<const void *>(values), tp.splat_lds_bytes);
         if (e != hipSuccess)
             return e;
-        hipLaunchKernelGGL(values, dim3(blocks), dim3(256), tp.splat_lds_bytes, stream, a);
+        hipLaunchKernelGGL(values, dim3(blocks), dim3(kCellThreads), tp.splat_lds_bytes, stream, a);
         e = hipGetLastError();
         if (e != hipSuccess)
             return e;

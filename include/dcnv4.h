@@ -163,10 +163,10 @@ DCNV4_API int dcnv4_forward(const void *value, const void *offset_mask, void *ou
  * grad_offset_mask rounded to nearest-even into the storage dtype) when the
  * LDS-tiled kernels cover the geometry: group_channels in {8, 16, 32} and
  * K <= 25, otherwise DCNV4_ERR_UNSUPPORTED.
- * grad_offset_mask is deterministic.  grad_value is deterministic except for
- * the contributions of samples that land more than a few pixels from their
- * grid position, which are added with device atomics after the rest (their
- * last bits may then differ from run to run).
+ * grad_offset_mask is deterministic.  grad_value is summed in an order that
+ * depends on thread timing (an on-chip counting sort of the samples, and
+ * device atomics for samples that land more than a few pixels from their
+ * grid position), so its last bits may differ from run to run.
  * Errors: as dcnv4_forward.
  */
 DCNV4_API int dcnv4_backward(const void *value, const void *offset_mask, const void *grad_output,
