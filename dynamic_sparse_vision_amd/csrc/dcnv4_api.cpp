@@ -210,6 +210,10 @@ bool pow2(int v)
 
 constexpr int kRowSlots = 512;        // a staged LDS row spans at most 8 x 64 slots
 constexpr int kMaxTiledK = 25;        // grid points of the tiled kernels
+#ifndef DCNV4_FWD_RMAX
+#define DCNV4_FWD_RMAX 7
+#endif
+constexpr int kForwardRmax = DCNV4_FWD_RMAX;   // largest halo of the forward tiles
 constexpr int kTiledMaxLds = 80 * 1024;
 constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kTileThreads = 512;
@@ -404,7 +408,8 @@ int plan_tiled_common(const Problem &p, int elem, int om_dw, int row_elems, int 
 int plan_forward_tiled(const Problem &p, TilePlan *tp)
 {
     *tp = TilePlan{};
-    const int st = plan_tiled_common(p, p.elem, staged_om_dwords(p, p.elem), 0, 5, kTiledMaxLds, tp);
+    // offsets and masks go to registers, the LDS holds the value rows only
+    const int st = plan_tiled_common(p, p.elem, 0, 0, kForwardRmax, kTiledMaxLds, tp);
     if (st != DCNV4_OK)
         return st;
     tp->images_per_launch = (int)(kMaxBytesPerLaunch / image_bytes_max(p, false));

@@ -184,9 +184,7 @@ __device__ __forceinline__ void staging_done()
 // Offset/mask entries of group g for the tile's pixels, in dwords: pixel
 // q = py*tw + px owns om_dw dwords from dword q*om_dw, covering its 3K
 // entries from the dword that holds entry 0 (2-byte entries of odd groups
-// start one element into it).  Value rows of group g for the tile plus the
-// halo: region pixel (rr, cc) is image pixel (ry0 + rr, rx0 + cc) and starts
-// at 16-byte slot (rr*rw + cc)*ps; zeros outside the image.
+// start one element into it).
 // Per-lane byte offsets, within an image row of offset_mask (pixel stride
 // pix_bytes), of the slots of a tile row that holds `w` dwords per pixel from
 // byte `first` of each pixel: slot j = c*64 + lane is dword j % w of tile
@@ -210,21 +208,13 @@ __device__ __forceinline__ void pixel_row_offsets(const TArgs &a, const Tile &t,
     }
 }
 
-__device__ __forceinline__ void stage_tile(const TArgs &a, const Tile &t, char *om_s, char *val_s, int es)
+// Value rows of group g for the tile plus the halo: region pixel (rr, cc) is
+// image pixel (ry0 + rr, rx0 + cc) and starts at 16-byte slot
+// (rr*rw + cc)*ps; zeros outside the image.
+__device__ __forceinline__ void stage_values(const TArgs &a, const Tile &t, char *val_s, int es)
 {
     const Geom &geo = a.geo;
     const int lane = threadIdx.x & 63;
-    {
-        unsigned lo[kMaxRowChunks];
-        pixel_row_offsets(a, t, a.om_dw, a.om_dw_magic, (unsigned)(a.P * es),
-                          (unsigned)((t.g * 3 * a.K * es) & ~3), lo);
-        const unsigned row_bytes = (unsigned)(geo.Wo * a.P * es);
-        const int row0 = t.n * geo.Ho + t.oy0;
-        const int rows_in = geo.Ho - t.oy0;
-        stage_rows<4>(rsrc(a.om, a.om_bytes), om_s, a.th, a.tw * a.om_dw, lo, [&](int rr) {
-            return rr < rows_in ? (unsigned)(row0 + rr) * row_bytes : kOutOfRange;
-        });
-    }
     {
         unsigned lo[kMaxRowChunks];
         const int row_slots = a.rw * a.ps;
@@ -250,6 +240,107 @@ __device__ __forceinline__ void stage_tile(const TArgs &a, const Tile &t, char *
         });
     }
 }
+
+// Offset/mask rows (om_dw dwords per pixel, see pixel_row_offsets) and the
+// value rows of the tile.
+__device__ __forceinline__ void stage_tile(const TArgs &a, const Tile &t, char *om_s, char *val_s, int es)
+{
+    const Geom &geo = a.geo;
+    unsigned lo[kMaxRowChunks];
+    pixel_row_offsets(a, t, a.om_dw, a.om_dw_magic, (unsigned)(a.P * es), (unsigned)((t.g * 3 * a.K * es) & ~3), lo);
+    const unsigned row_bytes = (unsigned)(geo.Wo * a.P * es);
+    const int row0 = t.n * geo.Ho + t.oy0;
+    const int rows_in = geo.Ho - t.oy0;
+    stage_rows<4>(rsrc(a.om, a.om_bytes), om_s, a.th, a.tw * a.om_dw, lo, [&](int rr) {
+        return rr < rows_in ? (unsigned)(row0 + rr) * row_bytes : kOutOfRange;
+    });
+    stage_values(a, t, val_s, es);
+}
+
+// ---- offsets and masks in registers ------------------------------------------
+//
+// A pixel's group slice of offset_mask starts at the same element offset in
+// every pixel row, so its misalignment inside a 16-byte vector (mis) is the
+// same for the whole block.  A lane loads the aligned vectors that cover the
+// slice, and the shift is a register renaming chosen once per block (a
+// switch on mis) rather than per-lane arithmetic.
+
+template <typename T, int NVEC, int NOUT, int MIS>
+__device__ __forceinline__ void take_entries(const u32x4 (&v)[NVEC], float (&out)[NOUT])
+{
+    constexpr int EPV = 16 / (int)sizeof(T);
+    static_assert(MIS + NOUT <= EPV * NVEC, "vectors too short");
+    // keeps the cases of entries_at apart: merged, they would become one
+    // dynamically indexed array in scratch memory
+    asm volatile("; entries shifted by %0" ::"n"(MIS));
+    unsigned w[4 * NVEC];
+#pragma unroll
+    for (int i = 0; i < NVEC; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[4 * i + e] = v[i][e];
+#pragma unroll
+    for (int e = 0; e < NOUT; ++e) {
+        const int idx = e + MIS;
+        if constexpr (sizeof(T) == 4)
+            out[e] = __builtin_bit_cast(float, w[idx]);
+        else
+            out[e] = Store<T>::from_bits((idx & 1) ? w[idx >> 1] >> 16 : w[idx >> 1]);
+    }
+}
+
+template <typename T, int NVEC, int NOUT>
+__device__ __forceinline__ void entries_at(const u32x4 (&v)[NVEC], int mis, float (&out)[NOUT])
+{
+    switch (mis) {
+    case 0: take_entries<T, NVEC, NOUT, 0>(v, out); break;
+    case 1: take_entries<T, NVEC, NOUT, 1>(v, out); break;
+    case 2: take_entries<T, NVEC, NOUT, 2>(v, out); break;
+    case 3: take_entries<T, NVEC, NOUT, 3>(v, out); break;
+    default:
+        if constexpr (sizeof(T) == 2) {
+            switch (mis) {
+            case 4: take_entries<T, NVEC, NOUT, 4>(v, out); break;
+            case 5: take_entries<T, NVEC, NOUT, 5>(v, out); break;
+            case 6: take_entries<T, NVEC, NOUT, 6>(v, out); break;
+            default: take_entries<T, NVEC, NOUT, 7>(v, out); break;
+            }
+        }
+        break;
+    }
+}
+
+// Vectors covering a pixel's 2K offsets and K masks (group g, entries from
+// element g*3K of the pixel's row).
+template <typename T, int KMAX>
+struct OmVectors {
+    static constexpr int EPV = 16 / (int)sizeof(T);
+    static constexpr int NVO = (2 * KMAX + 2 * (EPV - 1)) / EPV;
+    static constexpr int NVM = (KMAX + 2 * (EPV - 1)) / EPV;
+    u32x4 o[NVO], m[NVM];
+    int mis_o, mis_m;
+
+    // pix: byte offset of the pixel's row, or kOutOfRange (zeros)
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, unsigned pix, int g, int K)
+    {
+        const int eo = g * 3 * K, em = eo + 2 * K;
+        mis_o = eo & (EPV - 1);
+        mis_m = em & (EPV - 1);
+        const unsigned bo = (unsigned)((eo - mis_o) * (int)sizeof(T)), bm = (unsigned)((em - mis_m) * (int)sizeof(T));
+#pragma unroll
+        for (int j = 0; j < NVO; ++j)
+            o[j] = load16(r, pix == kOutOfRange ? kOutOfRange : pix + bo + 16u * j);
+#pragma unroll
+        for (int j = 0; j < NVM; ++j)
+            m[j] = load16(r, pix == kOutOfRange ? kOutOfRange : pix + bm + 16u * j);
+    }
+
+    __device__ __forceinline__ void get(float (&offs)[2 * KMAX], float (&msk)[KMAX]) const
+    {
+        entries_at<T>(o, mis_o, offs);
+        entries_at<T>(m, mis_m, msk);
+    }
+};
 
 // Per-pixel constants of the near test and of LDS corner addresses.
 struct NearFrame {
@@ -334,7 +425,46 @@ __device__ __forceinline__ void softmax_stats(const T *m, int K, float &mx, floa
 
 // ---- forward ---------------------------------------------------------------
 
-template <typename T, int DP, bool SM>
+// Far sample of the forward: corners from global memory, corners outside
+// the image weighted 0 (the buffer range check zero-fills reads past the end).
+template <typename T, int DP>
+__device__ __forceinline__ void far_sample_fwd(const Geom &geo, __amdgpu_buffer_rsrc_t vr, int n, int chan_off,
+                                               const NearSample &s, float m, float (&acc)[DP])
+{
+    constexpr int es = (int)sizeof(T);
+    constexpr int NV = DP * es / 16;
+    Footprint f;
+    f.h0 = (int)s.fh;
+    f.w0 = (int)s.fw;
+    f.lh = s.lh - s.fh;
+    f.lw = s.lw - s.fw;
+    f.r0 = f.h0 >= 0;
+    f.r1 = f.h0 + 1 < geo.H;
+    f.c0 = f.w0 >= 0;
+    f.c1 = f.w0 + 1 < geo.W;
+    float w00, w01, w10, w11;
+    masked_weights(f, m, w00, w01, w10, w11);
+    const unsigned cs = (unsigned)(geo.C * es), rs = (unsigned)geo.W * cs;
+    u32x4 p00[NV], p01[NV], p10[NV], p11[NV];
+    far_corner_loads<NV>(vr, corner_offset(geo, n, f, es, chan_off), cs, rs, p00, p01, p10, p11);
+#pragma unroll
+    for (int c = 0; c < DP; ++c) {
+        float x = acc[c];
+        x = __builtin_fmaf(w00, Store<T>::get(p00, c), x);
+        x = __builtin_fmaf(w01, Store<T>::get(p01, c), x);
+        x = __builtin_fmaf(w10, Store<T>::get(p10, c), x);
+        x = __builtin_fmaf(w11, Store<T>::get(p11, c), x);
+        acc[c] = x;
+    }
+}
+
+// A block owns a th x tw output tile of one (image, group); `lanes` threads
+// per pixel, DP channels each.  The value rows of the tile plus a halo of R
+// pixels are staged in LDS while each lane loads its pixel's offsets and
+// masks into registers; the K samples are unrolled (KMAX >= K).  A far
+// sample (rare once R covers the offsets' spread) is taken on the spot from
+// global memory.
+template <typename T, int DP, int KMAX, bool SM>
 __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_fwd_tiled(TArgs a)
 {
     extern __shared__ u32x4 smem[];
@@ -342,124 +472,86 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_fwd_tiled(TArgs a)
     constexpr int NV = DP * es / 16;
     const Geom &geo = a.geo;
     const Tile t = out_tile(a);
-    char *om_s = reinterpret_cast<char *>(smem);
-    char *val_s = om_s + a.om_lds_bytes;
-    stage_tile(a, t, om_s, val_s, es);
-    staging_done();
+    char *val_s = reinterpret_cast<char *>(smem);
+    stage_values(a, t, val_s, es);
 
     const int q = threadIdx.x >> a.lanes_shift;
     const int chunk = threadIdx.x & ((1 << a.lanes_shift) - 1);
     const int py = (int)divm((unsigned)q, a.tw_magic);
     const int px = q - py * a.tw;
     const int oy = t.oy0 + py, ox = t.ox0 + px;
-    if (py >= a.th || oy >= geo.Ho || ox >= geo.Wo)
+    const bool valid = py < a.th && oy < geo.Ho && ox < geo.Wo;
+    OmVectors<T, KMAX> omv;
+    omv.load(rsrc(a.om, a.om_bytes),
+             valid ? (unsigned)((t.n * geo.Ho + oy) * geo.Wo + ox) * (unsigned)(a.P * es) : kOutOfRange, t.g, a.K);
+    staging_done();
+    if (!valid)
         return;   // no barrier follows
 
-    constexpr int epd = 4 / es;   // entries per staged dword
-    const T *om = reinterpret_cast<const T *>(om_s + q * a.om_dw * 4) + ((t.g * 3 * a.K) & (epd - 1));
+    float offs[2 * KMAX], msk[KMAX];
+    omv.get(offs, msk);
+    if (SM) {
+        float mx = msk[0];
+#pragma unroll
+        for (int k = 1; k < KMAX; ++k)
+            mx = k < a.K ? fmaxf(mx, msk[k]) : mx;
+        float sum = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            msk[k] = k < a.K ? expf(msk[k] - mx) : 0.0f;
+            sum += msk[k];
+        }
+        const float inv = 1.0f / sum;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            msk[k] *= inv;
+    }
     const NearFrame nf = near_frame(a, t, oy, ox);
     const char *vb = val_s + chunk * NV * 16;
-    float smx = 0.0f, sinv = 1.0f;
-    if (SM)
-        softmax_stats(om + 2 * a.K, a.K, smx, sinv);
+    const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
+    const int chan_off = (t.g * a.Cg + chunk * DP) * es;
 
     float acc[DP];
 #pragma unroll
     for (int c = 0; c < DP; ++c)
         acc[c] = 0.0f;
-
-    // the first far sample's corners are loaded as soon as it is found, so
-    // the loads overlap the rest of the near loop; later ones wait (rare)
-    const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
-    const int chan_off = (t.g * a.Cg + chunk * DP) * es;
-    const unsigned cs = (unsigned)(geo.C * es), rs = (unsigned)geo.W * cs;
-    unsigned farbits = 0;
-    int pk = -1;
-    u32x4 p00[NV], p01[NV], p10[NV], p11[NV];
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
-        p00[v] = p01[v] = p10[v] = p11[v] = u32x4{0u, 0u, 0u, 0u};
-    for (int k = 0; k < a.K; ++k) {
-        int gi, gj;
-        grid_point(geo, k, gi, gj);
-        const float dx = Store<T>::scalar(om[2 * k]);
-        const float dy = Store<T>::scalar(om[2 * k + 1]);
-        float m = Store<T>::scalar(om[2 * a.K + k]);
-        if (SM)
-            m = expf(m - smx) * sinv;
-        const float bh = nf.bh0 + (float)(gj * geo.dh), bw = nf.bw0 + (float)(gi * geo.dw);
-        const NearSample s = near_sample(nf, geo.scale, bh, bw, dx, dy);
-        if (!s.nr && live_loc(geo, s.lh, s.lw)) {
-            if (pk < 0) {
-                pk = k;
-                Footprint f;
-                f.h0 = (int)s.fh;
-                f.w0 = (int)s.fw;
-                far_corner_loads<NV>(vr, corner_offset(geo, t.n, f, es, chan_off), cs, rs, p00, p01, p10, p11);
-            } else {
-                farbits |= 1u << k;
+    for (int k = 0; k < KMAX; ++k) {
+        if (k < a.K) {
+            int gi, gj;
+            grid_point(geo, k, gi, gj);
+            const float m = msk[k];
+            const float bh = nf.bh0 + (float)(gj * geo.dh), bw = nf.bw0 + (float)(gi * geo.dw);
+            const NearSample s = near_sample(nf, geo.scale, bh, bw, offs[2 * k], offs[2 * k + 1]);
+            if (!s.nr && live_loc(geo, s.lh, s.lw))
+                far_sample_fwd<T, DP>(geo, vr, t.n, chan_off, s, m, acc);
+            // a sample that is not near gets zero weights (its reads hit slot 0)
+            const float ah = s.nr ? s.lh - s.fh : 0.0f, aw = s.nr ? s.lw - s.fw : 0.0f;
+            const float mm = s.nr ? m : 0.0f;
+            const float mh = __builtin_fmaf(-mm, ah, mm), ml = mm * ah;
+            const float w00 = __builtin_fmaf(-mh, aw, mh), w01 = mh * aw;
+            const float w10 = __builtin_fmaf(-ml, aw, ml), w11 = ml * aw;
+            const u32x4 *q00 = reinterpret_cast<const u32x4 *>(vb + s.addr);
+            const u32x4 *q01 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.colb);
+            const u32x4 *q10 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.rowb);
+            const u32x4 *q11 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.rowb + nf.colb);
+            u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                v00[v] = q00[v];
+                v01[v] = q01[v];
+                v10[v] = q10[v];
+                v11[v] = q11[v];
             }
-        }
-        // a sample that is not near gets zero weights (its reads hit slot 0)
-        const float ah = s.nr ? s.lh - s.fh : 0.0f, aw = s.nr ? s.lw - s.fw : 0.0f;
-        const float mm = s.nr ? m : 0.0f;
-        const float mh = __builtin_fmaf(-mm, ah, mm), ml = mm * ah;
-        const float w00 = __builtin_fmaf(-mh, aw, mh), w01 = mh * aw;
-        const float w10 = __builtin_fmaf(-ml, aw, ml), w11 = ml * aw;
-        const u32x4 *q00 = reinterpret_cast<const u32x4 *>(vb + s.addr);
-        const u32x4 *q01 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.colb);
-        const u32x4 *q10 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.rowb);
-        const u32x4 *q11 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.rowb + nf.colb);
-        u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            v00[v] = q00[v];
-            v01[v] = q01[v];
-            v10[v] = q10[v];
-            v11[v] = q11[v];
-        }
-#pragma unroll
-        for (int c = 0; c < DP; ++c) {
-            float x = acc[c];
-            x = __builtin_fmaf(w00, Store<T>::get(v00, c), x);
-            x = __builtin_fmaf(w01, Store<T>::get(v01, c), x);
-            x = __builtin_fmaf(w10, Store<T>::get(v10, c), x);
-            x = __builtin_fmaf(w11, Store<T>::get(v11, c), x);
-            acc[c] = x;
-        }
-    }
-
-    // far samples: corners outside the image get weight 0 (the buffer range
-    // check zero-fills reads past the end)
-    while (pk >= 0 || farbits) {
-        int k;
-        const bool pre = pk >= 0;
-        if (pre) {
-            k = pk;
-            pk = -1;
-        } else {
-            k = __builtin_ctz(farbits);
-            farbits &= farbits - 1;
-        }
-        const float dx = Store<T>::scalar(om[2 * k]);
-        const float dy = Store<T>::scalar(om[2 * k + 1]);
-        float m = Store<T>::scalar(om[2 * a.K + k]);
-        if (SM)
-            m = expf(m - smx) * sinv;
-        const Loc l = locate_lane(a, oy, ox, k, dx, dy);
-        const Footprint f = footprint(geo, l);
-        float w00, w01, w10, w11;
-        masked_weights(f, m, w00, w01, w10, w11);
-        if (!pre)
-            far_corner_loads<NV>(vr, corner_offset(geo, t.n, f, es, chan_off), cs, rs, p00, p01, p10, p11);
-#pragma unroll
-        for (int c = 0; c < DP; ++c) {
-            float x = acc[c];
-            x = __builtin_fmaf(w00, Store<T>::get(p00, c), x);
-            x = __builtin_fmaf(w01, Store<T>::get(p01, c), x);
-            x = __builtin_fmaf(w10, Store<T>::get(p10, c), x);
-            x = __builtin_fmaf(w11, Store<T>::get(p11, c), x);
-            acc[c] = x;
+            for (int c = 0; c < DP; ++c) {
+                float x = acc[c];
+                x = __builtin_fmaf(w00, Store<T>::get(v00, c), x);
+                x = __builtin_fmaf(w01, Store<T>::get(v01, c), x);
+                x = __builtin_fmaf(w10, Store<T>::get(v10, c), x);
+                x = __builtin_fmaf(w11, Store<T>::get(v11, c), x);
+                acc[c] = x;
+            }
         }
     }
 
@@ -1244,8 +1336,7 @@ TArgs make_targs(const Problem &p, const TilePlan &tp)
 bool out_tiles_ok(const Problem &p, const TilePlan &tp)
 {
     return tp.threads % 64 == 0 && tp.threads <= kMaxTileThreads && tp.threads >= tp.th * tp.tw * tp.lanes &&
-           tp.rw * tp.ps <= 64 * kMaxRowChunks && tp.tw * tp.om_dw <= 64 * kMaxRowChunks && p.K <= 32 &&
-           tp.om_dw >= 3 * p.K * p.elem / 4 &&
+           tp.rw * tp.ps <= 64 * kMaxRowChunks && tp.tw * tp.om_dw <= 64 * kMaxRowChunks && p.K <= 25 &&
            tp.ps >= tp.nvp && tp.om_lds_bytes % 16 == 0;
 }
 
@@ -1267,7 +1358,8 @@ hipError_t launch_forward_tiled(const Problem &p, const TilePlan &tp, const void
     const dim3 grid(blocks), block(tp.threads);
 #define DCNV4_FWD(T, D)                                                                              \
     do {                                                                                             \
-        void (*k_)(TArgs) = p.softmax ? dcnv4_fwd_tiled<T, D, true> : dcnv4_fwd_tiled<T, D, false>;  \
+        void (*k_)(TArgs) = p.K <= 9 ? (p.softmax ? dcnv4_fwd_tiled<T, D, 9, true> : dcnv4_fwd_tiled<T, D, 9, false>) \
+                                     : (p.softmax ? dcnv4_fwd_tiled<T, D, 25, true> : dcnv4_fwd_tiled<T, D, 25, false>); \
         const hipError_t e_ = allow_lds(reinterpret_cast<const void *>(k_), tp.lds_bytes);           \
         if (e_ != hipSuccess)                                                                        \
             return e_;                                                                               \
