@@ -214,6 +214,10 @@ constexpr int kMaxTiledK = 25;        // grid points of the tiled kernels
 #define DCNV4_FWD_RMAX 7
 #endif
 constexpr int kForwardRmax = DCNV4_FWD_RMAX;   // largest halo of the forward tiles
+#ifndef DCNV4_BWD_RMAX
+#define DCNV4_BWD_RMAX 7
+#endif
+constexpr int kBackwardRmax = DCNV4_BWD_RMAX;  // largest halo of the backward tiles (both kernels)
 constexpr int kTiledMaxLds = 80 * 1024;
 constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kTileThreads = 512;
@@ -221,20 +225,6 @@ constexpr int kCellTileLds = 78 * 1024;   // two cell-tile blocks per CU
 constexpr int kCellThreads = 512;         // threads of a cell-tile block: one per vertical pair of cells
 constexpr int kCellBinSlots = 2048;       // bin counters: (ch + 1) * (cw + 1) < 2048
 constexpr int kCellBinBytes = kCellBinSlots * 4 + (kCellThreads / 64) * 4;   // counters, scan scratch
-
-// Staged offset/mask dwords per pixel: a group's 3K entries, widened to whole
-// dwords (2-byte entries of odd groups start mid-dword).
-int staged_om_dwords(const Problem &p, int elem)
-{
-    return elem == 4 ? 3 * p.K : (3 * p.K + 2) / 2;
-}
-
-// LDS dwords per pixel of the backward's offset/mask rows: the staged
-// entries, plus 2K in softmax mode (fp32 probabilities and their gradients).
-int backward_om_dwords(const Problem &p)
-{
-    return staged_om_dwords(p, p.elem) + (p.softmax ? 2 * p.K : 0);
-}
 
 int region_rows(const Problem &p, int th, int R)
 {
@@ -248,12 +238,13 @@ int region_cols(const Problem &p, int tw, int R)
 
 // Output tile for halo radius R: th x tw pixels with `lanes` threads per
 // pixel, at most kTileThreads threads, staged rows (om_dw dwords per pixel)
-// and written-back rows (row_elems entries per pixel) within the row limit.
+// and written-back rows (row_elems entries per pixel) within the row limit;
+// the LDS also holds pixel_bytes per tile pixel at the end (0: nothing).
 // Modelled time: per block, a lane-sample costs ~40 instructions plus one
 // FMA per channel and corner, a staged region slot ~8; blocks run
 // concurrently until 24 waves share a CU (fewer when LDS limits them).
 bool choose_out_tile(const Problem &p, int lanes, int dp, int ps, int om_dw, int R, int lds_budget, int row_elems,
-                     int *th, int *tw)
+                     int pixel_bytes, int *th, int *tw)
 {
     double best = -1;
     for (int w = 1; w <= 64 && w <= p.Wo; ++w) {
@@ -265,7 +256,7 @@ bool choose_out_tile(const Problem &p, int lanes, int dp, int ps, int om_dw, int
                 break;
             const int rh = region_rows(p, h, R), rw = region_cols(p, w, R);
             const int om = (h * w * om_dw * 4 + 15) / 16 * 16;
-            const int lds = om + rh * rw * ps * 16;
+            const int lds = std::max(om + rh * rw * ps * 16, h * w * pixel_bytes);
             if (lds > lds_budget)
                 continue;
             const int waves = (threads + 63) / 64;
@@ -352,7 +343,7 @@ bool choose_cell_tile(const Problem &p, int R, int src_cap, int gps, int *ch, in
 }
 
 // Fill the LDS geometry for halo radius R; returns total LDS bytes.
-int tile_lds(const Problem &p, TilePlan *tp, int R, int om_dw)
+int tile_lds(const Problem &p, TilePlan *tp, int R, int om_dw, int pixel_bytes)
 {
     tp->R = R;
     tp->rh = region_rows(p, tp->th, R);
@@ -360,11 +351,12 @@ int tile_lds(const Problem &p, TilePlan *tp, int R, int om_dw)
     tp->om_dw = om_dw;
     const int om = tp->th * tp->tw * tp->om_dw * 4;
     tp->om_lds_bytes = (om + 15) / 16 * 16;
-    tp->lds_bytes = tp->om_lds_bytes + tp->rh * tp->rw * tp->ps * 16;
+    tp->lds_bytes = std::max(tp->om_lds_bytes + tp->rh * tp->rw * tp->ps * 16, tp->th * tp->tw * pixel_bytes);
     return tp->lds_bytes;
 }
 
-int plan_tiled_common(const Problem &p, int elem, int om_dw, int row_elems, int r_max, int lds_budget, TilePlan *tp)
+int plan_tiled_common(const Problem &p, int elem, int om_dw, int row_elems, int pixel_bytes, int r_max, int lds_budget,
+                      TilePlan *tp)
 {
     if ((p.Cg * elem) % 16 != 0 || p.K > kMaxTiledK)
         return DCNV4_ERR_UNSUPPORTED;
@@ -390,9 +382,9 @@ int plan_tiled_common(const Problem &p, int elem, int om_dw, int row_elems, int 
         return DCNV4_ERR_UNSUPPORTED;
     // the largest halo radius that has a tile within the LDS budget
     for (int R = r_max; R >= 1; --R) {
-        if (!choose_out_tile(p, tp->lanes, dp, tp->ps, om_dw, R, lds_budget, row_elems, &tp->th, &tp->tw))
+        if (!choose_out_tile(p, tp->lanes, dp, tp->ps, om_dw, R, lds_budget, row_elems, pixel_bytes, &tp->th, &tp->tw))
             continue;
-        tile_lds(p, tp, R, om_dw);
+        tile_lds(p, tp, R, om_dw, pixel_bytes);
         // whole waves: the staging loops take rows per wave
         tp->threads = (tp->th * tp->tw * tp->lanes + 63) / 64 * 64;
         tp->tiles_y = (p.Ho + tp->th - 1) / tp->th;
@@ -409,7 +401,7 @@ int plan_forward_tiled(const Problem &p, TilePlan *tp)
 {
     *tp = TilePlan{};
     // offsets and masks go to registers, the LDS holds the value rows only
-    const int st = plan_tiled_common(p, p.elem, 0, 0, kForwardRmax, kTiledMaxLds, tp);
+    const int st = plan_tiled_common(p, p.elem, 0, 0, 0, kForwardRmax, kTiledMaxLds, tp);
     if (st != DCNV4_OK)
         return st;
     tp->images_per_launch = (int)(kMaxBytesPerLaunch / image_bytes_max(p, false));
@@ -423,8 +415,12 @@ int plan_backward_tiled(const Problem &p, TilePlan *tp)
     const bool cg_ok = p.Cg == 8 || p.Cg == 16 || p.Cg == 32 || (p.Cg == 4 && p.elem == 4);
     if (!cg_ok)
         return DCNV4_ERR_UNSUPPORTED;
-    // the gradient write-back stores the 3K entries of a tile row slot by slot
-    int st = plan_tiled_common(p, p.elem, backward_om_dwords(p), 3 * p.K, 5, kTiledMaxLds, tp);
+    // offsets and masks go to registers; the gradient write-back stores the
+    // 3K entries of a tile row slot by slot from rows padded to the kernel's
+    // K bound (9 or 25) in whole 16-byte vectors, in the value rows' LDS
+    const int kmax = p.K <= 9 ? 9 : 25;
+    const int pixel_bytes = (3 * kmax * p.elem + 15) / 16 * 16;
+    int st = plan_tiled_common(p, p.elem, 0, 3 * p.K, pixel_bytes, kBackwardRmax, kTiledMaxLds, tp);
     if (st != DCNV4_OK)
         return st;
     // cell tiles for grad_value: LDS holds the bins, up to src_cap*K sorted

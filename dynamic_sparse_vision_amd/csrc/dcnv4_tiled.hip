@@ -579,172 +579,130 @@ __device__ __forceinline__ void sample_grads(float ah, float aw, float t00, floa
     gh = hw * (t10 - t00) + aw * (t11 - t01);
 }
 
-template <typename T, int DP, bool SM>
+// Sum of x over the `lanes` consecutive lanes of a pixel (1, 2, 4, ... 64;
+// uniform): DPP swaps inside quads, then lane swizzles.
+__device__ __forceinline__ float pixel_sum(float x, int lanes)
+{
+    if (lanes >= 2)
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+    if (lanes >= 4)
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+    for (int d = 4; d < lanes; d <<= 1)
+        x += __shfl_xor(x, d);
+    return x;
+}
+
+// A block owns a th x tw output tile of one (image, group), as in the
+// forward.  Per sample the dot products t_q = sum_c grad_out_c * v_q,c of the
+// four corners give d/dm and d/d(loc) (right derivative at integers), summed
+// over the pixel's lanes; the 3K gradients of a pixel stay in registers (the
+// samples are unrolled, KMAX >= K).  A far sample reads its corners from
+// global memory on the spot and adds its grad_value contributions with
+// device atomics, one 64-lane instruction per (sample, lane) taken by the
+// whole wave.  At the end the value rows are no longer needed and their LDS
+// holds the tile's gradient rows, which are written back row by row.
+template <typename T, int DP, int KMAX, bool SM>
 __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs a)
 {
     extern __shared__ u32x4 smem[];
     constexpr int es = (int)sizeof(T);
     constexpr int NV = DP * es / 16;
-    constexpr int epd = 4 / es;   // entries per staged dword
+    constexpr int EPV = 16 / es;
+    constexpr int ES = (3 * KMAX + EPV - 1) / EPV * EPV;   // LDS entries per pixel of the gradient rows
     const Geom &geo = a.geo;
     const Tile t = out_tile(a);
-    char *om_b = reinterpret_cast<char *>(smem);
-    char *val_s = om_b + a.om_lds_bytes;
-    stage_tile(a, t, om_b, val_s, es);
-    staging_done();
+    char *val_s = reinterpret_cast<char *>(smem);
+    stage_values(a, t, val_s, es);
 
-    const int K3 = 3 * a.K;
-    const int par = (t.g * K3) & (epd - 1);   // element of entry 0 inside its staged dword
     const int q = threadIdx.x >> a.lanes_shift;
     const int chunk = threadIdx.x & ((1 << a.lanes_shift) - 1);
     const int lanes = 1 << a.lanes_shift;
     const int py = (int)divm((unsigned)q, a.tw_magic);
     const int px = q - py * a.tw;
     const int oy = t.oy0 + py, ox = t.ox0 + px;
-    // every thread stays to the end (far samples are written by whole
-    // waves); threads past the tile or the image only take part in that
+    // every thread stays to the end (far samples are written by whole waves,
+    // and the gradient rows are written back by the block)
     const bool valid = py < a.th && oy < geo.Ho && ox < geo.Wo;
-    char *row = om_b + (valid ? q : 0) * a.om_dw * 4;
-    T *om = reinterpret_cast<T *>(row) + par;   // overwritten in place with the gradients
-    // softmax mode: the row's last 2K dwords hold p_k and dL/dp_k in fp32
-    // until the logit gradients are formed at the end
-    float *prob = reinterpret_cast<float *>(row) + (a.om_dw - 2 * a.K);
-    const NearFrame nf = near_frame(a, t, oy, ox);
+    const unsigned q_pix = (unsigned)((t.n * geo.Ho + oy) * geo.Wo + ox);
+    OmVectors<T, KMAX> omv;
+    omv.load(rsrc(a.om, a.om_bytes), valid ? q_pix * (unsigned)(a.P * es) : kOutOfRange, t.g, a.K);
     const int chan_off = (t.g * a.Cg + chunk * DP) * es;
-    const unsigned cs = (unsigned)(geo.C * es), rs = (unsigned)geo.W * cs;
-    const char *vb = val_s + chunk * NV * 16;
-    const unsigned pix_off = ((unsigned)((t.n * geo.Ho + oy) * geo.Wo + ox)) * cs + (unsigned)chan_off;
-    const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
-    float smx = 0.0f, sinv = 1.0f;
-    if (SM)
-        softmax_stats(om + 2 * a.K, a.K, smx, sinv);
-
     float go[DP];
     {
         const __amdgpu_buffer_rsrc_t gor = rsrc(a.gout, a.gout_bytes);
         u32x4 gv[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v)
-            gv[v] = load16(gor, valid ? pix_off + 16 * v : kOutOfRange);
+            gv[v] = load16(gor, valid ? q_pix * (unsigned)(geo.C * es) + (unsigned)chan_off + 16 * v : kOutOfRange);
 #pragma unroll
         for (int c = 0; c < DP; ++c)
             go[c] = Store<T>::get(gv, c);
-        // wait for grad_out here: inside the loop the compiler cannot tell
-        // these loads from the far-sample prefetch and would drain both
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     }
+    staging_done();
 
-    // the first far sample's corners are loaded as soon as it is found, so
-    // the loads overlap the rest of the near loop; later ones wait (rare)
-    unsigned farbits = 0;
-    int pk = -1;
-    u32x4 p00[NV], p01[NV], p10[NV], p11[NV];
+    float offs[2 * KMAX], msk[KMAX];
+    omv.get(offs, msk);
+    if (SM) {
+        // msk becomes the probabilities p_k
+        float mx = msk[0];
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
-        p00[v] = p01[v] = p10[v] = p11[v] = u32x4{0u, 0u, 0u, 0u};
-    for (int k = 0; k < a.K; ++k) {
-        int gi, gj;
-        grid_point(geo, k, gi, gj);
-        const float dx = Store<T>::scalar(om[2 * k]), dy = Store<T>::scalar(om[2 * k + 1]);
-        float m = Store<T>::scalar(om[2 * a.K + k]);
-        if (SM) {
-            m = expf(m - smx) * sinv;
-            if (valid && chunk == 0)
-                prob[k] = m;
+        for (int k = 1; k < KMAX; ++k)
+            mx = k < a.K ? fmaxf(mx, msk[k]) : mx;
+        float sum = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            msk[k] = k < a.K ? expf(msk[k] - mx) : 0.0f;
+            sum += msk[k];
         }
-        const float bh = nf.bh0 + (float)(gj * geo.dh), bw = nf.bw0 + (float)(gi * geo.dw);
-        const NearSample s = near_sample(nf, geo.scale, bh, bw, dx, dy);
-        const bool nr = s.nr && valid;
-        const int addr = nr ? s.addr : 0;
-        const bool far = valid && !s.nr && live_loc(geo, s.lh, s.lw);
-        if (far) {
-            if (pk < 0) {
-                pk = k;
+        const float inv = 1.0f / sum;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            msk[k] *= inv;
+    }
+    const NearFrame nf = near_frame(a, t, oy, ox);
+    const char *vb = val_s + chunk * NV * 16;
+    const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
+    const unsigned cs = (unsigned)(geo.C * es), rs = (unsigned)geo.W * cs;
+    // far samples' grad_value: this lane's part of one atomic instruction
+    // (fp32 for every storage dtype): corner lane / DP, channel lane % DP
+    const __amdgpu_buffer_rsrc_t gr = rsrc(a.gvalue, a.gvalue_bytes);
+    const int lane = threadIdx.x & 63;
+    const int my_corner = lane / DP, my_c = lane % DP;
+    const unsigned gcs = (unsigned)(geo.C * 4), grs = (unsigned)geo.W * gcs;
+    const unsigned my_corner_off = (unsigned)(my_corner & 1) * gcs + (unsigned)(my_corner >> 1) * grs + 4u * (unsigned)my_c;
+
+    // gradients: d/d(dx_k), d/d(dy_k), d/dm_k (d/dp_k in softmax mode until the end)
+    float gx[KMAX], gy[KMAX], gmk[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        gx[k] = gy[k] = gmk[k] = 0.0f;
+        if (k < a.K) {
+            int gi, gj;
+            grid_point(geo, k, gi, gj);
+            const float m = msk[k];
+            const float bh = nf.bh0 + (float)(gj * geo.dh), bw = nf.bw0 + (float)(gi * geo.dw);
+            const NearSample s = near_sample(nf, geo.scale, bh, bw, offs[2 * k], offs[2 * k + 1]);
+            const bool nr = s.nr && valid;
+            const bool far = valid && !s.nr && live_loc(geo, s.lh, s.lw);
+            float t00 = 0.0f, t01 = 0.0f, t10 = 0.0f, t11 = 0.0f;
+            unsigned foff = 0;
+            float w00 = 0.0f, w01 = 0.0f, w10 = 0.0f, w11 = 0.0f;
+            const float ah = s.lh - s.fh, aw = s.lw - s.fw;
+            if (far) {
+                // corners from global memory; corners outside the image give
+                // zero dot products (zero-extended image)
                 Footprint f;
                 f.h0 = (int)s.fh;
                 f.w0 = (int)s.fw;
-                far_corner_loads<NV>(vr, corner_offset(geo, t.n, f, es, chan_off), cs, rs, p00, p01, p10, p11);
-            } else {
-                farbits |= 1u << k;
-            }
-        }
-        const u32x4 *q00 = reinterpret_cast<const u32x4 *>(vb + addr);
-        const u32x4 *q01 = reinterpret_cast<const u32x4 *>(vb + addr + nf.colb);
-        const u32x4 *q10 = reinterpret_cast<const u32x4 *>(vb + addr + nf.rowb);
-        const u32x4 *q11 = reinterpret_cast<const u32x4 *>(vb + addr + nf.rowb + nf.colb);
-        u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            v00[v] = q00[v];
-            v01[v] = q01[v];
-            v10[v] = q10[v];
-            v11[v] = q11[v];
-        }
-        float t00 = 0.0f, t01 = 0.0f, t10 = 0.0f, t11 = 0.0f;
-#pragma unroll
-        for (int c = 0; c < DP; ++c) {
-            t00 = __builtin_fmaf(go[c], Store<T>::get(v00, c), t00);
-            t01 = __builtin_fmaf(go[c], Store<T>::get(v01, c), t01);
-            t10 = __builtin_fmaf(go[c], Store<T>::get(v10, c), t10);
-            t11 = __builtin_fmaf(go[c], Store<T>::get(v11, c), t11);
-        }
-        float gm, gw, gh;
-        sample_grads(s.lh - s.fh, s.lw - s.fw, t00, t01, t10, t11, gm, gw, gh);
-        gm = nr ? gm : 0.0f;
-        gw = nr ? gw : 0.0f;
-        gh = nr ? gh : 0.0f;
-        for (int d = 1; d < lanes; d <<= 1) {
-            gm += __shfl_xor(gm, d);
-            gw += __shfl_xor(gw, d);
-            gh += __shfl_xor(gh, d);
-        }
-        if (valid && chunk == 0 && !far) {
-            // the lanes of this pixel have read entry k already; far entries
-            // are still needed by the loop below.  In softmax mode the mask
-            // slot holds dL/dp_k in fp32 until the final pass (kept exact).
-            const float sm = geo.scale * m;
-            om[2 * k] = Store<T>::make(sm * gw);
-            om[2 * k + 1] = Store<T>::make(sm * gh);
-            if (SM)
-                prob[a.K + k] = gm;
-            else
-                om[2 * a.K + k] = Store<T>::make(gm);
-        }
-    }
-
-    // far samples, one per lane and iteration (the prefetched one first); the
-    // whole wave stays in the loop for the grad_value atomics
-    {
-        const __amdgpu_buffer_rsrc_t gr = rsrc(a.gvalue, a.gvalue_bytes);
-        // this lane's part of a far sample's grad_value update (fp32 for
-        // every storage dtype): corner lane / DP, channel lane % DP
-        const int lane = threadIdx.x & 63;
-        const int my_corner = lane / DP, my_c = lane % DP;
-        const unsigned gcs = (unsigned)(geo.C * 4), grs = (unsigned)geo.W * gcs;
-        const unsigned my_corner_off = (unsigned)(my_corner & 1) * gcs + (unsigned)(my_corner >> 1) * grs + 4u * (unsigned)my_c;
-        while (__ballot(pk >= 0 || farbits != 0)) {
-            const bool has = pk >= 0 || farbits != 0;
-            int k = 0;
-            float gm = 0.0f, gw = 0.0f, gh = 0.0f, m = 0.0f;
-            unsigned off = 0;
-            float w00 = 0.0f, w01 = 0.0f, w10 = 0.0f, w11 = 0.0f;
-            if (has) {
-                const bool pre = pk >= 0;
-                if (pre) {
-                    k = pk;
-                    pk = -1;
-                } else {
-                    k = __builtin_ctz(farbits);
-                    farbits &= farbits - 1;
-                }
-                const float dx = Store<T>::scalar(om[2 * k]), dy = Store<T>::scalar(om[2 * k + 1]);
-                m = SM ? prob[k] : Store<T>::scalar(om[2 * a.K + k]);
-                const Loc l = locate_lane(a, oy, ox, k, dx, dy);
-                const Footprint f = footprint(geo, l);
-                off = corner_offset(geo, t.n, f, es, chan_off);
-                if (!pre)
-                    far_corner_loads<NV>(vr, off, cs, rs, p00, p01, p10, p11);
-                float t00 = 0.0f, t01 = 0.0f, t10 = 0.0f, t11 = 0.0f;
+                f.lh = ah;
+                f.lw = aw;
+                f.r0 = f.h0 >= 0;
+                f.r1 = f.h0 + 1 < geo.H;
+                f.c0 = f.w0 >= 0;
+                f.c1 = f.w0 + 1 < geo.W;
+                foff = corner_offset(geo, t.n, f, es, chan_off);
+                u32x4 p00[NV], p01[NV], p10[NV], p11[NV];
+                far_corner_loads<NV>(vr, foff, cs, rs, p00, p01, p10, p11);
 #pragma unroll
                 for (int c = 0; c < DP; ++c) {
                     t00 = __builtin_fmaf(go[c], Store<T>::get(p00, c), t00);
@@ -752,38 +710,53 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
                     t10 = __builtin_fmaf(go[c], Store<T>::get(p10, c), t10);
                     t11 = __builtin_fmaf(go[c], Store<T>::get(p11, c), t11);
                 }
-                // zero-extended image: dots of corners outside are 0
                 t00 = (f.r0 && f.c0) ? t00 : 0.0f;
                 t01 = (f.r0 && f.c1) ? t01 : 0.0f;
                 t10 = (f.r1 && f.c0) ? t10 : 0.0f;
                 t11 = (f.r1 && f.c1) ? t11 : 0.0f;
-                sample_grads(f.lh, f.lw, t00, t01, t10, t11, gm, gw, gh);
                 masked_weights(f, m, w00, w01, w10, w11);
+            } else {
+                // not near (or no pixel): reads of slot 0, weighted 0 below
+                const int addr = nr ? s.addr : 0;
+                const u32x4 *q00 = reinterpret_cast<const u32x4 *>(vb + addr);
+                const u32x4 *q01 = reinterpret_cast<const u32x4 *>(vb + addr + nf.colb);
+                const u32x4 *q10 = reinterpret_cast<const u32x4 *>(vb + addr + nf.rowb);
+                const u32x4 *q11 = reinterpret_cast<const u32x4 *>(vb + addr + nf.rowb + nf.colb);
+                u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
+#pragma unroll
+                for (int v = 0; v < NV; ++v) {
+                    v00[v] = q00[v];
+                    v01[v] = q01[v];
+                    v10[v] = q10[v];
+                    v11[v] = q11[v];
+                }
+#pragma unroll
+                for (int c = 0; c < DP; ++c) {
+                    t00 = __builtin_fmaf(go[c], Store<T>::get(v00, c), t00);
+                    t01 = __builtin_fmaf(go[c], Store<T>::get(v01, c), t01);
+                    t10 = __builtin_fmaf(go[c], Store<T>::get(v10, c), t10);
+                    t11 = __builtin_fmaf(go[c], Store<T>::get(v11, c), t11);
+                }
             }
-            for (int d = 1; d < lanes; d <<= 1) {
-                gm += __shfl_xor(gm, d);
-                gw += __shfl_xor(gw, d);
-                gh += __shfl_xor(gh, d);
-            }
-            if (has && chunk == 0) {
-                const float sm = geo.scale * m;
-                om[2 * k] = Store<T>::make(sm * gw);
-                om[2 * k + 1] = Store<T>::make(sm * gh);
-                if (SM)
-                    prob[a.K + k] = gm;
-                else
-                    om[2 * a.K + k] = Store<T>::make(gm);
-            }
-            // grad_value: one device atomic per corner and channel (pair),
-            // issued by the whole wave for one (sample, lane) at a time so
-            // that each instruction covers four contiguous corner rows
-            unsigned long long fm = __ballot(has);
+            float gm, gw, gh;
+            sample_grads(ah, aw, t00, t01, t10, t11, gm, gw, gh);
+            const bool use = nr || far;
+            gm = pixel_sum(use ? gm : 0.0f, lanes);
+            gw = pixel_sum(use ? gw : 0.0f, lanes);
+            gh = pixel_sum(use ? gh : 0.0f, lanes);
+            const float sm = geo.scale * m;
+            gx[k] = sm * gw;
+            gy[k] = sm * gh;
+            gmk[k] = gm;
+            // grad_value of far samples: the whole wave issues one atomic per
+            // (sample, lane), each covering four contiguous corner rows
+            unsigned long long fm = __ballot(far);
             while (fm) {
                 const int src = __builtin_ctzll(fm);
                 fm &= fm - 1;
                 // byte offset of the corner in grad_value (fp32) from the
                 // value offset (storage dtype; corner_offset wraps consistently)
-                const unsigned so = (unsigned)__builtin_amdgcn_readlane((int)off, src) * (4u / (unsigned)es);
+                const unsigned so = (unsigned)__builtin_amdgcn_readlane((int)foff, src) * (4u / (unsigned)es);
                 const float s00 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w00), src));
                 const float s01 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w01), src));
                 const float s10 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w10), src));
@@ -801,14 +774,45 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
             }
         }
     }
-    if (SM && valid && chunk == 0) {
+    if (SM) {
         // gradients with respect to the logits: p_k * (g_k - sum_j p_j g_j),
         // with g_k = dL/dp_k
         float sdot = 0.0f;
-        for (int k = 0; k < a.K; ++k)
-            sdot = __builtin_fmaf(prob[k], prob[a.K + k], sdot);
-        for (int k = 0; k < a.K; ++k)
-            om[2 * a.K + k] = Store<T>::make(prob[k] * (prob[a.K + k] - sdot));
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            sdot = k < a.K ? __builtin_fmaf(msk[k], gmk[k], sdot) : sdot;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            gmk[k] = msk[k] * (gmk[k] - sdot);
+    }
+    __syncthreads();   // the value rows are no longer read
+
+    // the tile's gradient rows: pixel q's entries from element q*ES, in the
+    // offset_mask layout of its group (2K offsets, then K masks)
+    if (valid && chunk == 0) {
+        // the 2K offsets as whole vectors (entries past 2K are overwritten
+        // by the masks below), then the K masks one by one from entry 2K
+        constexpr int NVX = (2 * KMAX + EPV - 1) / EPV;
+        float xy[NVX * EPV];
+#pragma unroll
+        for (int i = 0; i < NVX * EPV; ++i)
+            xy[i] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            xy[2 * k] = gx[k];
+            xy[2 * k + 1] = gy[k];
+        }
+        u32x4 xv[NVX];
+        Store<T>::pack(xy, xv, NVX);
+        char *row = val_s + (size_t)q * ES * es;
+#pragma unroll
+        for (int v = 0; v < NVX; ++v)
+            reinterpret_cast<u32x4 *>(row)[v] = xv[v];
+        T *mrow = reinterpret_cast<T *>(row) + 2 * a.K;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            if (k < a.K)
+                mrow[k] = Store<T>::make(gmk[k]);
     }
     __syncthreads();
 
@@ -816,12 +820,12 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
     // element (2-byte entries of neighbouring groups may share a dword);
     // group 0 also zeroes the padding channels
     {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+        const int wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
         const __amdgpu_buffer_rsrc_t r = rsrc(a.gom, a.om_bytes);
         const unsigned row_bytes = (unsigned)(geo.Wo * a.P * es);
         const int row0 = t.n * geo.Ho + t.oy0;
         const int rows = min(a.th, geo.Ho - t.oy0);
-        const int row_elems = a.om_dw * epd;   // LDS elements per pixel row
+        const int K3 = 3 * a.K;
         {
             // slot j of a row: entry j % 3K of tile column j / 3K
             unsigned lo[kMaxRowChunks];
@@ -833,12 +837,12 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
                 const int px2 = (int)divm((unsigned)j, a.k3_magic);
                 const int d = j - px2 * K3;
                 const int ox2 = t.ox0 + px2;
-                li[c] = px2 * row_elems + par + d;
+                li[c] = px2 * ES + d;
                 lo[c] = (px2 < a.tw && ox2 < geo.Wo) ? (unsigned)((ox2 * a.P + t.g * K3 + d) * es) : kOutOfRange;
             }
             for (int rr = wave; rr < rows; rr += nwaves) {
                 const unsigned base = (unsigned)(row0 + rr) * row_bytes;
-                const T *src = reinterpret_cast<const T *>(om_b + rr * a.tw * a.om_dw * 4);
+                const T *src = reinterpret_cast<const T *>(val_s + (size_t)rr * a.tw * ES * es);
 #pragma unroll
                 for (int c = 0; c < kMaxRowChunks; ++c) {
                     if (c * 64 < row_slots && c * 64 + lane < row_slots && lo[c] != kOutOfRange) {
@@ -1426,18 +1430,26 @@ Kernel values_kernel_for(int Cg, bool small_k, bool sm)
     }
 }
 
+template <typename T, int DP>
+Kernel offsets_kernel(bool small_k, bool sm)
+{
+    if (small_k)
+        return sm ? dcnv4_bwd_offsets_tiled<T, DP, 9, true> : dcnv4_bwd_offsets_tiled<T, DP, 9, false>;
+    return sm ? dcnv4_bwd_offsets_tiled<T, DP, 25, true> : dcnv4_bwd_offsets_tiled<T, DP, 25, false>;
+}
+
 template <typename T>
-Kernel offsets_kernel_for(int dp, bool sm)
+Kernel offsets_kernel_for(int dp, bool small_k, bool sm)
 {
     switch (dp) {
     case 4:
         if constexpr (sizeof(T) == 4)
-            return sm ? dcnv4_bwd_offsets_tiled<T, 4, true> : dcnv4_bwd_offsets_tiled<T, 4, false>;
+            return offsets_kernel<T, 4>(small_k, sm);
         return nullptr;
     case 8:
-        return sm ? dcnv4_bwd_offsets_tiled<T, 8, true> : dcnv4_bwd_offsets_tiled<T, 8, false>;
+        return offsets_kernel<T, 8>(small_k, sm);
     case 16:
-        return sm ? dcnv4_bwd_offsets_tiled<T, 16, true> : dcnv4_bwd_offsets_tiled<T, 16, false>;
+        return offsets_kernel<T, 16>(small_k, sm);
     default:
         return nullptr;
     }
@@ -1460,7 +1472,9 @@ hipError_t launch_backward_tiled(const Problem &p, const TilePlan &tp, const voi
         // source window width: within a batch and within a staged row
         (tp.cw + 2 * tp.R + (p.kw - 1) * p.dw + 1) / p.sw + 2 > tp.src_cap ||
         ((tp.cw + 2 * tp.R + (p.kw - 1) * p.dw + 1) / p.sw + 2) * tp.gps > 64 * kMaxRowChunks ||
-        tp.om_dw < (3 * p.K * es + 3) / 4 + (p.softmax ? 2 * p.K : 0))
+        // the gradient rows of the tile (padded to whole 16-byte vectors per
+        // pixel) reuse the value rows' LDS
+        tp.th * tp.tw * ((3 * (p.K <= 9 ? 9 : 25) * es + 15) / 16 * 16) > tp.lds_bytes)
         return hipErrorInvalidConfiguration;
     TArgs a = make_targs(p, tp);
     a.value = value;
@@ -1476,13 +1490,13 @@ hipError_t launch_backward_tiled(const Problem &p, const TilePlan &tp, const voi
     Kernel values = nullptr, offsets = nullptr;
     if (p.dtype == 0) {
         values = values_kernel_for<float>(p.Cg, small_k, sm);
-        offsets = offsets_kernel_for<float>(tp.dp, sm);
+        offsets = offsets_kernel_for<float>(tp.dp, small_k, sm);
     } else if (p.dtype == 1) {
         values = values_kernel_for<_Float16>(p.Cg, small_k, sm);
-        offsets = offsets_kernel_for<_Float16>(tp.dp, sm);
+        offsets = offsets_kernel_for<_Float16>(tp.dp, small_k, sm);
     } else if (p.dtype == 2) {
         values = values_kernel_for<bf16_t>(p.Cg, small_k, sm);
-        offsets = offsets_kernel_for<bf16_t>(tp.dp, sm);
+        offsets = offsets_kernel_for<bf16_t>(tp.dp, small_k, sm);
     }
     if (!values || !offsets)
         return hipErrorInvalidValue;
