@@ -10,6 +10,8 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 namespace dcnv4 {
 namespace {
@@ -237,26 +239,25 @@ int region_cols(const Problem &p, int tw, int R)
 }
 
 // Output tile for halo radius R: th x tw pixels with `lanes` threads per
-// pixel, at most kTileThreads threads, staged rows (om_dw dwords per pixel)
-// and written-back rows (row_elems entries per pixel) within the row limit;
-// the LDS also holds pixel_bytes per tile pixel at the end (0: nothing).
+// pixel, at most kTileThreads threads, staged value rows and written-back
+// rows (row_elems entries per pixel) within the row limit; the LDS also
+// holds pixel_bytes per tile pixel at the end (0: nothing).
 // Modelled time: per block, a lane-sample costs ~40 instructions plus one
 // FMA per channel and corner, a staged region slot ~8; blocks run
 // concurrently until 24 waves share a CU (fewer when LDS limits them).
-bool choose_out_tile(const Problem &p, int lanes, int dp, int ps, int om_dw, int R, int lds_budget, int row_elems,
+bool choose_out_tile(const Problem &p, int lanes, int dp, int ps, int R, int lds_budget, int row_elems,
                      int pixel_bytes, int *th, int *tw)
 {
     double best = -1;
     for (int w = 1; w <= 64 && w <= p.Wo; ++w) {
-        if (w * om_dw > kRowSlots || w * row_elems > kRowSlots || region_cols(p, w, R) * ps > kRowSlots)
+        if (w * row_elems > kRowSlots || region_cols(p, w, R) * ps > kRowSlots)
             break;
         for (int h = 1; h <= 64 && h <= p.Ho; ++h) {
             const int threads = h * w * lanes;
             if (threads > kTileThreads)
                 break;
             const int rh = region_rows(p, h, R), rw = region_cols(p, w, R);
-            const int om = (h * w * om_dw * 4 + 15) / 16 * 16;
-            const int lds = std::max(om + rh * rw * ps * 16, h * w * pixel_bytes);
+            const int lds = std::max(rh * rw * ps * 16, h * w * pixel_bytes);
             if (lds > lds_budget)
                 continue;
             const int waves = (threads + 63) / 64;
@@ -313,14 +314,30 @@ bool choose_cell_tile(const Problem &p, int R, int src_cap, int gps, int *ch, in
             if ((h / 2) * w > kCellThreads || (h + 1) * (w + 1) >= kCellBinSlots)
                 break;
             const int pair_waves = ((h / 2) * w + 63) / 64;
+            // tiles along each axis, grouped by source window size
+            std::vector<std::pair<int, int>> rows, cols;   // (window size, tiles)
+            auto windows = [&](int len, int size, int pad, int kern, int dil, int stride, int out,
+                               std::vector<std::pair<int, int>> &acc) {
+                for (int c0 = 0; c0 < size; c0 += len) {
+                    int s0, s1;
+                    source_range(c0, len, R, pad, kern, dil, stride, out, &s0, &s1);
+                    const int n = std::max(0, s1 - s0);
+                    bool found = false;
+                    for (auto &e : acc)
+                        if (e.first == n) {
+                            ++e.second;
+                            found = true;
+                        }
+                    if (!found)
+                        acc.emplace_back(n, 1);
+                }
+            };
+            windows(h, p.H, p.ph, p.kh, p.dh, p.sh, p.Ho, rows);
+            windows(w, p.W, p.pw, p.kw, p.dw, p.sw, p.Wo, cols);
             double cost = 0;
-            for (int y0 = 0; y0 < p.H; y0 += h) {
-                int r0, r1;
-                source_range(y0, h, R, p.ph, p.kh, p.dh, p.sh, p.Ho, &r0, &r1);
-                for (int x0 = 0; x0 < p.W; x0 += w) {
-                    int c0, c1;
-                    source_range(x0, w, R, p.pw, p.kw, p.dw, p.sw, p.Wo, &c0, &c1);
-                    const int sh = std::max(0, r1 - r0), sw = std::max(0, c1 - c0);
+            for (const auto &ry : rows) {
+                for (const auto &cx : cols) {
+                    const int sh = ry.first, sw = cx.first;
                     double blk = 400.0 + pair_waves * 90.0 * 4 * p.K;
                     if (sw > 0) {
                         const int br = std::max(1, src_cap / sw);
@@ -329,7 +346,7 @@ bool choose_cell_tile(const Problem &p, int R, int src_cap, int gps, int *ch, in
                             blk += 800.0 + ((nsrc + 63) / 64) * (40.0 * p.K + 60.0);
                         }
                     }
-                    cost += blk;
+                    cost += blk * ry.second * cx.second;
                 }
             }
             if (best < 0 || cost < best) {
@@ -343,20 +360,16 @@ bool choose_cell_tile(const Problem &p, int R, int src_cap, int gps, int *ch, in
 }
 
 // Fill the LDS geometry for halo radius R; returns total LDS bytes.
-int tile_lds(const Problem &p, TilePlan *tp, int R, int om_dw, int pixel_bytes)
+int tile_lds(const Problem &p, TilePlan *tp, int R, int pixel_bytes)
 {
     tp->R = R;
     tp->rh = region_rows(p, tp->th, R);
     tp->rw = region_cols(p, tp->tw, R);
-    tp->om_dw = om_dw;
-    const int om = tp->th * tp->tw * tp->om_dw * 4;
-    tp->om_lds_bytes = (om + 15) / 16 * 16;
-    tp->lds_bytes = std::max(tp->om_lds_bytes + tp->rh * tp->rw * tp->ps * 16, tp->th * tp->tw * pixel_bytes);
+    tp->lds_bytes = std::max(tp->rh * tp->rw * tp->ps * 16, tp->th * tp->tw * pixel_bytes);
     return tp->lds_bytes;
 }
 
-int plan_tiled_common(const Problem &p, int elem, int om_dw, int row_elems, int pixel_bytes, int r_max, int lds_budget,
-                      TilePlan *tp)
+int plan_tiled_common(const Problem &p, int elem, int row_elems, int pixel_bytes, int r_max, int lds_budget, TilePlan *tp)
 {
     if ((p.Cg * elem) % 16 != 0 || p.K > kMaxTiledK)
         return DCNV4_ERR_UNSUPPORTED;
@@ -382,9 +395,9 @@ int plan_tiled_common(const Problem &p, int elem, int om_dw, int row_elems, int 
         return DCNV4_ERR_UNSUPPORTED;
     // the largest halo radius that has a tile within the LDS budget
     for (int R = r_max; R >= 1; --R) {
-        if (!choose_out_tile(p, tp->lanes, dp, tp->ps, om_dw, R, lds_budget, row_elems, pixel_bytes, &tp->th, &tp->tw))
+        if (!choose_out_tile(p, tp->lanes, dp, tp->ps, R, lds_budget, row_elems, pixel_bytes, &tp->th, &tp->tw))
             continue;
-        tile_lds(p, tp, R, om_dw, pixel_bytes);
+        tile_lds(p, tp, R, pixel_bytes);
         // whole waves: the staging loops take rows per wave
         tp->threads = (tp->th * tp->tw * tp->lanes + 63) / 64 * 64;
         tp->tiles_y = (p.Ho + tp->th - 1) / tp->th;
@@ -395,20 +408,18 @@ int plan_tiled_common(const Problem &p, int elem, int om_dw, int row_elems, int 
     return DCNV4_ERR_UNSUPPORTED;
 }
 
-}  // namespace
-
-int plan_forward_tiled(const Problem &p, TilePlan *tp)
+int compute_forward_tiled(const Problem &p, TilePlan *tp)
 {
     *tp = TilePlan{};
     // offsets and masks go to registers, the LDS holds the value rows only
-    const int st = plan_tiled_common(p, p.elem, 0, 0, 0, kForwardRmax, kTiledMaxLds, tp);
+    const int st = plan_tiled_common(p, p.elem, 0, 0, kForwardRmax, kTiledMaxLds, tp);
     if (st != DCNV4_OK)
         return st;
     tp->images_per_launch = (int)(kMaxBytesPerLaunch / image_bytes_max(p, false));
     return DCNV4_OK;
 }
 
-int plan_backward_tiled(const Problem &p, TilePlan *tp)
+int compute_backward_tiled(const Problem &p, TilePlan *tp)
 {
     *tp = TilePlan{};
     // grad_value cell tiles are instantiated for these channel counts
@@ -420,7 +431,7 @@ int plan_backward_tiled(const Problem &p, TilePlan *tp)
     // K bound (9 or 25) in whole 16-byte vectors, in the value rows' LDS
     const int kmax = p.K <= 9 ? 9 : 25;
     const int pixel_bytes = (3 * kmax * p.elem + 15) / 16 * 16;
-    int st = plan_tiled_common(p, p.elem, 0, 3 * p.K, pixel_bytes, kBackwardRmax, kTiledMaxLds, tp);
+    int st = plan_tiled_common(p, p.elem, 3 * p.K, pixel_bytes, kBackwardRmax, kTiledMaxLds, tp);
     if (st != DCNV4_OK)
         return st;
     // cell tiles for grad_value: LDS holds the bins, up to src_cap*K sorted
@@ -438,6 +449,60 @@ int plan_backward_tiled(const Problem &p, TilePlan *tp)
     tp->ctiles_x = (p.W + tp->cw - 1) / tp->cw;
     tp->images_per_launch = (int)(kMaxBytesPerLaunch / image_bytes_max(p, true));
     return DCNV4_OK;
+}
+
+// Tile plans depend on the call's geometry only and their search costs up to
+// milliseconds on large images, so each distinct geometry is planned once
+// and kept (a small cache, oldest entry replaced when full).
+class PlanCache {
+public:
+    int get(const Problem &p, TilePlan *tp, int (*compute)(const Problem &, TilePlan *))
+    {
+        {
+            std::lock_guard<std::mutex> lock(mu_);
+            for (const Entry &e : entries_) {
+                if (std::memcmp(&e.p, &p, sizeof p) == 0) {
+                    *tp = e.plan;
+                    return e.status;
+                }
+            }
+        }
+        const int st = compute(p, tp);
+        std::lock_guard<std::mutex> lock(mu_);
+        const Entry e{p, st, *tp};
+        if (entries_.size() < kEntries) {
+            entries_.push_back(e);
+        } else {
+            entries_[next_] = e;
+            next_ = (next_ + 1) % kEntries;
+        }
+        return st;
+    }
+
+private:
+    static constexpr size_t kEntries = 64;
+    struct Entry {
+        Problem p;
+        int status;
+        TilePlan plan;
+    };
+    std::mutex mu_;
+    std::vector<Entry> entries_;
+    size_t next_ = 0;
+};
+
+}  // namespace
+
+int plan_forward_tiled(const Problem &p, TilePlan *tp)
+{
+    static PlanCache cache;
+    return cache.get(p, tp, compute_forward_tiled);
+}
+
+int plan_backward_tiled(const Problem &p, TilePlan *tp)
+{
+    static PlanCache cache;
+    return cache.get(p, tp, compute_backward_tiled);
 }
 
 }  // namespace dcnv4

@@ -52,10 +52,8 @@ struct TilePlan {
     int rh, rw;          // LDS value region, pixels
     int nvp;             // 16-byte vectors per region pixel (Cg * elem / 16)
     int ps;              // LDS pixel stride, 16-byte slots (nvp rounded up to odd)
-    int om_dw;           // LDS dwords per pixel of the offset/mask rows (staged entries, + K
-                         // softmax probabilities in the backward's softmax mode)
-    int om_lds_bytes;    // LDS for the staged offset/mask entries (16-byte multiple)
-    int lds_bytes;       // total LDS of an output-tile block
+    int lds_bytes;       // total LDS of an output-tile block (value rows; the backward's
+                         // gradient rows reuse it at the end)
     // cell tiles (backward grad_value): ch x cw input cells of one (image, group)
     int ch, cw;
     int ctiles_y, ctiles_x;

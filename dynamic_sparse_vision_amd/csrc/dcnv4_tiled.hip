@@ -18,9 +18,10 @@
 // A sample is "near" when its integer displacement is within R pixels on
 // both axes (|floor(loc) - grid position| <= R); its four corners then lie in
 // the staged region, so it needs no bounds test at all (corners outside the
-// image read the staged zeros).  Other samples are "far": the main loop only
-// records them in a bit mask and a second loop reads their corners from
-// global memory, so the near loop never waits on global loads.
+// image read the staged zeros).  Other samples are "far" and read their
+// corners from global memory where they occur; with R = 7 and offsets of a
+// few pixels they are rare.  The R the LDS allows is set by the value rows
+// alone: each lane keeps its pixel's offsets and masks in registers.
 //
 // Staging uses direct-to-LDS buffer loads, one LDS row per group of wave
 // instructions: slot j of every row comes from the row's base plus a
@@ -35,8 +36,8 @@
 // cells, the lists of the corner cells that reach them; the tile is then
 // written with plain stores.
 // grad_offset_mask is forward-shaped; it also adds the contributions of far
-// samples to grad_value with device atomics (one 64-lane instruction per far
-// sample), after the cell-tile kernel has written every cell.
+// samples to grad_value with device atomics (a whole-wave instruction per far
+// sample and lane), after the cell-tile kernel has written every cell.
 
 #include "dcnv4_device.h"
 #include "dcnv4_internal.h"
@@ -55,10 +56,6 @@ constexpr int kMaxTileThreads = 512;  // threads of an output-tile block
 constexpr int kCellThreads = 512;     // threads of a cell-tile block
 constexpr int kCellBinSlots = 2048;   // bin counters of a cell tile: (ch + 1) * (cw + 1) < 2048, 4 per thread
 constexpr unsigned kOutOfRange = 0x80000000u;   // >= any buffer size used here
-// s_waitcnt immediate: vector memory count 0, export and LDS/scalar counts
-// left at their maxima (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
-// lgkmcnt [11:8])
-constexpr int kWaitVmcnt0 = 0x0F70;
 
 struct TArgs {
     Geom geo;
@@ -69,17 +66,14 @@ struct TArgs {
     float *gvalue;
     float *gom;
     int G, Cg, K, P;
-    unsigned kh_magic;           // ceil(2^32 / kernel_h)
     unsigned k3_magic;           // ceil(2^32 / (3K))
     // output tiles
     int th, tw, tiles_y, tiles_x, lanes_shift;
     int R, rh, rw;               // halo radius; LDS value region, pixels
     int ps, nvp;                 // LDS pixel stride; data vectors per pixel (16-byte units)
     unsigned ps_magic;
-    int om_dw;                   // staged dwords per pixel
-    unsigned om_dw_magic, tw_magic;
+    unsigned tw_magic;
     unsigned npad_magic;         // ceil(2^32 / (P - 3GK)), padding entries per pixel
-    int om_lds_bytes;
     // cell tiles (backward grad_value)
     int ch, cw, ctiles_y, ctiles_x;
     unsigned cw_magic;           // ceil(2^32 / cw)
@@ -118,22 +112,6 @@ __device__ __forceinline__ Tile out_tile(const TArgs &a)
     t.oy0 = ty * a.th;
     t.ox0 = tx * a.tw;
     return t;
-}
-
-// Location of grid point k for a per-lane k (the kernel_h division by
-// multiply-high); same arithmetic as the main loops.
-__device__ __forceinline__ Loc locate_lane(const TArgs &a, int ho, int wo, int k, float dx, float dy)
-{
-    const Geom &g = a.geo;
-    const int kk = k + ((g.rc && k >= g.kc) ? 1 : 0);
-    const int i = (int)divm((unsigned)kk, a.kh_magic);
-    const int j = kk - i * g.kh;
-    Loc l;
-    l.bh = ho * g.sh - g.ph + j * g.dh;
-    l.bw = wo * g.sw - g.pw + i * g.dw;
-    l.w = __builtin_fmaf(g.scale, dx, (float)l.bw);
-    l.h = __builtin_fmaf(g.scale, dy, (float)l.bh);
-    return l;
 }
 
 // ---- staging ----------------------------------------------------------------
@@ -181,33 +159,6 @@ __device__ __forceinline__ void staging_done()
     __syncthreads();
 }
 
-// Offset/mask entries of group g for the tile's pixels, in dwords: pixel
-// q = py*tw + px owns om_dw dwords from dword q*om_dw, covering its 3K
-// entries from the dword that holds entry 0 (2-byte entries of odd groups
-// start one element into it).
-// Per-lane byte offsets, within an image row of offset_mask (pixel stride
-// pix_bytes), of the slots of a tile row that holds `w` dwords per pixel from
-// byte `first` of each pixel: slot j = c*64 + lane is dword j % w of tile
-// column j / w; kOutOfRange past the tile or the image.
-__device__ __forceinline__ void pixel_row_offsets(const TArgs &a, const Tile &t, int w, unsigned w_magic,
-                                                  unsigned pix_bytes, unsigned first, unsigned (&lo)[kMaxRowChunks])
-{
-    const int lane = threadIdx.x & 63;
-    const int row_slots = a.tw * w;
-#pragma unroll
-    for (int c = 0; c < kMaxRowChunks; ++c) {
-        lo[c] = kOutOfRange;
-        if (c * 64 < row_slots) {
-            const int j = c * 64 + lane;
-            const int px = (int)divm((unsigned)j, w_magic);
-            const int d = j - px * w;
-            const int ox = t.ox0 + px;
-            if (px < a.tw && ox < a.geo.Wo)
-                lo[c] = (unsigned)ox * pix_bytes + first + 4u * (unsigned)d;
-        }
-    }
-}
-
 // Value rows of group g for the tile plus the halo: region pixel (rr, cc) is
 // image pixel (ry0 + rr, rx0 + cc) and starts at 16-byte slot
 // (rr*rw + cc)*ps; zeros outside the image.
@@ -239,22 +190,6 @@ __device__ __forceinline__ void stage_values(const TArgs &a, const Tile &t, char
             return (unsigned)y < (unsigned)geo.H ? (unsigned)(t.n * geo.H + y) * row_bytes : kOutOfRange;
         });
     }
-}
-
-// Offset/mask rows (om_dw dwords per pixel, see pixel_row_offsets) and the
-// value rows of the tile.
-__device__ __forceinline__ void stage_tile(const TArgs &a, const Tile &t, char *om_s, char *val_s, int es)
-{
-    const Geom &geo = a.geo;
-    unsigned lo[kMaxRowChunks];
-    pixel_row_offsets(a, t, a.om_dw, a.om_dw_magic, (unsigned)(a.P * es), (unsigned)((t.g * 3 * a.K * es) & ~3), lo);
-    const unsigned row_bytes = (unsigned)(geo.Wo * a.P * es);
-    const int row0 = t.n * geo.Ho + t.oy0;
-    const int rows_in = geo.Ho - t.oy0;
-    stage_rows<4>(rsrc(a.om, a.om_bytes), om_s, a.th, a.tw * a.om_dw, lo, [&](int rr) {
-        return rr < rows_in ? (unsigned)(row0 + rr) * row_bytes : kOutOfRange;
-    });
-    stage_values(a, t, val_s, es);
 }
 
 // ---- offsets and masks in registers ------------------------------------------
@@ -407,20 +342,6 @@ __device__ __forceinline__ void far_corner_loads(__amdgpu_buffer_rsrc_t vr, unsi
         v10[v] = load16(vr, off + rs + 16 * v);
         v11[v] = load16(vr, off + rs + cs + 16 * v);
     }
-}
-
-// Softmax statistics of the K mask logits m[stride*k] of one (pixel, group):
-// the maximum and 1 / sum_k exp(m_k - max).
-template <typename T>
-__device__ __forceinline__ void softmax_stats(const T *m, int K, float &mx, float &inv)
-{
-    mx = Store<T>::scalar(m[0]);
-    for (int k = 1; k < K; ++k)
-        mx = fmaxf(mx, Store<T>::scalar(m[k]));
-    float sum = 0.0f;
-    for (int k = 0; k < K; ++k)
-        sum += expf(Store<T>::scalar(m[k]) - mx);
-    inv = 1.0f / sum;
 }
 
 // ---- forward ---------------------------------------------------------------
@@ -1305,7 +1226,6 @@ TArgs make_targs(const Problem &p, const TilePlan &tp)
     a.Cg = p.Cg;
     a.K = p.K;
     a.P = p.P;
-    a.kh_magic = magic_for(p.kh);
     a.k3_magic = magic_for(3 * p.K);
     a.th = tp.th;
     a.tw = tp.tw;
@@ -1318,11 +1238,8 @@ TArgs make_targs(const Problem &p, const TilePlan &tp)
     a.ps = tp.ps;
     a.nvp = tp.nvp;
     a.ps_magic = magic_for(tp.ps);
-    a.om_dw = tp.om_dw;
-    a.om_dw_magic = magic_for(tp.om_dw);
     a.npad_magic = magic_for(p.P - 3 * p.G * p.K);
     a.tw_magic = magic_for(tp.tw);
-    a.om_lds_bytes = tp.om_lds_bytes;
     a.ch = tp.ch;
     a.cw = tp.cw;
     a.ctiles_y = tp.ctiles_y;
@@ -1340,8 +1257,7 @@ TArgs make_targs(const Problem &p, const TilePlan &tp)
 bool out_tiles_ok(const Problem &p, const TilePlan &tp)
 {
     return tp.threads % 64 == 0 && tp.threads <= kMaxTileThreads && tp.threads >= tp.th * tp.tw * tp.lanes &&
-           tp.rw * tp.ps <= 64 * kMaxRowChunks && tp.tw * tp.om_dw <= 64 * kMaxRowChunks && p.K <= 25 &&
-           tp.ps >= tp.nvp && tp.om_lds_bytes % 16 == 0;
+           tp.rw * tp.ps <= 64 * kMaxRowChunks && p.K <= 25 && tp.ps >= tp.nvp;
 }
 
 }  // namespace
