@@ -223,9 +223,10 @@ constexpr int kBackwardRmax = DCNV4_BWD_RMAX;  // largest halo of the backward t
 constexpr int kTiledMaxLds = 80 * 1024;
 constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kTileThreads = 512;
-constexpr int kCellTileLds = 78 * 1024;   // two cell-tile blocks per CU
-constexpr int kCellThreads = 512;         // threads of a cell-tile block: one per vertical pair of cells
-constexpr int kCellBinSlots = 2048;       // bin counters: (ch + 1) * (cw + 1) < 2048
+#ifndef DCNV4_CELL_LDS_KB
+#define DCNV4_CELL_LDS_KB 78
+#endif
+constexpr int kCellTileLds = DCNV4_CELL_LDS_KB * 1024;   // two cell-tile blocks per CU
 constexpr int kCellBinBytes = kCellBinSlots * 4 + (kCellThreads / 64) * 4;   // counters, scan scratch
 
 int region_rows(const Problem &p, int th, int R)

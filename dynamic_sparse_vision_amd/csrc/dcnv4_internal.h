@@ -39,6 +39,16 @@ struct Plan {
     int images_per_launch;
 };
 
+// Cell-tile blocks of the backward's grad_value kernel: threads (one per
+// vertical pair of cells) and the bin counters of a tile ((ch + 1) * (cw + 1)
+// < kCellBinSlots; the in-place scan takes four per thread).
+#ifndef DCNV4_CELL_THREADS
+#define DCNV4_CELL_THREADS 512
+#endif
+constexpr int kCellThreads = DCNV4_CELL_THREADS;
+constexpr int kCellBinSlots = 2048;
+static_assert(4 * kCellThreads >= kCellBinSlots, "scan covers the bins");
+
 // Tiled path.  A sample (output pixel, group, grid point k) is "near" when
 // the integer part of its displacement is within R pixels on both axes:
 // floor(loc) - (integer grid position) in [-R, R].  Every near sample's four

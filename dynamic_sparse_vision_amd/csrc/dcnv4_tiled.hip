@@ -53,8 +53,6 @@ using namespace dev;
 
 constexpr int kMaxRowChunks = 8;      // a staged row spans at most 8 x 64 slots
 constexpr int kMaxTileThreads = 512;  // threads of an output-tile block
-constexpr int kCellThreads = 512;     // threads of a cell-tile block
-constexpr int kCellBinSlots = 2048;   // bin counters of a cell tile: (ch + 1) * (cw + 1) < 2048, 4 per thread
 constexpr unsigned kOutOfRange = 0x80000000u;   // >= any buffer size used here
 
 struct TArgs {
