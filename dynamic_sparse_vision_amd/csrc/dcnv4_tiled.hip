@@ -878,6 +878,21 @@ __device__ __forceinline__ void entries_of(const u32x4 (&v)[NVEC], int mis, floa
         shifted_entries16<T>(v, mis, out);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2,
+// 4, 8 inside rows of 16 lanes, then lane 15 of rows 0 and 2 added to rows 1
+// and 3, then lane 31 to rows 2 and 3 (lanes without a source add 0).
+__device__ __forceinline__ unsigned wave_inclusive_sum(unsigned v)
+{
+    int x = (int)v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return (unsigned)x;
+}
+
 // A cell-tile block: ch x cw input cells of one (image, group), ch even;
 // thread t < (ch / 2) * cw owns the vertical pair of cells (2 * (t / cw),
 // t % cw) and the one below it.  The output pixels whose near samples can
@@ -943,20 +958,7 @@ __global__ __launch_bounds__(kCellThreads) __attribute__((amdgpu_waves_per_eu(4)
     const __amdgpu_buffer_rsrc_t omr = rsrc(a.om, a.om_bytes);
     const __amdgpu_buffer_rsrc_t gor = rsrc(a.gout, a.gout_bytes);
     char *g_s = lds + a.gs_offset;   // grad_out of the batch's sources
-    // grad_out rows: slot j of a row is vector j % gps of source column j / gps
-    unsigned glo[kMaxRowChunks];
     const int grow_slots = SW * a.gps;
-#pragma unroll
-    for (int c = 0; c < kMaxRowChunks; ++c) {
-        glo[c] = kOutOfRange;
-        if (c * 64 < grow_slots) {
-            const int j = c * 64 + lane;
-            const int s = (int)divm((unsigned)j, a.gps_magic);
-            const int v = j - s * a.gps;
-            if (s < SW && v < NVG)
-                glo[c] = (unsigned)(sx0 + s) * cs + (unsigned)(g * CG * es + 16 * v);
-        }
-    }
     // a source's offsets and masks: 16-byte aligned vectors from the one that
     // holds the first entry (pixel rows are 16-byte multiples)
     const int eo = g * 3 * a.K, em = eo + 2 * a.K;
@@ -982,9 +984,25 @@ __global__ __launch_bounds__(kCellThreads) __attribute__((amdgpu_waves_per_eu(4)
         const int nrows = (SH - bt + nb - 1) / nb;
         for (int i = 4 * tid; i <= NB; i += 4 * kCellThreads)
             *reinterpret_cast<u32x4 *>(bins + i) = u32x4{0u, 0u, 0u, 0u};
-        const unsigned row_bytes = (unsigned)geo.Wo * cs;
-        stage_rows<16>(gor, g_s, nrows, grow_slots, glo,
-                       [&](int rr) { return (unsigned)(n * geo.Ho + r0 + rr * nb) * row_bytes; });
+        {
+            // grad_out rows: slot j of a row is vector j % gps of source
+            // column j / gps (offsets made per batch: fewer live registers)
+            unsigned glo[kMaxRowChunks];
+#pragma unroll
+            for (int c = 0; c < kMaxRowChunks; ++c) {
+                glo[c] = kOutOfRange;
+                if (c * 64 < grow_slots) {
+                    const int j = c * 64 + lane;
+                    const int s = (int)divm((unsigned)j, a.gps_magic);
+                    const int v = j - s * a.gps;
+                    if (s < SW && v < NVG)
+                        glo[c] = (unsigned)(sx0 + s) * cs + (unsigned)(g * CG * es + 16 * v);
+                }
+            }
+            const unsigned row_bytes = (unsigned)geo.Wo * cs;
+            stage_rows<16>(gor, g_s, nrows, grow_slots, glo,
+                           [&](int rr) { return (unsigned)(n * geo.Ho + r0 + rr * nb) * row_bytes; });
+        }
         const bool src_ok = srow < nrows;
         const int oy = r0 + srow * nb, ox = sx0 + scol;
         const unsigned pix = (unsigned)((n * geo.Ho + oy) * geo.Wo + ox) * (unsigned)(a.P * es);
@@ -1056,12 +1074,7 @@ __global__ __launch_bounds__(kCellThreads) __attribute__((amdgpu_waves_per_eu(4)
             c[2] = i0 + 2 <= NB ? c[2] : 0u;
             c[3] = i0 + 3 <= NB ? c[3] : 0u;
             const unsigned mine = c[0] + c[1] + c[2] + c[3];
-            unsigned x = mine;
-            for (int d = 1; d < 64; d <<= 1) {
-                const unsigned y = __shfl_up(x, d);
-                if (lane >= d)
-                    x += y;
-            }
+            const unsigned x = wave_inclusive_sum(mine);
             if (lane == 63)
                 wsum[wave] = x;
             __syncthreads();
