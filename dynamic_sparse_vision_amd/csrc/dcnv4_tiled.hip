@@ -53,6 +53,7 @@ using namespace dev;
 
 constexpr int kMaxRowChunks = 8;      // a staged row spans at most 8 x 64 slots
 constexpr int kMaxTileThreads = 512;  // threads of an output-tile block
+constexpr int kMaxTiledPoints = 25;   // K of the tiled kernels (KMAX 9 or 25)
 constexpr unsigned kOutOfRange = 0x80000000u;   // >= any buffer size used here
 
 struct TArgs {
@@ -64,6 +65,9 @@ struct TArgs {
     float *gvalue;
     float *gom;
     int G, Cg, K, P;
+    // grid point k sits at (j*dh, i*dw) from the window origin (as floats,
+    // exact small integers): a table instead of a division by kernel_h
+    float gdh[kMaxTiledPoints], gdw[kMaxTiledPoints];
     unsigned k3_magic;           // ceil(2^32 / (3K))
     // output tiles
     int th, tw, tiles_y, tiles_x, lanes_shift;
@@ -437,10 +441,8 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_fwd_tiled(TArgs a)
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         if (k < a.K) {
-            int gi, gj;
-            grid_point(geo, k, gi, gj);
             const float m = msk[k];
-            const float bh = nf.bh0 + (float)(gj * geo.dh), bw = nf.bw0 + (float)(gi * geo.dw);
+            const float bh = nf.bh0 + a.gdh[k], bw = nf.bw0 + a.gdw[k];
             const NearSample s = near_sample(nf, geo.scale, bh, bw, offs[2 * k], offs[2 * k + 1]);
             if (!s.nr && live_loc(geo, s.lh, s.lw))
                 far_sample_fwd<T, DP>(geo, vr, t.n, chan_off, s, m, acc);
@@ -596,10 +598,8 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
     for (int k = 0; k < KMAX; ++k) {
         gx[k] = gy[k] = gmk[k] = 0.0f;
         if (k < a.K) {
-            int gi, gj;
-            grid_point(geo, k, gi, gj);
             const float m = msk[k];
-            const float bh = nf.bh0 + (float)(gj * geo.dh), bw = nf.bw0 + (float)(gi * geo.dw);
+            const float bh = nf.bh0 + a.gdh[k], bw = nf.bw0 + a.gdw[k];
             const NearSample s = near_sample(nf, geo.scale, bh, bw, offs[2 * k], offs[2 * k + 1]);
             const bool nr = s.nr && valid;
             const bool far = valid && !s.nr && live_loc(geo, s.lh, s.lw);
@@ -1040,9 +1040,7 @@ __global__ __launch_bounds__(kCellThreads) __attribute__((amdgpu_waves_per_eu(4)
         // Evaluated twice, to count and then to place, so that nothing but the
         // offsets and masks stays live across the scan.
         auto sample = [&](int k, unsigned &bin, float &fa, float &fb) {
-            int gi, gj;
-            grid_point(geo, k, gi, gj);
-            const float bh = bh0 + (float)(gj * geo.dh), bw = bw0 + (float)(gi * geo.dw);
+            const float bh = bh0 + a.gdh[k], bw = bw0 + a.gdw[k];
             const float lh = __builtin_fmaf(geo.scale, offs[2 * k + 1], bh);
             const float lw = __builtin_fmaf(geo.scale, offs[2 * k], bw);
             const float fh = __builtin_floorf(lh), fw = __builtin_floorf(lw);
@@ -1251,6 +1249,13 @@ TArgs make_targs(const Problem &p, const TilePlan &tp)
     a.ps_magic = magic_for(tp.ps);
     a.npad_magic = magic_for(p.P - 3 * p.G * p.K);
     a.tw_magic = magic_for(tp.tw);
+    for (int k = 0; k < p.K && k < kMaxTiledPoints; ++k) {
+        const int kc = ((p.kw - 1) / 2) * p.kh + (p.kh - 1) / 2;   // centre of the full grid (i over kernel_w outer)
+        const int kk = k + ((p.remove_center && k >= kc) ? 1 : 0);
+        const int i = kk / p.kh, j = kk - i * p.kh;
+        a.gdh[k] = (float)(j * p.dh);
+        a.gdw[k] = (float)(i * p.dw);
+    }
     a.ch = tp.ch;
     a.cw = tp.cw;
     a.ctiles_y = tp.ctiles_y;
