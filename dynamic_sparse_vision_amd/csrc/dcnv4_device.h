@@ -17,6 +17,8 @@ constexpr int kRawBufferConfig = 0x00020000;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 // __builtin_bit_cast is only ever applied to whole vectors or scalars here;
 // applied to a vector-element lvalue it reads element 0 with this compiler.

@@ -523,7 +523,7 @@ __device__ __forceinline__ float pixel_sum(float x, int lanes)
 // whole wave.  At the end the value rows are no longer needed and their LDS
 // holds the tile's gradient rows, which are written back row by row.
 template <typename T, int DP, int KMAX, bool SM>
-__global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs a)
+__global__ __launch_bounds__(kMaxTileThreads) __attribute__((amdgpu_waves_per_eu(4))) void dcnv4_bwd_offsets_tiled(TArgs a)
 {
     extern __shared__ u32x4 smem[];
     constexpr int es = (int)sizeof(T);
@@ -703,6 +703,49 @@ __global__ __launch_bounds__(kMaxTileThreads) void dcnv4_bwd_offsets_tiled(TArgs
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
             gmk[k] = msk[k] * (gmk[k] - sdot);
+    }
+    if constexpr (es == 4) {
+        // fp32: every entry is dword aligned, so each pixel writes its rows
+        // straight from registers with multi-dword stores, no block barrier:
+        // the first lane the 2K offsets, the second (or the same) the K masks;
+        // group 0 also zeroes the padding channels
+        const __amdgpu_buffer_rsrc_t r = rsrc(a.gom, a.om_bytes);
+        const unsigned row = q_pix * (unsigned)(a.P * 4);
+        const unsigned base = row + (unsigned)(t.g * 3 * a.K * 4);
+        const int mask_lane = lanes > 1 ? 1 : 0;
+        if (valid && chunk == 0) {
+#pragma unroll
+            for (int k = 0; k < KMAX; k += 2) {
+                if (k + 1 < a.K) {
+                    const f32x4 v{gx[k], gy[k], gx[k + 1], gy[k + 1]};
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, base + 8 * k, 0, 0);
+                } else if (k < a.K) {
+                    const f32x2 v{gx[k], gy[k]};
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, base + 8 * k, 0, 0);
+                }
+            }
+        }
+        if (valid && chunk == mask_lane) {
+            const unsigned mb = base + (unsigned)(8 * a.K);
+#pragma unroll
+            for (int k = 0; k < KMAX; k += 4) {
+                if (k + 3 < a.K) {
+                    const f32x4 v{gmk[k], gmk[k + 1], gmk[k + 2], gmk[k + 3]};
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, mb + 4 * k, 0, 0);
+                } else {
+#pragma unroll
+                    for (int kk = k; kk < k + 4 && kk < KMAX; ++kk)
+                        if (kk < a.K)
+                            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, gmk[kk]), r, mb + 4 * kk, 0,
+                                                                  0);
+                }
+            }
+            if (t.g == 0) {
+                for (int d = a.G * 3 * a.K; d < a.P; ++d)
+                    __builtin_amdgcn_raw_buffer_store_b32(0u, r, row + 4u * (unsigned)d, 0, 0);
+            }
+        }
+        return;
     }
     __syncthreads();   // the value rows are no longer read
 
