@@ -382,7 +382,10 @@ int plan_tiled_common(const Problem &p, int elem, int row_elems, int pixel_bytes
     // 8 channels per lane: two lanes share a 16-channel pixel, which doubles
     // the waves that hide LDS latency at little extra per-sample work
     int dp = 0;
-    for (int cand : {8, 16, 4}) {
+#ifndef DCNV4_DP_FIRST
+#define DCNV4_DP_FIRST 8
+#endif
+    for (int cand : {DCNV4_DP_FIRST, 8, 16, 4}) {
         if (p.Cg % cand == 0 && (cand * elem) % 16 == 0) {
             dp = cand;
             break;

@@ -965,7 +965,8 @@ __global__ __launch_bounds__(kCellThreads) __attribute__((amdgpu_waves_per_eu(4)
     // then (after placing) the end of each bin
     unsigned *bins = reinterpret_cast<unsigned *>(lds);
     unsigned *wsum = bins + kCellBinSlots;               // [kCellThreads / 64] per-wave scan totals
-    // sorted records: (frac h, frac w, m, LDS byte offset of the source's grad_out)
+    // sorted records: (m * (1 - frac h), m * frac h, frac w, LDS byte offset of the
+    // source's grad_out)
     f32x4 *rec = reinterpret_cast<f32x4 *>(lds + a.rec_offset);
 
     int b = xcd_tile(blockIdx.x, gridDim.x);
@@ -1149,10 +1150,12 @@ __global__ __launch_bounds__(kCellThreads) __attribute__((amdgpu_waves_per_eu(4)
                 sample(k, bin, fa, fb);
                 if (bin != 0xffffffffu) {
                     const unsigned idx = atomicAdd(&bins[bin], 1u);
+                    // the mask times the weight of the samples' upper and
+                    // lower corner rows, the column fraction, the source
                     f32x4 r;
-                    r[0] = fa;
-                    r[1] = fb;
-                    r[2] = msk[k];
+                    r[0] = msk[k] * (1.0f - fa);
+                    r[1] = msk[k] * fa;
+                    r[2] = fb;
                     r[3] = __builtin_bit_cast(float, my_gs);
                     rec[idx] = r;
                 }
@@ -1178,34 +1181,32 @@ __global__ __launch_bounds__(kCellThreads) __attribute__((amdgpu_waves_per_eu(4)
                         gv[v] = gp[v];
                     rv = rec[idx + 1];
                     // column px of the bin pair: this cell is the samples' right column
-                    const float wx = idx < mid ? cur[1] : 1.0f - cur[1];
-                    add(cur[0], wx, cur[2], gv);
+                    const float wx = idx < mid ? cur[2] : 1.0f - cur[2];
+                    add(cur[0] * wx, cur[1] * wx, gv);
                 }
             };
             // bin row 2py: the upper cell is the samples' lower row
-            gather(binA, [&](float fy, float wx, float m, const u32x4(&gv)[NVG]) {
-                const float w = m * (fy * wx);
+            // (wu, wl: the sample's weights on its upper and lower corner row
+            // in this cell's column)
+            gather(binA, [&](float, float wl, const u32x4(&gv)[NVG]) {
 #pragma unroll
                 for (int c = 0; c < CG; ++c)
-                    acc0[c] = __builtin_fmaf(w, Store<T>::get(gv, c), acc0[c]);
+                    acc0[c] = __builtin_fmaf(wl, Store<T>::get(gv, c), acc0[c]);
             });
             // bin row 2py+1: upper row of the upper cell, lower row of the lower
-            gather(binA + AW, [&](float fy, float wx, float m, const u32x4(&gv)[NVG]) {
-                const float w0 = m * ((1.0f - fy) * wx);
-                const float w1 = m * (fy * wx);
+            gather(binA + AW, [&](float wu, float wl, const u32x4(&gv)[NVG]) {
 #pragma unroll
                 for (int c = 0; c < CG; ++c) {
                     const float gc = Store<T>::get(gv, c);
-                    acc0[c] = __builtin_fmaf(w0, gc, acc0[c]);
-                    acc1[c] = __builtin_fmaf(w1, gc, acc1[c]);
+                    acc0[c] = __builtin_fmaf(wu, gc, acc0[c]);
+                    acc1[c] = __builtin_fmaf(wl, gc, acc1[c]);
                 }
             });
             // bin row 2py+2: the lower cell is the samples' upper row
-            gather(binA + 2 * AW, [&](float fy, float wx, float m, const u32x4(&gv)[NVG]) {
-                const float w = m * ((1.0f - fy) * wx);
+            gather(binA + 2 * AW, [&](float wu, float, const u32x4(&gv)[NVG]) {
 #pragma unroll
                 for (int c = 0; c < CG; ++c)
-                    acc1[c] = __builtin_fmaf(w, Store<T>::get(gv, c), acc1[c]);
+                    acc1[c] = __builtin_fmaf(wu, Store<T>::get(gv, c), acc1[c]);
             });
         }
         __syncthreads();
