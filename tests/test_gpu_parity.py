@@ -125,6 +125,9 @@ COVERAGE = [
     _wl("k1x1_fp32", "fp32", N=2, H=5, W=6, C=32, G=2, kernel=(1, 1), pad=(0, 0)),
     _wl("scale_half_fp32", "fp32", N=2, H=9, W=9, C=32, G=2, offset_scale=0.5),
     _wl("far_offsets_fp16", "fp16", N=1, H=8, W=8, C=32, G=2, sigma_off=40.0),
+    # offsets of ~9 px: near and far samples (beyond the tiles' halo) mixed,
+    # far ones inside and outside the image
+    _wl("mixed_far_fp32", "fp32", N=2, H=24, W=21, C=32, G=2, sigma_off=9.0),
     _wl("tiny_1x1_image_fp32", "fp32", N=3, H=1, W=1, C=32, G=2),
     _wl("int_offsets_fp32", "fp32", N=2, H=7, W=9, C=32, G=2, integer_offsets=True),
 ]
