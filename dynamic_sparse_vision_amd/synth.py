@@ -17,8 +17,9 @@ Generator (published definitions, restated):
     (round-to-nearest-even) to the storage dtype.
 
 Each tensor has its own stream, seeded ``seed * 16 + tensor_id`` with
-tensor_id 0 = value, 1 = offset_mask, 2 = grad_output; elements are drawn in
-memory order.
+tensor_id 0 = value, 1 = offset_mask (or the locations and logits of flash
+deformable attention), 2 = grad_output, 3 = the attention reference points;
+elements are drawn in memory order.
 """
 from __future__ import annotations
 
@@ -27,7 +28,7 @@ import numpy as np
 GAMMA = np.uint64(0x9E3779B97F4A7C15)
 M1 = np.uint64(0xBF58476D1CE4E5B9)
 M2 = np.uint64(0x94D049BB133111EB)
-TENSOR_VALUE, TENSOR_OFFSET_MASK, TENSOR_GRAD_OUT = 0, 1, 2
+TENSOR_VALUE, TENSOR_OFFSET_MASK, TENSOR_GRAD_OUT, TENSOR_REFERENCE = 0, 1, 2, 3
 _CHUNK = 1 << 22  # pairs per chunk
 
 
@@ -137,3 +138,54 @@ def to_storage(a_f32: np.ndarray, dtype: str):
     else:
         raise ValueError(dtype)
     return st, st.to(torch.float32).numpy()
+
+
+def fdattn_channels(L: int, K: int) -> int:
+    """Padded entry count of a (query, head) row of loc_attn (multiple of 8)."""
+    return (3 * L * K + 7) // 8 * 8
+
+
+def fdattn_loc_attn_f32(N: int, Q: int, M: int, shapes, K: int, P: int, seed: int,
+                        sigma_px: float, sigma_logit: float, encoder_queries: bool = True,
+                        pad_fill: float = float("nan")) -> np.ndarray:
+    """Locations and logits of flash deformable attention, (N, Q, M, P).
+
+    Row of (query, head): L*K normalised (u, v) pairs (level-major, point
+    inner), then L*K logits, then padding up to P filled with ``pad_fill``.
+
+    Locations are a reference point plus a normal offset of ``sigma_px``
+    pixels of the sampled level: u = ref_u + sigma_px * z / W_l.  With
+    ``encoder_queries`` (Q must equal sum H_l*W_l) query q is pixel q of the
+    concatenated levels and its reference point is that pixel's centre;
+    otherwise reference points are uniform in [0, 1)^2 (stream 3).
+    Logits are sigma_logit * N(0, 1).  Drawn in float64, rounded to float32.
+    """
+    shapes = [(int(h), int(w)) for h, w in shapes]
+    L = len(shapes)
+    LK = L * K
+    if encoder_queries:
+        S = sum(h * w for h, w in shapes)
+        if Q != S:
+            raise ValueError("encoder queries need Q == sum H_l*W_l")
+        ref = np.empty((Q, 2), np.float64)
+        q0 = 0
+        for h, w in shapes:
+            r, c = np.divmod(np.arange(h * w, dtype=np.float64), w)
+            ref[q0:q0 + h * w, 0] = (c + 0.5) / w
+            ref[q0:q0 + h * w, 1] = (r + 0.5) / h
+            q0 += h * w
+        ref = np.broadcast_to(ref[None], (N, Q, 2))
+    else:
+        ref = uniform(stream(seed, TENSOR_REFERENCE), 0, N * Q * 2).reshape(N, Q, 2)
+    z = normal_f32(stream(seed, TENSOR_OFFSET_MASK), N * Q * M * P).reshape(N, Q, M, P).astype(np.float64)
+    out = np.empty((N, Q, M, P), np.float64)
+    wl = np.array([w for _, w in shapes], np.float64)
+    hl = np.array([h for h, _ in shapes], np.float64)
+    zl = z[..., :2 * LK].reshape(N, Q, M, L, K, 2)
+    u = ref[:, :, None, None, None, 0] + sigma_px * zl[..., 0] / wl[None, None, None, :, None]
+    v = ref[:, :, None, None, None, 1] + sigma_px * zl[..., 1] / hl[None, None, None, :, None]
+    loc = np.stack([u, v], -1).reshape(N, Q, M, 2 * LK)
+    out[..., :2 * LK] = loc
+    out[..., 2 * LK:3 * LK] = sigma_logit * z[..., 2 * LK:3 * LK]
+    out[..., 3 * LK:] = pad_fill
+    return out.astype(np.float32)

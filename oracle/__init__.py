@@ -1,4 +1,5 @@
-"""CPU oracle for the DCNv4 spatial-aggregation operator.
+"""CPU oracle for the DCNv4 spatial-aggregation operator and for flash
+deformable attention (multi-scale deformable attention).
 
 TEST INFRASTRUCTURE ONLY: imported by the test suite, by the smoke check and
 by the CPU-baseline leg of the benchmark, never by the product library.  The
@@ -11,6 +12,9 @@ Every function here follows the definition cited in ``dcnv4_oracle.c``
 removed, bilinear sampling with zero padding).  ``softmax=True`` selects the
 DCNv3 form, with the masks of each (pixel, group) normalised by a softmax
 over the K points.
+
+``fdattn_forward`` / ``fdattn_backward`` wrap ``fdattn_oracle.c`` (the
+multi-scale deformable attention definition cited there; its own library).
 """
 from __future__ import annotations
 
@@ -23,6 +27,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dcnv4_oracle.c")
 _LIB = os.path.join(_HERE, "libdcnv4_oracle.so")
+FDA_SRC = os.path.join(_HERE, "fdattn_oracle.c")
+FDA_LIB = os.path.join(_HERE, "libfdattn_oracle.so")
 
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra"]
@@ -34,6 +40,12 @@ def build(src: str = _SRC, out: str = _LIB, extra: list[str] | None = None) -> s
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
     return out
+
+
+def build_all() -> None:
+    """Compile both oracle libraries."""
+    build()
+    build(FDA_SRC, FDA_LIB)
 
 
 _lib_cache: dict[str, ctypes.CDLL] = {}
@@ -152,3 +164,68 @@ def backward(value, offset_mask, grad_output, kernel_h=3, kernel_w=3, stride_h=1
     if K < 0:
         raise ValueError("oracle rejected the geometry")
     return gv, gom
+
+
+# ------------------------------------------------- flash deformable attention --
+
+def load_fdattn(path: str = FDA_LIB) -> ctypes.CDLL:
+    """Load the flash deformable attention oracle; build it if missing."""
+    if path in _lib_cache:
+        return _lib_cache[path]
+    if not os.path.exists(path):
+        if path != FDA_LIB:
+            raise FileNotFoundError(path)
+        build(FDA_SRC, FDA_LIB)
+    lib = ctypes.CDLL(path)
+    i, p = ctypes.c_int, ctypes.c_void_p
+    dims = [i] * 7  # N S Q M D K P
+    lib.fdao_forward.argtypes = [p, p, i, p, p] + dims + [i]
+    lib.fdao_forward.restype = i
+    lib.fdao_backward.argtypes = [p, p, i, p, p, p, p] + dims + [i]
+    lib.fdao_backward.restype = i
+    _lib_cache[path] = lib
+    return lib
+
+
+def _fda_dims(value, shapes, loc_attn, points):
+    shapes = np.ascontiguousarray(np.asarray(shapes, dtype=np.int32).reshape(-1, 2))
+    N, S, M, D = value.shape
+    if loc_attn.ndim != 4 or loc_attn.shape[0] != N or loc_attn.shape[2] != M:
+        raise ValueError(f"loc_attn shape {loc_attn.shape} does not match value {value.shape}")
+    Q, P = loc_attn.shape[1], loc_attn.shape[3]
+    return shapes, (N, S, Q, M, D, int(points), P)
+
+
+def fdattn_forward(value, spatial_shapes, loc_attn, points, nthreads=0, lib=None):
+    """out (N,Q,M,D) float64 from value (N,S,M,D), the level shapes (L,2) =
+    (H_l, W_l) and loc_attn (N,Q,M,P); inputs are upcast to float32."""
+    lib = lib or load_fdattn()
+    value = _f32(value)
+    loc_attn = _f32(loc_attn)
+    shapes, dims = _fda_dims(value, spatial_shapes, loc_attn, points)
+    N, S, Q, M, D = dims[:5]
+    out = np.zeros((N, Q, M, D), np.float64)
+    rc = lib.fdao_forward(value.ctypes.data, shapes.ctypes.data, shapes.shape[0], loc_attn.ctypes.data,
+                          out.ctypes.data, *dims, int(nthreads))
+    if rc < 0:
+        raise ValueError("oracle rejected the arguments")
+    return out
+
+
+def fdattn_backward(value, spatial_shapes, loc_attn, grad_output, points, nthreads=0, lib=None):
+    """(grad_value (N,S,M,D), grad_loc_attn (N,Q,M,P)), both float64."""
+    lib = lib or load_fdattn()
+    value = _f32(value)
+    loc_attn = _f32(loc_attn)
+    grad_output = _f32(grad_output)
+    shapes, dims = _fda_dims(value, spatial_shapes, loc_attn, points)
+    N, S, Q, M, D = dims[:5]
+    if grad_output.shape != (N, Q, M, D):
+        raise ValueError(f"grad_output shape {grad_output.shape} != {(N, Q, M, D)}")
+    gv = np.zeros(value.shape, np.float64)
+    gla = np.zeros(loc_attn.shape, np.float64)
+    rc = lib.fdao_backward(value.ctypes.data, shapes.ctypes.data, shapes.shape[0], loc_attn.ctypes.data,
+                           grad_output.ctypes.data, gv.ctypes.data, gla.ctypes.data, *dims, int(nthreads))
+    if rc < 0:
+        raise ValueError("oracle rejected the arguments")
+    return gv, gla
