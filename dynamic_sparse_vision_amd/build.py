@@ -13,7 +13,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdcnv4.so")
-SOURCES = [os.path.join(CSRC, n) for n in ("dcnv4_kernels.hip", "dcnv4_tiled.hip", "dcnv4_api.cpp")]
+SOURCES = [os.path.join(CSRC, n) for n in ("dcnv4_kernels.hip", "dcnv4_tiled.hip", "dcnv4_api.cpp",
+                                            "fdattn_kernels.hip", "fdattn_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -511,9 +511,12 @@ int plan_backward_tiled(const Problem &p, TilePlan *tp)
 
 }  // namespace dcnv4
 
-using namespace dcnv4;
+namespace dcnv4 {
 
-namespace {
+void clear_hip_error()
+{
+    g_last_hip_error[0] = '\0';
+}
 
 int hip_status(hipError_t e)
 {
@@ -523,6 +526,12 @@ int hip_status(hipError_t e)
                   hipGetErrorString(e));
     return DCNV4_ERR_HIP;
 }
+
+}  // namespace dcnv4
+
+using namespace dcnv4;
+
+namespace {
 
 bool aligned16(const void *p)
 {

@@ -84,6 +84,12 @@ int plan_backward_tiled(const Problem &p, TilePlan *tp);
 
 dev::Geom make_geom(const Problem &p);
 
+// The per-thread last-HIP-error text behind dcnv4_last_hip_error(): cleared
+// at the start of every entry point; hip_status() records a failure and
+// returns DCNV4_ERR_HIP (DCNV4_OK for hipSuccess).
+void clear_hip_error();
+int hip_status(hipError_t e);
+
 // Enqueue kernels for images [0, p.N) of the given tensors (the caller has
 // already offset the pointers).  Return hipError_t.
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);

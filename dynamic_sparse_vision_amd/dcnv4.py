@@ -63,6 +63,15 @@ def load() -> ctypes.CDLL:
     lib.dcnv4_last_hip_error.restype = ctypes.c_char_p
     lib.dcnv4_abi_version.argtypes = []
     lib.dcnv4_abi_version.restype = i
+    # flash deformable attention (include/flash_deform_attn.h)
+    ip = ctypes.POINTER(i)
+    dims = [i] * 8 + [p]   # N S Q M D K P dtype | stream
+    lib.flash_deform_attn_channels.argtypes = [i, i]
+    lib.flash_deform_attn_channels.restype = i
+    lib.flash_deform_attn_forward.argtypes = [p, ip, i, p, p] + dims
+    lib.flash_deform_attn_forward.restype = i
+    lib.flash_deform_attn_backward.argtypes = [p, ip, i, p, p, p, p] + dims
+    lib.flash_deform_attn_backward.restype = i
     _lib = lib
     return lib
 

@@ -1,0 +1,92 @@
+"""ctypes binding of the flash deformable attention entry points of
+libdcnv4.so (argument marshalling only; include/flash_deform_attn.h).
+
+Tensors are torch device tensors (memory and the current stream come from
+torch); ``spatial_shapes`` is a host sequence of (H_l, W_l) pairs.  Every
+step of the operator runs in the library's HIP kernels; a missing library
+or a failing call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from .dcnv4 import DCNV4_OK, Dcnv4Error, _check, _dtype_code, _stream_ptr, load
+
+
+def _shapes_arg(spatial_shapes):
+    flat = [int(v) for hw in spatial_shapes for v in hw]
+    if len(flat) % 2:
+        raise ValueError("spatial_shapes must be (H, W) pairs")
+    arr = (ctypes.c_int * max(1, len(flat)))(*flat)
+    return arr, len(flat) // 2
+
+
+def flash_deform_attn_channels(num_levels: int, num_points: int) -> int:
+    st = load().flash_deform_attn_channels(num_levels, num_points)
+    if st < 0:
+        raise Dcnv4Error(st, "flash_deform_attn_channels")
+    return st
+
+
+def flash_deform_attn_forward(value, spatial_shapes, loc_attn, output, *, num_points, stream=None) -> None:
+    """value (N,S,M,D), loc_attn (N,Q,M,P), output (N,Q,M,D): device tensors
+    of one dtype.  Enqueues the forward on ``stream`` (default: torch's
+    current stream)."""
+    for t, nm in ((value, "value"), (loc_attn, "loc_attn"), (output, "output")):
+        _check(t, nm)
+        if t.dtype != value.dtype:
+            raise TypeError(f"{nm} dtype {t.dtype} != value dtype {value.dtype}")
+    N, S, M, D = value.shape
+    Q, P = loc_attn.shape[1], loc_attn.shape[3]
+    arr, L = _shapes_arg(spatial_shapes)
+    st = load().flash_deform_attn_forward(
+        ctypes.c_void_p(value.data_ptr()), arr, L, ctypes.c_void_p(loc_attn.data_ptr()),
+        ctypes.c_void_p(output.data_ptr()), N, S, Q, M, D, int(num_points), P, _dtype_code(value),
+        _stream_ptr(stream))
+    if st != DCNV4_OK:
+        raise Dcnv4Error(st, "flash_deform_attn_forward")
+
+
+def flash_deform_attn_backward(value, spatial_shapes, loc_attn, grad_output, grad_value, grad_loc_attn, *,
+                               num_points, stream=None) -> None:
+    """Backward into caller-allocated grad_value (N,S,M,D) float32 and
+    grad_loc_attn (N,Q,M,P) in the inputs' dtype (both overwritten)."""
+    import torch
+
+    for t, nm in ((value, "value"), (loc_attn, "loc_attn"), (grad_output, "grad_output"),
+                  (grad_value, "grad_value"), (grad_loc_attn, "grad_loc_attn")):
+        _check(t, nm)
+        want = torch.float32 if nm == "grad_value" else value.dtype
+        if t.dtype != want:
+            raise TypeError(f"{nm} dtype {t.dtype} != {want}")
+    N, S, M, D = value.shape
+    Q, P = loc_attn.shape[1], loc_attn.shape[3]
+    arr, L = _shapes_arg(spatial_shapes)
+    st = load().flash_deform_attn_backward(
+        ctypes.c_void_p(value.data_ptr()), arr, L, ctypes.c_void_p(loc_attn.data_ptr()),
+        ctypes.c_void_p(grad_output.data_ptr()), ctypes.c_void_p(grad_value.data_ptr()),
+        ctypes.c_void_p(grad_loc_attn.data_ptr()), N, S, Q, M, D, int(num_points), P,
+        _dtype_code(value), _stream_ptr(stream))
+    if st != DCNV4_OK:
+        raise Dcnv4Error(st, "flash_deform_attn_backward")
+
+
+def forward(value, spatial_shapes, loc_attn, num_points):
+    """Allocate the output (N,Q,M,D) with torch and call the forward."""
+    import torch
+
+    N, S, M, D = value.shape
+    out = torch.empty((N, loc_attn.shape[1], M, D), dtype=value.dtype, device=value.device)
+    flash_deform_attn_forward(value, spatial_shapes, loc_attn, out, num_points=num_points)
+    return out
+
+
+def backward(value, spatial_shapes, loc_attn, grad_output, num_points):
+    """Allocate grad_value (fp32) and grad_loc_attn with torch and call the
+    backward."""
+    import torch
+
+    gv = torch.empty(value.shape, dtype=torch.float32, device=value.device)
+    gla = torch.empty_like(loc_attn)
+    flash_deform_attn_backward(value, spatial_shapes, loc_attn, grad_output, gv, gla, num_points=num_points)
+    return gv, gla

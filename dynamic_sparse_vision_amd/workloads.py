@@ -129,3 +129,88 @@ WORKLOADS = {
                  integer_offsets=True),
     ]
 }
+
+
+# ------------------------------------------------- flash deformable attention --
+
+@dataclass(frozen=True)
+class FdaWorkload:
+    """A flash deformable attention problem: value (N, S, M, D) over the
+    levels ``shapes``; Q queries per image (encoder queries: one per value
+    pixel, Q = S); L*K points per (query, head)."""
+    name: str
+    N: int
+    shapes: tuple
+    M: int
+    D: int
+    K: int
+    dtype: str
+    seed: int
+    sigma_px: float = 2.0
+    sigma_logit: float = 1.0
+    Q: int = 0                 # 0: encoder queries (Q = S)
+    note: str = field(default="", compare=False)
+
+    @property
+    def L(self) -> int:
+        return len(self.shapes)
+
+    @property
+    def S(self) -> int:
+        return sum(h * w for h, w in self.shapes)
+
+    @property
+    def queries(self) -> int:
+        return self.Q or self.S
+
+    @property
+    def P(self) -> int:
+        return synth.fdattn_channels(self.L, self.K)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "fp32" else 2
+
+    @property
+    def points(self) -> int:
+        """Sampled points per call: N * Q * M * L * K * D."""
+        return self.N * self.queries * self.M * self.L * self.K * self.D
+
+    def fwd_bytes(self) -> int:
+        """Compulsory forward bytes: value + loc_attn + output."""
+        s = self.elem_bytes
+        return s * self.N * (self.S * self.M * self.D + self.queries * self.M * (self.P + self.D))
+
+    def bwd_bytes(self) -> int:
+        """Compulsory backward bytes: read value, loc_attn, grad_output, write
+        grad_loc_attn in the storage dtype and grad_value in fp32."""
+        s = self.elem_bytes
+        nv = self.N * self.S * self.M * self.D
+        nq = self.N * self.queries * self.M
+        return s * (nv + nq * (2 * self.P + self.D)) + 4 * nv
+
+    def make_inputs(self, pad_fill: float = float("nan"), N: int | None = None):
+        """float32 numpy (value, loc_attn, grad_out) before storage rounding."""
+        n = self.N if N is None else N
+        v = synth.value_f32((n, self.S, self.M, self.D), self.seed)
+        la = synth.fdattn_loc_attn_f32(n, self.queries, self.M, self.shapes, self.K, self.P, self.seed,
+                                       self.sigma_px, self.sigma_logit, encoder_queries=self.Q == 0,
+                                       pad_fill=pad_fill)
+        g = synth.grad_out_f32((n, self.queries, self.M, self.D), self.seed)
+        return v, la, g
+
+
+# Multi-scale maps of an 800x1280 detection input at strides 8, 16, 32, 64
+# (the high-resolution input of the walkthrough's operator benchmarks,
+# section 3.1), 8 heads of 32 channels (32 channels per head/group there),
+# 4 points per level, encoder queries.
+FDA_WORKLOADS = {
+    w.name: w
+    for w in [
+        FdaWorkload("fda_enc_800x1280_b4_fp32", 4, ((100, 160), (50, 80), (25, 40), (13, 20)), 8, 32, 4,
+                    "fp32", 60, note="encoder self-attention over four levels"),
+        FdaWorkload("fda_enc_800x1280_b4_fp16", 4, ((100, 160), (50, 80), (25, 40), (13, 20)), 8, 32, 4,
+                    "fp16", 61),
+        FdaWorkload("fda_small_fp32", 2, ((12, 20), (6, 10), (3, 5), (2, 3)), 4, 32, 4, "fp32", 62),
+    ]
+}

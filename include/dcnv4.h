@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define DCNV4_ABI_VERSION 2
+#define DCNV4_ABI_VERSION 3
 
 enum dcnv4_status {
     DCNV4_OK = 0,

@@ -1,5 +1,5 @@
 """The C ABI of libdcnv4.so on the CPU: the library loads, exports every
-symbol include/dcnv4.h declares, and rejects bad arguments before any HIP
+symbol include/*.h declares, and rejects bad arguments before any HIP
 call.  No call here reaches a kernel launch: each one fails validation (the
 pointers are fake, 16-byte aligned addresses that are never dereferenced)."""
 import ctypes
@@ -12,7 +12,8 @@ import pytest
 from dynamic_sparse_vision_amd import dcnv4
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "dcnv4.h")
+HEADERS = [os.path.join(ROOT, "include", n) for n in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if n.endswith(".h")]
 
 OK, NULL, SHAPE, PARAM, DTYPE, ALIGN, UNSUP, OVERFLOW, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
@@ -22,15 +23,19 @@ A, B, Cp, D, E = (ctypes.c_void_p(x) for x in (0x100000000, 0x200000000, 0x30000
 
 
 def declared_symbols():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"DCNV4_API\s+[\w\s\*]+?\b(dcnv4_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        names |= set(re.findall(r"DCNV4_API\s+[\w\s\*]+?\b((?:dcnv4|flash_deform_attn)_\w+)\s*\(",
+                                open(h).read()))
+    return sorted(names)
 
 
 def test_header_declares_the_abi():
     assert declared_symbols() == sorted([
         "dcnv4_abi_version", "dcnv4_status_string", "dcnv4_last_hip_error",
         "dcnv4_output_size", "dcnv4_om_channels", "dcnv4_forward", "dcnv4_backward",
-        "dcnv4_forward_ex", "dcnv4_backward_ex"])
+        "dcnv4_forward_ex", "dcnv4_backward_ex",
+        "flash_deform_attn_channels", "flash_deform_attn_forward", "flash_deform_attn_backward"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -39,7 +44,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", dcnv4.LIB_PATH], check=True,
                          capture_output=True, text=True).stdout
-    exported = set(re.findall(r"\bT (dcnv4_\w+)", out))
+    exported = set(re.findall(r"\bT ((?:dcnv4|flash_deform_attn)_\w+)", out))
     assert set(declared_symbols()) <= exported
     # nothing else with the prefix leaks out
     assert exported == set(declared_symbols())
@@ -47,7 +52,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = dcnv4.load()
-    assert lib.dcnv4_abi_version() == 2
+    assert lib.dcnv4_abi_version() == 3
     for st in (OK, NULL, SHAPE, PARAM, DTYPE, ALIGN, UNSUP, OVERFLOW, HIP):
         assert lib.dcnv4_status_string(st)
     assert lib.dcnv4_status_string(12345) == b"unknown status"

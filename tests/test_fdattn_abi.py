@@ -1,0 +1,92 @@
+"""The flash deformable attention entry points of libdcnv4.so on the CPU:
+every rejected argument is refused before any HIP call (the pointers are
+fake, 16-byte aligned addresses that are never dereferenced)."""
+import ctypes
+
+import pytest
+
+from dynamic_sparse_vision_amd import dcnv4
+from dynamic_sparse_vision_amd import flash_deform_attn as fda
+
+OK, NULL, SHAPE, PARAM, DTYPE, ALIGN, UNSUP, OVERFLOW = 0, -1, -2, -3, -4, -5, -6, -7
+
+A, B, Cp, D, E = (ctypes.c_void_p(x) for x in (0x100000000, 0x200000000, 0x300000000,
+                                               0x400000000, 0x500000000))
+SHAPES = [(8, 10), (4, 5)]   # S = 100
+
+
+def shapes_arr(shapes):
+    flat = [v for hw in shapes for v in hw]
+    return (ctypes.c_int * max(1, len(flat)))(*flat), len(shapes)
+
+
+def fwd(ptrs=(A, B, Cp), shapes=SHAPES, L=None, N=2, S=100, Q=7, M=2, Dh=32, K=4, P=24, dtype=0):
+    arr, nl = shapes_arr(shapes)
+    return dcnv4.load().flash_deform_attn_forward(ptrs[0], arr, nl if L is None else L, ptrs[1], ptrs[2],
+                                                  N, S, Q, M, Dh, K, P, dtype, None)
+
+
+def bwd(ptrs=(A, B, Cp, D, E), shapes=SHAPES, L=None, N=2, S=100, Q=7, M=2, Dh=32, K=4, P=24, dtype=0):
+    arr, nl = shapes_arr(shapes)
+    return dcnv4.load().flash_deform_attn_backward(ptrs[0], arr, nl if L is None else L, ptrs[1], ptrs[2],
+                                                   ptrs[3], ptrs[4], N, S, Q, M, Dh, K, P, dtype, None)
+
+
+def test_channels():
+    assert fda.flash_deform_attn_channels(4, 4) == 48
+    assert fda.flash_deform_attn_channels(3, 3) == 32
+    assert fda.flash_deform_attn_channels(1, 1) == 8
+    assert dcnv4.load().flash_deform_attn_channels(0, 4) == PARAM
+    assert dcnv4.load().flash_deform_attn_channels(16, 9) == PARAM   # L*K = 144 > 128
+
+
+@pytest.mark.parametrize("call", [fwd, bwd], ids=["forward", "backward"])
+@pytest.mark.parametrize("over,expect", [
+    (dict(dtype=3), DTYPE),
+    (dict(L=0), PARAM),
+    (dict(shapes=[(2, 2)] * 17, S=68), PARAM),          # 17 levels
+    (dict(K=0), SHAPE),
+    (dict(M=0), SHAPE),
+    (dict(Dh=0), SHAPE),
+    (dict(N=-1), SHAPE),
+    (dict(Q=-1), SHAPE),
+    (dict(S=99), SHAPE),                                 # sum H_l*W_l = 100
+    (dict(shapes=[(8, 10), (0, 5)]), SHAPE),
+    (dict(K=65, P=392), PARAM),                          # L*K = 130 > 128
+    (dict(P=16), PARAM),                                 # < 3LK = 24
+    (dict(P=28), PARAM),                                 # not a multiple of 8
+    (dict(Dh=12), UNSUP),
+    (dict(Dh=24), UNSUP),                                # 3 lanes: not a power of two
+    (dict(shapes=[(1 << 14, 1 << 14)], S=1 << 28, M=1, Dh=8), OVERFLOW),   # one image > 2^31 bytes
+])
+def test_rejected_before_any_device_work(call, over, expect):
+    assert call(**over) == expect
+
+
+def test_head_dim_limits():
+    assert fwd(Dh=128, ptrs=(None, None, None)) == NULL      # 128 passes the shape rules of the forward
+    assert bwd(Dh=128, ptrs=(None,) * 5) == UNSUP             # the backward stops at 64
+
+
+def test_pointer_checks():
+    assert fwd(ptrs=(None, B, Cp)) == NULL
+    assert fwd(ptrs=(A, B, None)) == NULL
+    assert fwd(ptrs=(ctypes.c_void_p(0x100000008), B, Cp)) == ALIGN
+    assert fwd(ptrs=(A, B, ctypes.c_void_p(0x100000010))) == PARAM     # output overlaps value
+    assert fwd(ptrs=(A, B, ctypes.c_void_p(0x200000000 + 64))) == PARAM  # ... overlaps loc_attn
+    assert fwd(N=0, ptrs=(None, None, None)) == OK
+    assert fwd(Q=0, ptrs=(None, None, None)) == OK
+    for i in range(5):
+        ptrs = [A, B, Cp, D, E]
+        ptrs[i] = None
+        assert bwd(ptrs=tuple(ptrs)) == NULL
+    assert bwd(ptrs=(A, B, Cp, ctypes.c_void_p(0x400000004), E)) == ALIGN
+    assert bwd(ptrs=(A, B, Cp, ctypes.c_void_p(0x100000040), E)) == PARAM   # grad_value overlaps value
+    assert bwd(ptrs=(A, B, Cp, D, ctypes.c_void_p(0x400000010))) == PARAM   # grad outputs overlap
+    assert bwd(N=0, ptrs=(None,) * 5) == OK
+
+
+def test_null_shapes():
+    lib = dcnv4.load()
+    assert lib.flash_deform_attn_forward(A, None, 2, B, Cp, 2, 100, 7, 2, 32, 4, 24, 0, None) == NULL
+    assert lib.flash_deform_attn_backward(A, None, 2, B, Cp, D, E, 2, 100, 7, 2, 32, 4, 24, 0, None) == NULL
