@@ -32,30 +32,35 @@ sys.path.insert(0, ROOT)
 
 METRIC = "DCNv4 fwd/bwd sampled points/s (N·H·W·G·K·C') + achieved HBM GB/s % of peak"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SRCS = [os.path.join(ROOT, "dynamic_sparse_vision_amd", "csrc", n) for n in
-               ("dcnv4_device.h", "dcnv4_kernels.hip", "dcnv4_tiled.hip")]
+KERNEL_SRCS = {op: [os.path.join(ROOT, "dynamic_sparse_vision_amd", "csrc", n) for n in names]
+               for op, names in (("dcnv4", ("dcnv4_device.h", "dcnv4_kernels.hip", "dcnv4_tiled.hip")),
+                                 ("fdattn", ("dcnv4_device.h", "dcnv4_kernels.hip", "fdattn_kernels.hip")))}
+FDA_METRIC = "flash deformable attention fwd/bwd sampled points/s (N·Q·M·L·K·D) + achieved HBM GB/s % of peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(op: str = "dcnv4") -> str:
+    """sha256 of the kernel sources of one operator (dcnv4 or fdattn)."""
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
+    for path in KERNEL_SRCS[op]:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, call: str):
+def measured_traffic(workload: str, call: str, op: str = "dcnv4"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    the kernel source has not changed since the counters were taken."""
+    the operator's kernel sources have not changed since the counters were
+    taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != kernel_source_hash():
+    wl = t.get("workloads", {}).get(workload, {})
+    if wl.get("kernel_source_sha256") != kernel_source_hash(op):
         return None
-    entry = t.get("workloads", {}).get(workload, {}).get(call)
+    entry = wl.get(call)
     return None if entry is None else entry.get("hbm_bytes_per_launch")
 
 
@@ -167,10 +172,60 @@ def time_configs(path, steps, warmup):
         torch.cuda.empty_cache()
     lines.append(time_layer(flush, steps, warmup))
     print(json.dumps(lines[-1]), file=sys.stderr, flush=True)
+    for line in time_fdattn_configs(flush, steps, warmup):
+        lines.append(line)
+        print(json.dumps(line), file=sys.stderr, flush=True)
     os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
     with open(path, "w") as f:
         for line in lines:
             f.write(json.dumps(line) + "\n")
+
+
+def time_fdattn_configs(flush, steps, warmup):
+    """Flash deformable attention, forward and backward alone, on each of
+    its full-size workloads (512 MB cache flush between calls)."""
+    import torch
+
+    from dynamic_sparse_vision_amd import flash_deform_attn as fda
+    from dynamic_sparse_vision_amd import synth
+    from dynamic_sparse_vision_amd.workloads import FDA_WORKLOADS
+
+    dev = torch.device("cuda")
+    out_lines = []
+    for name in ("fda_enc_800x1280_b4_fp32", "fda_enc_800x1280_b4_fp16"):
+        w = FDA_WORKLOADS[name]
+        v32, la32, g32 = w.make_inputs(pad_fill=0.0)
+        v, la, g = (synth.to_storage(a, w.dtype)[0].to(dev) for a in (v32, la32, g32))
+        out = torch.empty((w.N, w.queries, w.M, w.D), dtype=v.dtype, device=dev)
+        gv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+        gla = torch.empty_like(la)
+        for direction in ("fwd", "bwd"):
+            if direction == "fwd":
+                call = lambda: fda.flash_deform_attn_forward(v, w.shapes, la, out, num_points=w.K)  # noqa: E731
+                nbytes = w.fwd_bytes()
+            else:
+                call = lambda: fda.flash_deform_attn_backward(v, w.shapes, la, g, gv, gla,  # noqa: E731
+                                                              num_points=w.K)
+                nbytes = w.bwd_bytes()
+            times = []
+            for i in range(warmup + steps):
+                flush.fill_(float(i))
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                call()
+                e1.record()
+                e1.synchronize()
+                if i >= warmup:
+                    times.append(e0.elapsed_time(e1))
+            ms = statistics.median(times)
+            out_lines.append({"workload": name.replace("fda_", f"fda_{direction}_"), "direction": direction,
+                              "softmax": True, "dtype": w.dtype, "ms": ms,
+                              "points_per_s": w.points / (ms * 1e-3), "compulsory_bytes": nbytes,
+                              "gbps": nbytes / (ms * 1e-3) / 1e9,
+                              "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS})
+        del v, la, g, out, gv, gla
+        torch.cuda.empty_cache()
+    return out_lines
 
 
 def time_layer(flush, steps, warmup):
@@ -204,12 +259,148 @@ def time_layer(flush, steps, warmup):
             "note": "DCNv4 layer: value / offset-mask / output projections (vendor BLAS) + operator"}
 
 
+def copy_probe(dev):
+    """A copy kernel of known size (256 MiB read + 256 MiB written per
+    launch, 3 launches): the calibration of the HBM byte counters."""
+    import torch
+
+    src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def fdattn_cpu_baseline(w, arrays, seconds):
+    """The oracle as it stands, forward + backward, on blocks of 2048
+    queries of one image at a time (cycling over the images and query
+    blocks) until the time budget is spent: a bounded sample of the same
+    workload."""
+    import oracle
+
+    v32, la32, g32 = arrays
+    nthreads = min(int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), os.cpu_count() or 1)
+    lib = oracle.load_fdattn()
+    qb = 2048
+    nblk = -(-w.queries // qb)
+    passes, units = 0, 0
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    while elapsed < seconds:
+        n, b = divmod(passes, nblk)
+        n %= w.N
+        sl = slice(b * qb, min(w.queries, (b + 1) * qb))
+        la = la32[n:n + 1, sl]
+        oracle.fdattn_forward(v32[n:n + 1], w.shapes, la, w.K, nthreads=nthreads, lib=lib)
+        oracle.fdattn_backward(v32[n:n + 1], w.shapes, la, g32[n:n + 1, sl], w.K, nthreads=nthreads, lib=lib)
+        units += la.shape[1] * w.M
+        passes += 1
+        elapsed = time.perf_counter() - t0
+    pts = units * w.L * w.K * w.D
+    return {"value": pts / elapsed, "unit": "sampled points/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{passes} forward + backward passes over blocks of up to {qb} queries of one image "
+                      f"of the same workload (the oracle's backward is serial per image), {elapsed:.1f} s"}
+
+
+def run_fdattn(args):
+    """The flash deformable attention step (forward + backward) of
+    ``args.workload`` (a FDA_WORKLOADS name); prints one JSON line."""
+    import torch
+
+    from dynamic_sparse_vision_amd import dcnv4, synth
+    from dynamic_sparse_vision_amd import flash_deform_attn as fda
+    from dynamic_sparse_vision_amd.workloads import FDA_WORKLOADS
+
+    dcnv4.load()
+    w = FDA_WORKLOADS[args.workload]
+    dev = torch.device("cuda")
+    print(f"bench: generating {w.name}", file=sys.stderr, flush=True)
+    v32, la32, g32 = w.make_inputs(pad_fill=0.0)
+    base = {k: synth.to_storage(a, w.dtype)[0].to(dev) for k, a in (("v", v32), ("la", la32), ("g", g32))}
+    es = w.elem_bytes
+    per_set = es * w.N * (w.S * w.M * w.D + w.queries * w.M * (2 * w.P + 2 * w.D)) + 4 * w.N * w.S * w.M * w.D
+    nsets = max(2, -(-(768 * 1024 * 1024) // per_set))
+    sets = []
+    for i in range(nsets):
+        st = {k: (t if i == 0 else t.clone()) for k, t in base.items()}
+        st["out"] = torch.empty((w.N, w.queries, w.M, w.D), dtype=st["v"].dtype, device=dev)
+        st["gv"] = torch.empty(st["v"].shape, dtype=torch.float32, device=dev)
+        st["gla"] = torch.empty_like(st["la"])
+        sets.append(st)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        st = sets[i % nsets]
+        if ev is not None:
+            ev[0].record(stream)
+        fda.flash_deform_attn_forward(st["v"], w.shapes, st["la"], st["out"], num_points=w.K)
+        if ev is not None:
+            ev[1].record(stream)
+        fda.flash_deform_attn_backward(st["v"], w.shapes, st["la"], st["g"], st["gv"], st["gla"], num_points=w.K)
+        if ev is not None:
+            ev[2].record(stream)
+
+    print(f"bench: {nsets} buffer sets of {per_set / 1e6:.0f} MB; warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    fwd_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in events)
+    bwd_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in events)
+    print(f"bench: {ms_per_step:.4f} ms/step (forward {fwd_ms:.4f} ms, backward {bwd_ms:.4f} ms)",
+          file=sys.stderr, flush=True)
+    calls = {"flash_deform_attn_forward": (fwd_ms, w.fwd_bytes()),
+             "flash_deform_attn_backward": (bwd_ms, w.bwd_bytes())}
+    dom = max(calls, key=lambda c: calls[c][0])
+    dom_ms, dom_bytes = calls[dom]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = fdattn_cpu_baseline(w, (v32, la32, g32), args.cpu_seconds)
+    line = {
+        "metric": FDA_METRIC,
+        "value": w.points / (ms_per_step * 1e-3),
+        "unit": "sampled points/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "fp32" else w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"flash deformable attention forward+backward, N={w.N}, levels "
+                               + "/".join(f"{h}x{ww}" for h, ww in w.shapes)
+                               + f", Q={w.queries}, M={w.M}, D={w.D}, K={w.K}, {w.dtype}",
+                   "points_per_step": w.points},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name, dom, "fdattn"),
+                     "kernel": dom, "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 5)},
+        "cpu_baseline": cpu,
+        "detail": {"forward_ms": round(fwd_ms, 5), "backward_ms": round(bwd_ms, 5),
+                   "forward_gbps": round(w.fwd_bytes() / (fwd_ms * 1e-3) / 1e9, 1),
+                   "backward_gbps": round(w.bwd_bytes() / (bwd_ms * 1e-3) / 1e9, 1),
+                   "forward_bytes": w.fwd_bytes(), "backward_bytes": w.bwd_bytes(),
+                   "buffer_sets": nsets, "set_bytes": per_set},
+    }
+    if args.copy_probe:
+        copy_probe(dev)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2_fwd_fp32_56x56_b64")
+    ap.add_argument("--op", choices=("dcnv4", "fdattn"), default="dcnv4",
+                    help="dcnv4 (the default step) or flash deformable attention")
+    ap.add_argument("--workload", default=None,
+                    help="workload name (default: c2_fwd_fp32_56x56_b64, or fda_enc_800x1280_b4_fp32 "
+                         "with --op fdattn)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--configs-out", default=None,
@@ -225,6 +416,11 @@ def main():
               "communication inside the operator) is not built. Run with --gpus 1.",
               file=sys.stderr, flush=True)
         sys.exit(2)
+    if args.op == "fdattn":
+        args.workload = args.workload or "fda_enc_800x1280_b4_fp32"
+        run_fdattn(args)
+        return
+    args.workload = args.workload or "c2_fwd_fp32_56x56_b64"
 
     import torch
 
@@ -318,12 +514,7 @@ def main():
     if args.configs_out:
         time_configs(args.configs_out, steps=max(20, args.steps), warmup=5)
     if args.copy_probe:
-        # a copy kernel of known size: 256 MiB read + 256 MiB written per launch
-        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+        copy_probe(dev)
     print(json.dumps(line), flush=True)
 
 

@@ -8,11 +8,12 @@
 // channels, taken at column u*W_l - 1/2 and row v*H_l - 1/2 of level l.
 //
 // Layout and mapping:
-//   * A "unit" is one (n, q, m); units are numbered (n, q, m) row-major, so
-//     consecutive units are the heads of one query, then the next query.
-//     The blocks of a launch are renumbered XCD-aware, so each XCD's L2 sees
-//     a contiguous range of queries (neighbouring queries sample
-//     neighbouring value rows).
+//   * A "unit" is one (n, q, m); units are numbered head-major, (n, m, q),
+//     so a block holds consecutive queries of one head, and the blocks of a
+//     launch are renumbered XCD-aware, so each XCD works through a
+//     contiguous range of (image, head) slices: the value rows one head of
+//     one image can sample (S * D elements, 2.7 MB for four levels of an
+//     800x1280 input at D = 32 fp32) stay in that XCD's L2.
 //   * Forward: D/8 lanes per unit, 8 channels per lane (the D' channels per
 //     thread and 128-bit loads of the walkthrough "DCNv4论文解析", section
 //     2.2); a corner is one (fp16/bf16) or two (fp32) 128-bit buffer loads.
@@ -53,8 +54,7 @@ struct Args {
     float *grad_value;
     void *grad_loc;
     int units;            // N*Q*M
-    int qm;               // Q*M
-    int M, D, K, L, LK, P;
+    int Q, M, D, K, L, LK, P;
     unsigned value_bytes; // bytes of value in this launch
     unsigned gv_bytes;    // bytes of grad_value in this launch
     unsigned img_bytes;   // bytes of one image of value
@@ -232,10 +232,12 @@ __global__ __launch_bounds__(kThreads) void fdattn_fwd(Args a)
     const int lane = (int)threadIdx.x % U;
     if (unit >= a.units)
         return;
-    const int n = unit / a.qm;
-    const int m = unit % a.M;
+    const int nm = unit / a.Q;
+    const int n = nm / a.M;
+    const int m = nm - n * a.M;
+    const size_t qrow = ((size_t)n * a.Q + (unit - nm * a.Q)) * a.M + m;   // (n, q, m) row
     const int LK = a.LK;
-    const T *row = static_cast<const T *>(a.loc_attn) + (size_t)unit * a.P;
+    const T *row = static_cast<const T *>(a.loc_attn) + qrow * a.P;
     float mx, inv;
     softmax_stats(row + 2 * LK, LK, mx, inv);
 
@@ -244,25 +246,30 @@ __global__ __launch_bounds__(kThreads) void fdattn_fwd(Args a)
     float acc[8];
     for (int c = 0; c < 8; ++c)
         acc[c] = 0.0f;
-    int i = 0;
+    // The sample loop has no branch: a sample outside its map gets zero
+    // weights and out-of-range offsets, so the compiler can overlap the
+    // loads of several samples.
     for (int l = 0; l < a.L; ++l) {
         const int H = a.lvl_h[l], W = a.lvl_w[l], start = a.lvl_start[l];
         const float Hf = (float)H, Wf = (float)W;
-        for (int k = 0; k < a.K; ++k, ++i) {
+        const int i0 = l * a.K;
+#pragma unroll 4
+        for (int k = 0; k < a.K; ++k) {
+            const int i = i0 + k;
             float u, v;
             ld2(row + 2 * i, u, v);
             const float x = __builtin_fmaf(u, Wf, -0.5f);
             const float y = __builtin_fmaf(v, Hf, -0.5f);
-            if (!live(y, x, Hf, Wf))
-                continue;
+            const bool in = live(y, x, Hf, Wf);
             const float att = expf(ld1(row + 2 * LK + i) - mx) * inv;
-            const Corners c = corners(y, x, H, W, start, a.pix_bytes, base);
+            Corners c = corners(y, x, H, W, start, a.pix_bytes, base);
             float v0[8], v1[8], v2[8], v3[8];
-            load8<T>(vr, c.o[0], v0);
-            load8<T>(vr, c.o[1], v1);
-            load8<T>(vr, c.o[2], v2);
-            load8<T>(vr, c.o[3], v3);
-            const float a0 = att * c.w[0], a1 = att * c.w[1], a2 = att * c.w[2], a3 = att * c.w[3];
+            load8<T>(vr, in ? c.o[0] : kOutOfRange, v0);
+            load8<T>(vr, in ? c.o[1] : kOutOfRange, v1);
+            load8<T>(vr, in ? c.o[2] : kOutOfRange, v2);
+            load8<T>(vr, in ? c.o[3] : kOutOfRange, v3);
+            const float a0 = in ? att * c.w[0] : 0.0f, a1 = in ? att * c.w[1] : 0.0f;
+            const float a2 = in ? att * c.w[2] : 0.0f, a3 = in ? att * c.w[3] : 0.0f;
             for (int e = 0; e < 8; ++e) {
                 float s = acc[e];
                 s = __builtin_fmaf(a0, v0[e], s);
@@ -272,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void fdattn_fwd(Args a)
             }
         }
     }
-    T *out = static_cast<T *>(a.out) + (size_t)unit * a.D + lane * 8;
+    T *out = static_cast<T *>(a.out) + qrow * a.D + lane * 8;
     u32x4 r[2];
     Store<T>::pack(acc, r, 8 * es / 16);
     reinterpret_cast<u32x4 *>(out)[0] = r[0];
@@ -295,15 +302,17 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd(Args a)
     const int unit = blk * upb + lu;
     if (unit >= a.units)
         return;   // whole units leave together; lane sums stay inside a unit
-    const int n = unit / a.qm;
-    const int m = unit % a.M;
+    const int nm = unit / a.Q;
+    const int n = nm / a.M;
+    const int m = nm - n * a.M;
+    const size_t qrow = ((size_t)n * a.Q + (unit - nm * a.Q)) * a.M + m;   // (n, q, m) row
     const int LK = a.LK;
-    const T *row = static_cast<const T *>(a.loc_attn) + (size_t)unit * a.P;
-    T *grow = static_cast<T *>(a.grad_loc) + (size_t)unit * a.P;
+    const T *row = static_cast<const T *>(a.loc_attn) + qrow * a.P;
+    T *grow = static_cast<T *>(a.grad_loc) + qrow * a.P;
     float *ga = ga_lds + lu * LK;
     float mx, inv;
     softmax_stats(row + 2 * LK, LK, mx, inv);
-    const float g = ld1(static_cast<const T *>(a.grad_out) + (size_t)unit * D + lane);
+    const float g = ld1(static_cast<const T *>(a.grad_out) + qrow * D + lane);
 
     const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, (int)a.value_bytes);
     const __amdgpu_buffer_rsrc_t gr = rsrc(a.grad_value, (int)a.gv_bytes);
@@ -366,7 +375,7 @@ Args make_args(const Problem &p)
 {
     Args a;
     a.units = p.N * p.Q * p.M;
-    a.qm = p.Q * p.M;
+    a.Q = p.Q;
     a.M = p.M;
     a.D = p.D;
     a.K = p.K;
