@@ -199,13 +199,14 @@ def time_fdattn_configs(flush, steps, warmup):
         out = torch.empty((w.N, w.queries, w.M, w.D), dtype=v.dtype, device=dev)
         gv = torch.empty(v.shape, dtype=torch.float32, device=dev)
         gla = torch.empty_like(la)
+        ws = fda.workspace_for(v, w.shapes, la, w.K)
         for direction in ("fwd", "bwd"):
             if direction == "fwd":
                 call = lambda: fda.flash_deform_attn_forward(v, w.shapes, la, out, num_points=w.K)  # noqa: E731
                 nbytes = w.fwd_bytes()
             else:
                 call = lambda: fda.flash_deform_attn_backward(v, w.shapes, la, g, gv, gla,  # noqa: E731
-                                                              num_points=w.K)
+                                                              num_points=w.K, workspace=ws)
                 nbytes = w.bwd_bytes()
             times = []
             for i in range(warmup + steps):
@@ -223,7 +224,7 @@ def time_fdattn_configs(flush, steps, warmup):
                               "points_per_s": w.points / (ms * 1e-3), "compulsory_bytes": nbytes,
                               "gbps": nbytes / (ms * 1e-3) / 1e9,
                               "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS})
-        del v, la, g, out, gv, gla
+        del v, la, g, out, gv, gla, ws
         torch.cuda.empty_cache()
     return out_lines
 
@@ -328,6 +329,8 @@ def run_fdattn(args):
         st["gla"] = torch.empty_like(st["la"])
         sets.append(st)
     stream = torch.cuda.current_stream()
+    # the sorted grad_value path: one workspace, reused by every step
+    ws = fda.workspace_for(sets[0]["v"], w.shapes, sets[0]["la"], w.K)
 
     def step(i, ev=None):
         st = sets[i % nsets]
@@ -336,7 +339,8 @@ def run_fdattn(args):
         fda.flash_deform_attn_forward(st["v"], w.shapes, st["la"], st["out"], num_points=w.K)
         if ev is not None:
             ev[1].record(stream)
-        fda.flash_deform_attn_backward(st["v"], w.shapes, st["la"], st["g"], st["gv"], st["gla"], num_points=w.K)
+        fda.flash_deform_attn_backward(st["v"], w.shapes, st["la"], st["g"], st["gv"], st["gla"], num_points=w.K,
+                                       workspace=ws)
         if ev is not None:
             ev[2].record(stream)
 

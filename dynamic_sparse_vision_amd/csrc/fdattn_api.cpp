@@ -8,6 +8,7 @@
 #include "fdattn_internal.h"
 
 #include <algorithm>
+#include <cstddef>
 #include <cstdint>
 
 namespace {
@@ -75,9 +76,32 @@ int describe(const int *shapes, int L, int N, int S, int Q, int M, int D, int K,
     p->P = P;
     p->dtype = dtype;
     p->elem = es;
-    // value (and grad_value) of one launch are addressed with 31-bit offsets
-    *per_launch = (int)std::max<int64_t>(1, kMaxLaunchBytes / (backward ? img_gv : img_v));
+    // value (and grad_value) of one launch are addressed with 31-bit offsets,
+    // and the sorted backward numbers a launch's samples with 31 bits
+    int64_t per = std::max<int64_t>(1, kMaxLaunchBytes / (backward ? img_gv : img_v));
+    if (backward) {
+        const int64_t samples = std::max<int64_t>(1, (int64_t)Q * M * L * K);
+        if (samples > INT32_MAX)
+            return DCNV4_ERR_OVERFLOW;
+        per = std::min<int64_t>(per, INT32_MAX / samples);
+    }
+    *per_launch = (int)std::max<int64_t>(1, per);
     return DCNV4_OK;
+}
+
+// Workspace of the largest need among the launches a call is split into
+// (full launches of per_launch images and the remainder).
+size_t workspace_need(const fdattn::Problem &p, int N, int per_launch)
+{
+    size_t need = 0;
+    for (int n : {std::min(N, per_launch), N % per_launch}) {
+        if (n <= 0)
+            continue;
+        fdattn::Problem q = p;
+        q.N = n;
+        need = std::max(need, fdattn::workspace_bytes(q));
+    }
+    return need;
 }
 
 }  // namespace
@@ -126,10 +150,26 @@ int flash_deform_attn_forward(const void *value, const int *spatial_shapes, int 
     return DCNV4_OK;
 }
 
+int flash_deform_attn_backward_workspace(const int *spatial_shapes, int num_levels, int N, int num_value,
+                                         int num_query, int num_heads, int head_dim, int num_points,
+                                         int loc_attn_channels, int dtype, size_t *bytes)
+{
+    if (!bytes)
+        return DCNV4_ERR_NULL;
+    fdattn::Problem p;
+    int per_launch = 1;
+    int st = describe(spatial_shapes, num_levels, N, num_value, num_query, num_heads, head_dim, num_points,
+                      loc_attn_channels, dtype, true, &p, &per_launch);
+    if (st != DCNV4_OK)
+        return st;
+    *bytes = (N == 0 || num_query == 0) ? 0 : workspace_need(p, N, per_launch);
+    return DCNV4_OK;
+}
+
 int flash_deform_attn_backward(const void *value, const int *spatial_shapes, int num_levels, const void *loc_attn,
-                               const void *grad_output, void *grad_value, void *grad_loc_attn, int N, int num_value,
-                               int num_query, int num_heads, int head_dim, int num_points, int loc_attn_channels,
-                               int dtype, void *stream)
+                               const void *grad_output, void *grad_value, void *grad_loc_attn, void *workspace,
+                               size_t workspace_bytes, int N, int num_value, int num_query, int num_heads,
+                               int head_dim, int num_points, int loc_attn_channels, int dtype, void *stream)
 {
     dcnv4::clear_hip_error();
     fdattn::Problem p;
@@ -143,8 +183,14 @@ int flash_deform_attn_backward(const void *value, const int *spatial_shapes, int
     if (!value || !grad_value || (num_query > 0 && (!loc_attn || !grad_output || !grad_loc_attn)))
         return DCNV4_ERR_NULL;
     if (!aligned16(value) || !aligned16(loc_attn) || !aligned16(grad_output) || !aligned16(grad_value) ||
-        !aligned16(grad_loc_attn))
+        !aligned16(grad_loc_attn) || !aligned16(workspace))
         return DCNV4_ERR_ALIGN;
+    size_t need = 0;
+    if (workspace && num_query > 0) {
+        need = workspace_need(p, N, per_launch);
+        if (workspace_bytes < need)
+            return DCNV4_ERR_PARAM;
+    }
     const int64_t es = p.elem;
     const int64_t img_v = (int64_t)p.S * p.M * p.D * es, img_la = (int64_t)p.Q * p.M * p.P * es,
                   img_o = (int64_t)p.Q * p.M * p.D * es, img_gv = (int64_t)p.S * p.M * p.D * 4;
@@ -156,6 +202,15 @@ int flash_deform_attn_backward(const void *value, const int *spatial_shapes, int
     }
     if (overlap(grad_value, img_gv * N, grad_loc_attn, img_la * N))
         return DCNV4_ERR_PARAM;
+    if (need > 0) {
+        const int64_t nw = (int64_t)need;
+        for (int i = 0; i < 3; ++i) {
+            if (overlap(workspace, nw, ins[i], in_sz[i]))
+                return DCNV4_ERR_PARAM;
+        }
+        if (overlap(workspace, nw, grad_value, img_gv * N) || overlap(workspace, nw, grad_loc_attn, img_la * N))
+            return DCNV4_ERR_PARAM;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     for (int n0 = 0; n0 < N; n0 += per_launch) {
         fdattn::Problem q = p;
@@ -169,7 +224,8 @@ int flash_deform_attn_backward(const void *value, const int *spatial_shapes, int
                                         static_cast<const char *>(loc_attn) + img_la * n0,
                                         static_cast<const char *>(grad_output) + img_o * n0,
                                         reinterpret_cast<float *>(static_cast<char *>(grad_value) + img_gv * n0),
-                                        static_cast<char *>(grad_loc_attn) + img_la * n0, s);
+                                        static_cast<char *>(grad_loc_attn) + img_la * n0, need > 0 ? workspace : nullptr,
+                                        s);
         }
         if (e != hipSuccess)
             return dcnv4::hip_status(e);

@@ -22,11 +22,14 @@ struct Problem {
 };
 
 // Enqueue the forward / backward for images [0, p.N) (pointers already
-// offset to the launch's first image).  The backward zero-fills grad_value
-// first.  Return hipError_t.
+// offset to the launch's first image).  The backward sorts the samples in
+// `workspace` (workspace_bytes(p) bytes, 16-byte aligned) and gathers
+// grad_value; with workspace == nullptr it zero-fills grad_value and adds to
+// it with device atomics.  Return hipError_t.
+size_t workspace_bytes(const Problem &p);
 hipError_t launch_forward(const Problem &p, const void *value, const void *loc_attn, void *output,
                           hipStream_t stream);
 hipError_t launch_backward(const Problem &p, const void *value, const void *loc_attn, const void *grad_output,
-                           float *grad_value, void *grad_loc_attn, hipStream_t stream);
+                           float *grad_value, void *grad_loc_attn, void *workspace, hipStream_t stream);
 
 }  // namespace fdattn

@@ -17,9 +17,18 @@
 //   * Forward: D/8 lanes per unit, 8 channels per lane (the D' channels per
 //     thread and 128-bit loads of the walkthrough "DCNv4论文解析", section
 //     2.2); a corner is one (fp16/bf16) or two (fp32) 128-bit buffer loads.
-//   * Backward: D lanes per unit, one channel per lane, so the grad_value
-//     atomics of one corner cover D contiguous floats (coalesced device
-//     atomics); the location and logit gradients are lane sums (DPP).
+//   * Backward: D lanes per unit, one channel per lane; the location and
+//     logit gradients are lane sums (DPP).  grad_value takes one of two
+//     paths.  With a workspace it is a gather: one block per (image, head)
+//     slice counting-sorts the slice's live samples by the bin of their
+//     top-left corner cell in LDS (count with LDS atomics, scan, place a
+//     16-byte record per sample; the coarse levels put hundreds of samples
+//     on one bin, which device atomics would serialise), then every value
+//     cell sums the records of the four bins whose samples have it as a
+//     corner -- two runs of adjacent bins, eight records in flight at a time
+//     -- and is written once.  Without one (or when a slice's bins do not fit
+//     the LDS), every (sample, corner, channel) is a device fp32 atomic
+//     (N*Q*M*L*K*4*D of them), resolved beyond the L2 on this part.
 //   * Every corner outside its level's map gets an out-of-range buffer
 //     offset: its loads return 0 and its atomics are dropped by the buffer
 //     range check, exactly the zero padding of the definition.
@@ -32,6 +41,9 @@
 
 #include <algorithm>
 #include <climits>
+#include <mutex>
+#include <utility>
+#include <vector>
 
 namespace fdattn {
 namespace {
@@ -41,10 +53,13 @@ using dcnv4::dev::f32x2;
 using dcnv4::dev::f32x4;
 using dcnv4::dev::rsrc;
 using dcnv4::dev::Store;
+using dcnv4::dev::u32x2;
 using dcnv4::dev::u32x4;
 using dcnv4::dev::xcd_tile;
 
 constexpr unsigned kOutOfRange = 0x80000000u;   // beyond any launch's buffer
+constexpr int kSortThreads = 1024;               // one block per (image, head) slice
+constexpr size_t kSortLdsMax = 150 * 1024;       // bin counters of one slice, LDS bytes
 
 struct Args {
     const void *value;
@@ -60,7 +75,19 @@ struct Args {
     unsigned img_bytes;   // bytes of one image of value
     unsigned gv_img_bytes;
     unsigned pix_bytes;   // bytes of one value pixel (all heads)
+    int S;
     int lvl_h[kMaxLevels], lvl_w[kMaxLevels], lvl_start[kMaxLevels];
+    // sorted grad_value path: bins of top-left corner cells, (H_l + 1) x
+    // (W_l + 1) per level (rows and columns -1 .. size-1), nbs per slice
+    int nbs;
+    int lvl_bin[kMaxLevels];
+    unsigned *counts;     // [N*M*nbs]: counts, then bin ends
+    unsigned *starts;     // [N*M*nbs]: first record of each bin
+    unsigned *bases;      // [N*M*sb*nbs]: a sort block's offset inside each bin
+    unsigned *keys;       // [N*M*Q*L*K]: each sample's bin (or ~0u), in (n, m, q, i) order
+    f32x4 *urecs;         // [N*M*Q*L*K]: each sample's record, same order
+    f32x4 *recs;          // [N*M*Q*L*K]: (a*(1-ly), a*ly, lx, query), sorted by bin
+    int sb;               // sort blocks per slice
 };
 
 template <typename T>
@@ -128,6 +155,7 @@ struct Corners {
     unsigned o[4];
     float w[4];
     float ly, lx, hy, hx;
+    int r0, c0;
 };
 
 __device__ __forceinline__ Corners corners(float y, float x, int H, int W, int start, unsigned pix_bytes,
@@ -136,6 +164,8 @@ __device__ __forceinline__ Corners corners(float y, float x, int H, int W, int s
     Corners c;
     const float fy = floorf(y), fx = floorf(x);
     const int r0 = (int)fy, c0 = (int)fx;
+    c.r0 = r0;
+    c.c0 = c0;
     c.ly = y - fy;
     c.lx = x - fx;
     c.hy = 1.0f - c.ly;
@@ -348,8 +378,7 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd(Args a)
                     const unsigned go = c.o[q] == kOutOfRange
                                             ? kOutOfRange
                                             : (c.o[q] - vbase) / es * 4 + gbase;
-                    if (c.w[q] != 0.0f)
-                        dcnv4_buffer_atomic_fadd(ag * c.w[q], gr, (int)go, 0, 0);
+                    dcnv4_buffer_atomic_fadd(ag * c.w[q], gr, (int)go, 0, 0);
                 }
             }
             gs = unit_sum(gs, D);
@@ -371,6 +400,316 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd(Args a)
         grow[e] = Store<T>::make(0.0f);
 }
 
+// Location and logit gradients, plus each sample's bin and record for the
+// grad_value sort: the forward's mapping, U = D/8 lanes of 8 channels per
+// unit, 128-bit corner loads, lane sums of eight lanes or fewer by DPP, and
+// a branch-free sample loop (dead samples: out-of-range loads, results
+// selected to 0).  With ST the block's bins and records are staged in LDS
+// and written out as one contiguous range at the end (the units of a block
+// are consecutive); otherwise each goes straight to memory.
+template <typename T, int U, bool ST>
+__global__ __launch_bounds__(kThreads) void fdattn_bwd_loc(Args a)
+{
+    extern __shared__ f32x4 lds4[];
+    constexpr int es = (int)sizeof(T);
+    constexpr int upb = kThreads / U;
+    const int LK = a.LK;
+    char *lds = reinterpret_cast<char *>(lds4);
+    f32x4 *rec_lds = lds4;                                                            // [upb * LK] (ST)
+    unsigned *key_lds = reinterpret_cast<unsigned *>(lds + (ST ? upb * LK * 16 : 0));  // [upb * LK] (ST)
+    float *ga_lds = reinterpret_cast<float *>(lds + (ST ? upb * LK * 20 : 0));        // [upb * LK]
+    const int blk = xcd_tile(blockIdx.x, gridDim.x);
+    const int lu = (int)threadIdx.x / U;
+    const int lane = (int)threadIdx.x % U;
+    const int unit = blk * upb + lu;
+    // whole units are valid or not; lane sums stay inside a unit
+    if (unit < a.units) {
+    const int nm = unit / a.Q;
+    const int n = nm / a.M;
+    const int m = nm - n * a.M;
+    const size_t qrow = ((size_t)n * a.Q + (unit - nm * a.Q)) * a.M + m;   // (n, q, m) row
+    const T *row = static_cast<const T *>(a.loc_attn) + qrow * a.P;
+    T *grow = static_cast<T *>(a.grad_loc) + qrow * a.P;
+    float *ga = ga_lds + lu * LK;
+    float mx, inv;
+    softmax_stats(row + 2 * LK, LK, mx, inv);
+    float g[8];
+    {
+        const u32x4 *gp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.grad_out) + qrow * a.D + lane * 8);
+        const u32x4 g0 = gp[0];
+        const u32x4 g1 = es == 4 ? gp[1] : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 gv[2] = {g0, g1};
+        for (int e = 0; e < 8; ++e)
+            g[e] = Store<T>::get(gv, e);
+    }
+    const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, (int)a.value_bytes);
+    const unsigned base = (unsigned)n * a.img_bytes + (unsigned)((m * a.D + lane * 8) * es);
+    float dot = 0.0f;
+    for (int l = 0; l < a.L; ++l) {
+        const int H = a.lvl_h[l], W = a.lvl_w[l], start = a.lvl_start[l];
+        const float Hf = (float)H, Wf = (float)W;
+        const int i0 = l * a.K;
+#pragma unroll 4
+        for (int k = 0; k < a.K; ++k) {
+            const int i = i0 + k;
+            float u, v;
+            ld2(row + 2 * i, u, v);
+            const float x = __builtin_fmaf(u, Wf, -0.5f);
+            const float y = __builtin_fmaf(v, Hf, -0.5f);
+            const bool in = live(y, x, Hf, Wf);
+            const float att = expf(ld1(row + 2 * LK + i) - mx) * inv;
+            const Corners c = corners(y, x, H, W, start, a.pix_bytes, base);
+            float v0[8], v1[8], v2[8], v3[8];
+            load8<T>(vr, in ? c.o[0] : kOutOfRange, v0);
+            load8<T>(vr, in ? c.o[1] : kOutOfRange, v1);
+            load8<T>(vr, in ? c.o[2] : kOutOfRange, v2);
+            load8<T>(vr, in ? c.o[3] : kOutOfRange, v3);
+            float gs = 0.0f, gx = 0.0f, gy = 0.0f;
+            for (int e = 0; e < 8; ++e) {
+                const float sm = c.w[0] * v0[e] + c.w[1] * v1[e] + c.w[2] * v2[e] + c.w[3] * v3[e];
+                const float dxv = c.hy * (v1[e] - v0[e]) + c.ly * (v3[e] - v2[e]);
+                const float dyv = c.hx * (v2[e] - v0[e]) + c.lx * (v3[e] - v1[e]);
+                gs = __builtin_fmaf(g[e], sm, gs);
+                gx = __builtin_fmaf(g[e], dxv, gx);
+                gy = __builtin_fmaf(g[e], dyv, gy);
+            }
+            gs = unit_sum(in ? gs : 0.0f, U);
+            gx = unit_sum(in ? gx : 0.0f, U);
+            gy = unit_sum(in ? gy : 0.0f, U);
+            dot += att * gs;
+            if (lane == (i & (U - 1))) {
+                st2(grow + 2 * i, att * Wf * gx, att * Hf * gy);
+                ga[i] = gs;
+                // the sample's bin and record for the grad_value sort
+                const unsigned key = in ? (unsigned)(a.lvl_bin[l] + (c.r0 + 1) * (W + 1) + (c.c0 + 1)) : ~0u;
+                f32x4 rec;
+                rec[0] = att * c.hy;
+                rec[1] = att * c.ly;
+                rec[2] = c.lx;
+                rec[3] = __builtin_bit_cast(float, (unsigned)(unit - nm * a.Q));
+                if (ST) {
+                    key_lds[lu * LK + i] = key;
+                    rec_lds[lu * LK + i] = rec;
+                } else {
+                    const size_t si = (size_t)unit * LK + i;
+                    a.keys[si] = key;
+                    a.urecs[si] = rec;
+                }
+            }
+        }
+    }
+    // logits: a_i (g_i - sum_j a_j g_j); lane i % U wrote ga[i] itself
+    for (int j = lane; j < LK; j += U) {
+        const float att = expf(ld1(row + 2 * LK + j) - mx) * inv;
+        grow[2 * LK + j] = Store<T>::make(att * (ga[j] - dot));
+    }
+    for (int e = 3 * LK + lane; e < a.P; e += U)
+        grow[e] = Store<T>::make(0.0f);
+    }
+    if (ST) {
+        __syncthreads();
+        const int u0 = blk * upb;
+        const int nv = min(upb, a.units - u0) * LK;
+        const size_t si0 = (size_t)u0 * LK;
+        for (int t = (int)threadIdx.x; t < nv; t += kThreads) {
+            a.keys[si0 + t] = key_lds[t];
+            a.urecs[si0 + t] = rec_lds[t];
+        }
+    }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then
+// row broadcasts; lanes without a source add 0).
+__device__ __forceinline__ unsigned wave_prefix(unsigned v)
+{
+    int x = (int)v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return (unsigned)x;
+}
+
+// The sort of the sorted grad_value path: a slice's queries are split over
+// `sb` blocks; bins are the top-left corner cells, nbs per slice.
+//   fdattn_count: each block counts its samples per bin in LDS, then adds
+//     every non-zero count to the slice's global count with one device
+//     atomic, whose returned value is the block's offset inside the bin.
+//   fdattn_scan:  one block per slice turns the global counts into bin
+//     starts (offset by the slice's first record slot, slice * Q * L * K)
+//     and ends.
+//   fdattn_place: each block starts its LDS cursors at bin start + its
+//     offset and writes one record per sample.
+// The coarse levels put hundreds of samples on one bin; the LDS atomics take
+// those, and the device atomics see at most sb per bin.
+
+// Samples [s0, s1) of block `sbi` of a slice, as indices into keys / urecs.
+__device__ __forceinline__ void sort_range(const Args &a, int slice, int sbi, size_t &s0, size_t &s1)
+{
+    const size_t n = (size_t)a.Q * a.LK, per = (n + a.sb - 1) / a.sb;
+    const size_t first = (size_t)slice * n;
+    s0 = first + std::min(n, sbi * per);
+    s1 = first + std::min(n, sbi * per + per);
+}
+
+__global__ __launch_bounds__(kSortThreads) void fdattn_count(Args a)
+{
+    extern __shared__ unsigned bins[];   // [nbs]
+    const int slice = blockIdx.x / a.sb, sbi = blockIdx.x - slice * a.sb;
+    const int tid = (int)threadIdx.x;
+    for (int i = tid; i < a.nbs; i += kSortThreads)
+        bins[i] = 0u;
+    __syncthreads();
+    size_t s0, s1;
+    sort_range(a, slice, sbi, s0, s1);
+    for (size_t si = s0 + tid; si < s1; si += kSortThreads) {
+        const unsigned b = a.keys[si];
+        if (b != ~0u)
+            __hip_atomic_fetch_add(bins + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    unsigned *gcount = a.counts + (size_t)slice * a.nbs;
+    unsigned *base = a.bases + ((size_t)slice * a.sb + sbi) * a.nbs;
+    for (int i = tid; i < a.nbs; i += kSortThreads) {
+        const unsigned c = bins[i];
+        if (c)
+            base[i] = __hip_atomic_fetch_add(gcount + i, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+__global__ __launch_bounds__(kSortThreads) void fdattn_scan(Args a)
+{
+    __shared__ unsigned wsum[kSortThreads / 64];
+    const int slice = blockIdx.x;
+    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    unsigned *cnt = a.counts + (size_t)slice * a.nbs;   // counts in, bin ends out
+    unsigned *st = a.starts + (size_t)slice * a.nbs;
+    unsigned carry = (unsigned)slice * (unsigned)(a.Q * a.LK);
+    for (int base = 0; base < a.nbs; base += 4 * kSortThreads) {
+        const int i0 = base + 4 * tid;
+        unsigned c[4];
+        for (int e = 0; e < 4; ++e)
+            c[e] = i0 + e < a.nbs ? cnt[i0 + e] : 0u;
+        const unsigned mine = c[0] + c[1] + c[2] + c[3];
+        const unsigned x = wave_prefix(mine);
+        if (lane == 63)
+            wsum[wave] = x;
+        __syncthreads();
+        unsigned off = carry, tot = 0;
+        for (int w = 0; w < kSortThreads / 64; ++w) {
+            off += w < wave ? wsum[w] : 0u;
+            tot += wsum[w];
+        }
+        unsigned e0 = off + x - mine;
+        for (int e = 0; e < 4; ++e) {
+            if (i0 + e < a.nbs) {
+                st[i0 + e] = e0;
+                cnt[i0 + e] = e0 + c[e];
+            }
+            e0 += c[e];
+        }
+        carry += tot;
+        __syncthreads();   // wsum is rewritten by the next round
+    }
+}
+
+__global__ __launch_bounds__(kSortThreads) void fdattn_place(Args a)
+{
+    extern __shared__ unsigned cursor[];   // [nbs]
+    const int slice = blockIdx.x / a.sb, sbi = blockIdx.x - slice * a.sb;
+    const int tid = (int)threadIdx.x;
+    // bins this block has no sample in get a meaningless cursor (their
+    // offset entry was never written) and are never used
+    const unsigned *st = a.starts + (size_t)slice * a.nbs;
+    const unsigned *base = a.bases + ((size_t)slice * a.sb + sbi) * a.nbs;
+    for (int i = tid; i < a.nbs; i += kSortThreads)
+        cursor[i] = st[i] + base[i];
+    __syncthreads();
+    size_t s0, s1;
+    sort_range(a, slice, sbi, s0, s1);
+    for (size_t si = s0 + tid; si < s1; si += kSortThreads) {
+        const unsigned b = a.keys[si];
+        if (b != ~0u) {
+            const unsigned idx = __hip_atomic_fetch_add(cursor + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            a.recs[idx] = a.urecs[si];
+        }
+    }
+}
+
+// D lanes per value cell (one channel each): the cell is the top-left,
+// top-right, bottom-left and bottom-right corner of the samples in bins
+// (r, c), (r, c-1), (r-1, c) and (r-1, c-1); bins (r, c-1), (r, c) and
+// (r-1, c-1), (r-1, c) are adjacent, so the cell reads two runs.  A run is
+// read D records at a time, one per lane (coalesced), each reduced to (its
+// weight for this cell, its query) and staged in LDS, from where the unit's
+// lanes read them back as broadcasts.  Every cell is written once (no fill).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void fdattn_gather(Args a)
+{
+    extern __shared__ f32x2 stage_lds[];   // [units per block][D]: (weight, query)
+    const int D = a.D;
+    const int upb = kThreads / D;
+    const int blk = xcd_tile(blockIdx.x, gridDim.x);
+    const int lu = (int)threadIdx.x / D;
+    const int lane = (int)threadIdx.x - lu * D;
+    const int unit = blk * upb + lu;
+    const int cells = a.units / a.Q * a.S;   // N*M*S
+    if (unit >= cells)
+        return;
+    f32x2 *stage = stage_lds + lu * D;
+    const int slice = unit / a.S;
+    const int s = unit - slice * a.S;
+    const int n = slice / a.M;
+    const int m = slice - n * a.M;
+    int l = 0;
+    while (l + 1 < a.L && s >= a.lvl_start[l + 1])
+        ++l;
+    const int W = a.lvl_w[l];
+    const int rc = s - a.lvl_start[l];
+    const int r = rc / W, c = rc - r * W;
+    const size_t bin_lc = (size_t)slice * a.nbs + a.lvl_bin[l] + (size_t)(r + 1) * (W + 1) + c;   // bin (r, c-1)
+    const size_t bin_ulc = bin_lc - (W + 1);                                                         // bin (r-1, c-1)
+    const T *gq = static_cast<const T *>(a.grad_out) + (size_t)n * a.Q * a.M * D + m * D + lane;
+    const size_t qstride = (size_t)a.M * D;
+    float acc = 0.0f;
+    // run of bins b, b + 1: records of b have this cell as their right
+    // column (weight lx), those of b + 1 as their left column (1 - lx);
+    // row_part picks the weight of the records' upper or lower row
+    auto run = [&](size_t b, int row_part) {
+        const unsigned s0 = a.starts[b], mid = a.counts[b], e = a.counts[b + 1];
+        for (unsigned base = s0; base < e; base += (unsigned)D) {
+            const unsigned idx = base + (unsigned)lane;
+            f32x2 mine = {0.0f, 0.0f};
+            if (idx < e) {
+                const f32x4 rec = a.recs[idx];
+                const float wy = row_part == 0 ? rec[0] : rec[1];
+                mine[0] = wy * (idx < mid ? rec[2] : 1.0f - rec[2]);
+                mine[1] = rec[3];   // the query, as bits
+            }
+            // the unit's lanes are one wave: LDS accesses of a wave are
+            // performed in order, the barrier only keeps the compiler's order
+            __builtin_amdgcn_wave_barrier();
+            stage[lane] = mine;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int cnt = (int)min((unsigned)D, e - base);
+#pragma unroll 4
+            for (int t = 0; t < cnt; ++t) {
+                const f32x2 wq = stage[t];
+                const unsigned q = __builtin_bit_cast(u32x2, wq)[1];   // whole-vector cast, then index
+                acc = __builtin_fmaf(wq[0], ld1(gq + q * qstride), acc);
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    };
+    run(bin_lc, 0);    // bins (r, c-1), (r, c): the cell is in the records' upper row
+    run(bin_ulc, 1);   // bins (r-1, c-1), (r-1, c): the cell is in their lower row
+    a.grad_value[((size_t)n * a.S + s) * qstride + m * D + lane] = acc;
+}
+
 Args make_args(const Problem &p)
 {
     Args a;
@@ -387,11 +726,26 @@ Args make_args(const Problem &p)
     a.gv_img_bytes = (unsigned)p.S * (unsigned)(p.M * p.D * 4);
     a.value_bytes = a.img_bytes * (unsigned)p.N;
     a.gv_bytes = a.gv_img_bytes * (unsigned)p.N;
+    a.S = p.S;
+    a.nbs = 0;
     for (int l = 0; l < kMaxLevels; ++l) {
         a.lvl_h[l] = l < p.L ? p.lvl_h[l] : 0;
         a.lvl_w[l] = l < p.L ? p.lvl_w[l] : 0;
         a.lvl_start[l] = l < p.L ? p.lvl_start[l] : 0;
+        a.lvl_bin[l] = a.nbs;
+        if (l < p.L)
+            a.nbs += (p.lvl_h[l] + 1) * (p.lvl_w[l] + 1);
     }
+    a.counts = nullptr;
+    a.starts = nullptr;
+    a.bases = nullptr;
+    a.keys = nullptr;
+    a.urecs = nullptr;
+    a.recs = nullptr;
+    // enough sort blocks to give every CU one (one block per CU fits the
+    // bin counters), at most 16 per slice
+    const int slices = p.N * p.M;
+    a.sb = std::max(1, std::min(16, std::min(p.Q, (256 + slices - 1) / std::max(1, slices))));
     return a;
 }
 
@@ -412,13 +766,90 @@ hipError_t launch_fwd_t(const Args &a, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Dynamic LDS above 64 KB needs the kernel's limit raised once (gfx950 has
+// 160 KB per CU); remembered per kernel.
+hipError_t set_lds_limit(const void *fn, size_t bytes)
+{
+    if (bytes <= 64 * 1024)
+        return hipSuccess;
+    static std::mutex mu;
+    static std::vector<std::pair<const void *, size_t>> done;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto &d : done)
+        if (d.first == fn && d.second >= bytes)
+            return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess)
+        done.emplace_back(fn, bytes);
+    return e;
+}
+
+template <typename T, bool ST>
+hipError_t launch_bwd_loc_st(const Args &a, int blocks, size_t lds, hipStream_t stream)
+{
+    switch (a.D / 8) {
+    case 1: hipLaunchKernelGGL((fdattn_bwd_loc<T, 1, ST>), dim3(blocks), dim3(kThreads), lds, stream, a); break;
+    case 2: hipLaunchKernelGGL((fdattn_bwd_loc<T, 2, ST>), dim3(blocks), dim3(kThreads), lds, stream, a); break;
+    case 4: hipLaunchKernelGGL((fdattn_bwd_loc<T, 4, ST>), dim3(blocks), dim3(kThreads), lds, stream, a); break;
+    case 8: hipLaunchKernelGGL((fdattn_bwd_loc<T, 8, ST>), dim3(blocks), dim3(kThreads), lds, stream, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_bwd_loc_t(const Args &a, hipStream_t stream)
+{
+    const int upb = kThreads / (a.D / 8);
+    const int blocks = (a.units + upb - 1) / upb;
+    const size_t ga = (size_t)upb * a.LK * sizeof(float);
+    const size_t staged = ga + (size_t)upb * a.LK * (sizeof(unsigned) + sizeof(f32x4));
+    if (staged <= 64 * 1024)
+        return launch_bwd_loc_st<T, true>(a, blocks, staged, stream);
+    return launch_bwd_loc_st<T, false>(a, blocks, ga, stream);
+}
+
+// The sorted grad_value path applies when a slice's bin counters fit the LDS.
+bool sort_fits(const Args &a)
+{
+    return (size_t)a.nbs * sizeof(unsigned) <= kSortLdsMax;
+}
+
 template <typename T>
 hipError_t launch_bwd_t(const Args &a, hipStream_t stream)
 {
     const int upb = kThreads / a.D;
     const int blocks = (a.units + upb - 1) / upb;
     const size_t lds = (size_t)upb * a.LK * sizeof(float);
-    hipLaunchKernelGGL((fdattn_bwd<T>), dim3(blocks), dim3(kThreads), lds, stream, a);
+    if (!a.recs) {
+        hipLaunchKernelGGL((fdattn_bwd<T>), dim3(blocks), dim3(kThreads), lds, stream, a);
+        return hipGetLastError();
+    }
+    hipError_t e = launch_bwd_loc_t<T>(a, stream);
+    if (e != hipSuccess)
+        return e;
+    const int slices = a.units / a.Q;
+    const size_t sort_lds = (size_t)a.nbs * sizeof(unsigned);
+    e = set_lds_limit(reinterpret_cast<const void *>(&fdattn_count), sort_lds);
+    if (e == hipSuccess)
+        e = set_lds_limit(reinterpret_cast<const void *>(&fdattn_place), sort_lds);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(fdattn_count, dim3(slices * a.sb), dim3(kSortThreads), sort_lds, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(fdattn_scan, dim3(slices), dim3(kSortThreads), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(fdattn_place, dim3(slices * a.sb), dim3(kSortThreads), sort_lds, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int cells = slices * a.S;
+    hipLaunchKernelGGL((fdattn_gather<T>), dim3((cells + upb - 1) / upb), dim3(kThreads),
+                       (size_t)kThreads * sizeof(f32x2), stream, a);
     return hipGetLastError();
 }
 
@@ -439,8 +870,20 @@ hipError_t launch_forward(const Problem &p, const void *value, const void *loc_a
     }
 }
 
+size_t workspace_bytes(const Problem &p)
+{
+    const Args a = make_args(p);
+    if (!sort_fits(a))
+        return 0;   // the atomic path: no workspace
+    // counts/ends, starts, per-block offsets, records; whole 256-byte blocks
+    const size_t nb = ((size_t)p.N * p.M * a.nbs + 63) / 64 * 64;
+    const size_t nbb = ((size_t)p.N * p.M * a.sb * a.nbs + 63) / 64 * 64;
+    const size_t ns = ((size_t)p.N * p.M * p.Q * p.L * p.K + 63) / 64 * 64;   // samples
+    return (2 * nb + nbb + ns) * sizeof(unsigned) + 2 * ns * sizeof(f32x4);
+}
+
 hipError_t launch_backward(const Problem &p, const void *value, const void *loc_attn, const void *grad_output,
-                           float *grad_value, void *grad_loc_attn, hipStream_t stream)
+                           float *grad_value, void *grad_loc_attn, void *workspace, hipStream_t stream)
 {
     Args a = make_args(p);
     a.value = value;
@@ -448,9 +891,26 @@ hipError_t launch_backward(const Problem &p, const void *value, const void *loc_
     a.grad_out = grad_output;
     a.grad_value = grad_value;
     a.grad_loc = grad_loc_attn;
-    hipError_t e = dcnv4::launch_zero(grad_value, (size_t)a.gv_bytes, stream);
-    if (e != hipSuccess)
-        return e;
+    if (workspace && sort_fits(a)) {
+        const size_t nb = ((size_t)p.N * p.M * a.nbs + 63) / 64 * 64;
+        const size_t nbb = ((size_t)p.N * p.M * a.sb * a.nbs + 63) / 64 * 64;
+        const size_t ns = ((size_t)p.N * p.M * p.Q * p.L * p.K + 63) / 64 * 64;
+        a.counts = static_cast<unsigned *>(workspace);
+        a.starts = a.counts + nb;
+        a.bases = a.starts + nb;
+        a.keys = a.bases + nbb;
+        a.urecs = reinterpret_cast<f32x4 *>(a.keys + ns);
+        a.recs = a.urecs + ns;
+        // the global counts start at zero (the per-block offsets and bin
+        // starts are written before they are read)
+        const hipError_t e = dcnv4::launch_zero(a.counts, nb * sizeof(unsigned), stream);
+        if (e != hipSuccess)
+            return e;
+    } else {
+        const hipError_t e = dcnv4::launch_zero(grad_value, (size_t)a.gv_bytes, stream);
+        if (e != hipSuccess)
+            return e;
+    }
     switch (p.dtype) {
     case 0: return launch_bwd_t<float>(a, stream);
     case 1: return launch_bwd_t<_Float16>(a, stream);

@@ -70,8 +70,10 @@ def load() -> ctypes.CDLL:
     lib.flash_deform_attn_channels.restype = i
     lib.flash_deform_attn_forward.argtypes = [p, ip, i, p, p] + dims
     lib.flash_deform_attn_forward.restype = i
-    lib.flash_deform_attn_backward.argtypes = [p, ip, i, p, p, p, p] + dims
+    lib.flash_deform_attn_backward.argtypes = [p, ip, i, p, p, p, p, p, ctypes.c_size_t] + dims
     lib.flash_deform_attn_backward.restype = i
+    lib.flash_deform_attn_backward_workspace.argtypes = [ip, i] + [i] * 8 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.flash_deform_attn_backward_workspace.restype = i
     _lib = lib
     return lib
 

@@ -47,10 +47,27 @@ def flash_deform_attn_forward(value, spatial_shapes, loc_attn, output, *, num_po
         raise Dcnv4Error(st, "flash_deform_attn_forward")
 
 
+def flash_deform_attn_backward_workspace(value, spatial_shapes, loc_attn, *, num_points) -> int:
+    """Workspace bytes the sorted grad_value path needs for these tensors."""
+    N, S, M, D = value.shape
+    Q, P = loc_attn.shape[1], loc_attn.shape[3]
+    arr, L = _shapes_arg(spatial_shapes)
+    nbytes = ctypes.c_size_t()
+    st = load().flash_deform_attn_backward_workspace(arr, L, N, S, Q, M, D, int(num_points), P,
+                                                     _dtype_code(value), ctypes.byref(nbytes))
+    if st != DCNV4_OK:
+        raise Dcnv4Error(st, "flash_deform_attn_backward_workspace")
+    return nbytes.value
+
+
 def flash_deform_attn_backward(value, spatial_shapes, loc_attn, grad_output, grad_value, grad_loc_attn, *,
-                               num_points, stream=None) -> None:
+                               num_points, workspace=None, stream=None) -> None:
     """Backward into caller-allocated grad_value (N,S,M,D) float32 and
-    grad_loc_attn (N,Q,M,P) in the inputs' dtype (both overwritten)."""
+    grad_loc_attn (N,Q,M,P) in the inputs' dtype (both overwritten).
+
+    ``workspace``: a device tensor of at least
+    ``flash_deform_attn_backward_workspace`` bytes selects the sorted
+    (gather) grad_value path; None selects the device-atomic path."""
     import torch
 
     for t, nm in ((value, "value"), (loc_attn, "loc_attn"), (grad_output, "grad_output"),
@@ -59,14 +76,18 @@ def flash_deform_attn_backward(value, spatial_shapes, loc_attn, grad_output, gra
         want = torch.float32 if nm == "grad_value" else value.dtype
         if t.dtype != want:
             raise TypeError(f"{nm} dtype {t.dtype} != {want}")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _check(workspace, "workspace")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     N, S, M, D = value.shape
     Q, P = loc_attn.shape[1], loc_attn.shape[3]
     arr, L = _shapes_arg(spatial_shapes)
     st = load().flash_deform_attn_backward(
         ctypes.c_void_p(value.data_ptr()), arr, L, ctypes.c_void_p(loc_attn.data_ptr()),
         ctypes.c_void_p(grad_output.data_ptr()), ctypes.c_void_p(grad_value.data_ptr()),
-        ctypes.c_void_p(grad_loc_attn.data_ptr()), N, S, Q, M, D, int(num_points), P,
-        _dtype_code(value), _stream_ptr(stream))
+        ctypes.c_void_p(grad_loc_attn.data_ptr()), ctypes.c_void_p(ws_ptr), ws_bytes, N, S, Q, M, D,
+        int(num_points), P, _dtype_code(value), _stream_ptr(stream))
     if st != DCNV4_OK:
         raise Dcnv4Error(st, "flash_deform_attn_backward")
 
@@ -81,12 +102,24 @@ def forward(value, spatial_shapes, loc_attn, num_points):
     return out
 
 
-def backward(value, spatial_shapes, loc_attn, grad_output, num_points):
-    """Allocate grad_value (fp32) and grad_loc_attn with torch and call the
-    backward."""
+def workspace_for(value, spatial_shapes, loc_attn, num_points):
+    """A torch-allocated workspace for the sorted backward (None if empty)."""
+    import torch
+
+    nbytes = flash_deform_attn_backward_workspace(value, spatial_shapes, loc_attn, num_points=num_points)
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=value.device)
+
+
+def backward(value, spatial_shapes, loc_attn, grad_output, num_points, sorted_grad_value=True):
+    """Allocate grad_value (fp32), grad_loc_attn and (for the sorted path)
+    the workspace with torch and call the backward."""
     import torch
 
     gv = torch.empty(value.shape, dtype=torch.float32, device=value.device)
     gla = torch.empty_like(loc_attn)
-    flash_deform_attn_backward(value, spatial_shapes, loc_attn, grad_output, gv, gla, num_points=num_points)
+    ws = workspace_for(value, spatial_shapes, loc_attn, num_points) if sorted_grad_value else None
+    flash_deform_attn_backward(value, spatial_shapes, loc_attn, grad_output, gv, gla, num_points=num_points,
+                               workspace=ws)
     return gv, gla

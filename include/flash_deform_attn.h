@@ -48,6 +48,8 @@
 #ifndef FLASH_DEFORM_ATTN_H
 #define FLASH_DEFORM_ATTN_H
 
+#include <stddef.h>
+
 #include "dcnv4.h"
 
 #ifdef __cplusplus
@@ -87,6 +89,18 @@ DCNV4_API int flash_deform_attn_forward(const void *value, const int *spatial_sh
                                         int dtype, void *stream);
 
 /*
+ * Bytes of the workspace that flash_deform_attn_backward's sorted grad_value
+ * path needs for these arguments (0 when N or Q is 0): 2 x 4 bytes per
+ * corner bin ((H_l + 1) x (W_l + 1) bins per level, image and head) plus 16
+ * bytes per (query, head, point), for the largest launch the call is split
+ * into.  Writes *bytes.  Errors: NULL, and the argument errors of
+ * flash_deform_attn_backward.
+ */
+DCNV4_API int flash_deform_attn_backward_workspace(const int *spatial_shapes, int num_levels, int N, int num_value,
+                                                   int num_query, int num_heads, int head_dim, int num_points,
+                                                   int loc_attn_channels, int dtype, size_t *bytes);
+
+/*
  * Backward of flash_deform_attn_forward (chain rule of the operation above):
  *
  *   grad_value[corner]       = sum over samples of a * bilinear weight * grad_output
@@ -100,16 +114,27 @@ DCNV4_API int flash_deform_attn_forward(const void *value, const int *spatial_sh
  *   grad_value     (N, S, M, D)  fp32 for every dtype, written (overwritten)
  *   grad_loc_attn  (N, Q, M, P)  dtype, written; padding entries 0
  *
- * grad_loc_attn is deterministic.  grad_value is summed with device atomics
- * in an order that depends on thread timing, so its last bits may differ
+ *   workspace      device memory of at least
+ *                  flash_deform_attn_backward_workspace() bytes, 16-byte
+ *                  aligned, owned by the caller, overwritten (its contents
+ *                  are meaningless afterwards); or NULL
+ *
+ * With a workspace, grad_value is a gather: the samples are counting-sorted
+ * by the cell of their top-left corner and every value cell sums its own
+ * samples (atomic-free for floats; the sort uses integer device atomics).
+ * With workspace == NULL every (sample, corner, channel) contribution is a
+ * device fp32 atomic add into grad_value (about 8x slower at the measured
+ * sizes).  grad_loc_attn is deterministic.  grad_value is summed in an order
+ * that depends on thread timing on both paths, so its last bits may differ
  * from run to run.  Errors: as the forward, with UNSUPPORTED for D not in
- * {8, 16, 32, 64}.
+ * {8, 16, 32, 64}; PARAM also for a workspace smaller than required or
+ * overlapping another buffer; OVERFLOW also for Q*M*L*K above 2^31.
  */
 DCNV4_API int flash_deform_attn_backward(const void *value, const int *spatial_shapes, int num_levels,
                                          const void *loc_attn, const void *grad_output, void *grad_value,
-                                         void *grad_loc_attn, int N, int num_value, int num_query, int num_heads,
-                                         int head_dim, int num_points, int loc_attn_channels, int dtype,
-                                         void *stream);
+                                         void *grad_loc_attn, void *workspace, size_t workspace_bytes, int N,
+                                         int num_value, int num_query, int num_heads, int head_dim, int num_points,
+                                         int loc_attn_channels, int dtype, void *stream);
 
 #ifdef __cplusplus
 }

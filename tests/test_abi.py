@@ -35,7 +35,8 @@ def test_header_declares_the_abi():
         "dcnv4_abi_version", "dcnv4_status_string", "dcnv4_last_hip_error",
         "dcnv4_output_size", "dcnv4_om_channels", "dcnv4_forward", "dcnv4_backward",
         "dcnv4_forward_ex", "dcnv4_backward_ex",
-        "flash_deform_attn_channels", "flash_deform_attn_forward", "flash_deform_attn_backward"])
+        "flash_deform_attn_channels", "flash_deform_attn_forward", "flash_deform_attn_backward",
+        "flash_deform_attn_backward_workspace"])
 
 
 def test_library_exports_every_declared_symbol():

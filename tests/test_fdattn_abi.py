@@ -26,10 +26,22 @@ def fwd(ptrs=(A, B, Cp), shapes=SHAPES, L=None, N=2, S=100, Q=7, M=2, Dh=32, K=4
                                                   N, S, Q, M, Dh, K, P, dtype, None)
 
 
-def bwd(ptrs=(A, B, Cp, D, E), shapes=SHAPES, L=None, N=2, S=100, Q=7, M=2, Dh=32, K=4, P=24, dtype=0):
+F = ctypes.c_void_p(0x600000000)   # workspace
+
+
+def bwd(ptrs=(A, B, Cp, D, E), shapes=SHAPES, L=None, N=2, S=100, Q=7, M=2, Dh=32, K=4, P=24, dtype=0,
+        ws=None, ws_bytes=0):
     arr, nl = shapes_arr(shapes)
     return dcnv4.load().flash_deform_attn_backward(ptrs[0], arr, nl if L is None else L, ptrs[1], ptrs[2],
-                                                   ptrs[3], ptrs[4], N, S, Q, M, Dh, K, P, dtype, None)
+                                                   ptrs[3], ptrs[4], ws, ws_bytes, N, S, Q, M, Dh, K, P, dtype,
+                                                   None)
+
+
+def ws_bytes(shapes=SHAPES, N=2, S=100, Q=7, M=2, Dh=32, K=4, P=24, dtype=0):
+    arr, nl = shapes_arr(shapes)
+    out = ctypes.c_size_t()
+    st = dcnv4.load().flash_deform_attn_backward_workspace(arr, nl, N, S, Q, M, Dh, K, P, dtype, ctypes.byref(out))
+    return st, out.value
 
 
 def test_channels():
@@ -89,4 +101,27 @@ def test_pointer_checks():
 def test_null_shapes():
     lib = dcnv4.load()
     assert lib.flash_deform_attn_forward(A, None, 2, B, Cp, 2, 100, 7, 2, 32, 4, 24, 0, None) == NULL
-    assert lib.flash_deform_attn_backward(A, None, 2, B, Cp, D, E, 2, 100, 7, 2, 32, 4, 24, 0, None) == NULL
+    assert lib.flash_deform_attn_backward(A, None, 2, B, Cp, D, E, None, 0, 2, 100, 7, 2, 32, 4, 24, 0, None) == NULL
+    out = ctypes.c_size_t()
+    assert lib.flash_deform_attn_backward_workspace(None, 2, 2, 100, 7, 2, 32, 4, 24, 0, ctypes.byref(out)) == NULL
+    arr, nl = shapes_arr(SHAPES)
+    assert lib.flash_deform_attn_backward_workspace(arr, nl, 2, 100, 7, 2, 32, 4, 24, 0, None) == NULL
+
+
+def test_workspace_size_and_checks():
+    # bins: (8+1)*(10+1) + (4+1)*(5+1) = 129 per (image, head); 2 images x 2
+    # heads -> 516, rounded up to 576 entries, twice (counts, starts); the
+    # sort splits each slice over min(16, Q, ceil(256 / slices)) = 7 blocks,
+    # each with its own offsets: 4 * 7 * 129 = 3612 -> 3648 entries; 4 bytes
+    # each; per sample (2 * 2 * 7 * 2 * 4 = 224 -> 256 entries) a 4-byte key
+    # and two 16-byte records (unsorted, sorted)
+    st, n = ws_bytes()
+    assert st == OK
+    assert n == (2 * 576 + 3648 + 256) * 4 + 2 * 256 * 16
+    assert ws_bytes(N=0) == (OK, 0)
+    assert ws_bytes(Q=0) == (OK, 0)
+    assert ws_bytes(Dh=12)[0] == UNSUP
+    assert bwd(ws=F, ws_bytes=n - 1) == PARAM                              # too small
+    assert bwd(ws=ctypes.c_void_p(0x600000008), ws_bytes=n) == ALIGN
+    assert bwd(ws=ctypes.c_void_p(0x100000000 + 64), ws_bytes=n) == PARAM  # overlaps value
+    assert bwd(ws=ctypes.c_void_p(0x400000000 + 64), ws_bytes=n) == PARAM  # overlaps grad_value

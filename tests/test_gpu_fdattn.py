@@ -74,7 +74,7 @@ def to_dev(arrs, dtype):
     return out
 
 
-def run_case(w: FdaWorkload, N=None, backward=True, la_override=None):
+def run_case(w: FdaWorkload, N=None, backward=True, la_override=None, sorted_grad_value=True):
     v32, la32, g32 = w.make_inputs(N=N)
     if la_override is not None:
         la32 = la_override(la32)
@@ -85,7 +85,7 @@ def run_case(w: FdaWorkload, N=None, backward=True, la_override=None):
     check(out.float().cpu().numpy(), ref, w.dtype, f"{w.name} output")
     if not backward:
         return
-    gv, gla = fda.backward(v, w.shapes, la, g, w.K)
+    gv, gla = fda.backward(v, w.shapes, la, g, w.K, sorted_grad_value=sorted_grad_value)
     torch.cuda.synchronize()
     rgv, rgla = oracle.fdattn_backward(vr, w.shapes, lar, gr, w.K)
     LK = w.L * w.K
@@ -130,6 +130,16 @@ def test_parity(w):
     run_case(w)
 
 
+ATOMIC_CASES = [c for c in CASES if c.name in ("d32_fp32", "spread_fp32", "l16k8_fp32", "d16_bf16")]
+
+
+@pytest.mark.parametrize("w", ATOMIC_CASES, ids=[c.name for c in ATOMIC_CASES])
+def test_parity_atomic_grad_value(w):
+    """The backward without a workspace (grad_value by device atomics)."""
+    say(f"[fdattn] {w.name} atomic grad_value path")
+    run_case(w, sorted_grad_value=False)
+
+
 def test_forward_head_dim_128():
     w = _w("d128_fp32", D=128, M=2, Q=21)
     say(f"[fdattn] {w.name} forward only (the backward takes D <= 64)")
@@ -160,6 +170,9 @@ def test_boundary_and_non_finite_locations():
 
     say(f"[fdattn] {w.name}: border, out-of-map and NaN locations")
     run_case(w, la_override=override)
+    rng = np.random.default_rng(5)
+    say(f"[fdattn] {w.name}: the same, atomic grad_value path")
+    run_case(w, la_override=override, sorted_grad_value=False)
 
 
 def test_empty_query_set_zeroes_grad_value():
