@@ -75,6 +75,7 @@ struct Args {
     unsigned img_bytes;   // bytes of one image of value
     unsigned gv_img_bytes;
     unsigned pix_bytes;   // bytes of one value pixel (all heads)
+    int elem_bytes;       // bytes of the storage type
     int S;
     int lvl_h[kMaxLevels], lvl_w[kMaxLevels], lvl_start[kMaxLevels];
     // sorted grad_value path: bins of top-left corner cells, (H_l + 1) x
@@ -418,6 +419,7 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd_loc(Args a)
     f32x4 *rec_lds = lds4;                                                            // [upb * LK] (ST)
     unsigned *key_lds = reinterpret_cast<unsigned *>(lds + (ST ? upb * LK * 16 : 0));  // [upb * LK] (ST)
     float *ga_lds = reinterpret_cast<float *>(lds + (ST ? upb * LK * 20 : 0));        // [upb * LK]
+    T *grow_lds = reinterpret_cast<T *>(lds + upb * LK * (ST ? 24 : 4));              // [upb * P] (ST)
     const int blk = xcd_tile(blockIdx.x, gridDim.x);
     const int lu = (int)threadIdx.x / U;
     const int lane = (int)threadIdx.x % U;
@@ -429,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd_loc(Args a)
     const int m = nm - n * a.M;
     const size_t qrow = ((size_t)n * a.Q + (unit - nm * a.Q)) * a.M + m;   // (n, q, m) row
     const T *row = static_cast<const T *>(a.loc_attn) + qrow * a.P;
-    T *grow = static_cast<T *>(a.grad_loc) + qrow * a.P;
+    T *grow = ST ? grow_lds + lu * a.P : static_cast<T *>(a.grad_loc) + qrow * a.P;
     float *ga = ga_lds + lu * LK;
     float mx, inv;
     softmax_stats(row + 2 * LK, LK, mx, inv);
@@ -509,11 +511,24 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd_loc(Args a)
     if (ST) {
         __syncthreads();
         const int u0 = blk * upb;
-        const int nv = min(upb, a.units - u0) * LK;
+        const int nu = min(upb, a.units - u0);
+        const int nv = nu * LK;
         const size_t si0 = (size_t)u0 * LK;
         for (int t = (int)threadIdx.x; t < nv; t += kThreads) {
             a.keys[si0 + t] = key_lds[t];
             a.urecs[si0 + t] = rec_lds[t];
+        }
+        // the units' gradient rows, whole 16-byte vectors (rows are
+        // contiguous, one per unit, at (n, q, m))
+        const int rv = a.P * es / 16;
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(grow_lds);
+        for (int t = (int)threadIdx.x; t < nu * rv; t += kThreads) {
+            const int u = t / rv, v = t - u * rv;
+            const int un = u0 + u;
+            const int unm = un / a.Q;
+            const int un_n = unm / a.M;
+            const size_t r = ((size_t)un_n * a.Q + (un - unm * a.Q)) * a.M + (unm - un_n * a.M);
+            reinterpret_cast<u32x4 *>(static_cast<T *>(a.grad_loc) + r * a.P)[v] = src[u * rv + v];
         }
     }
 }
@@ -722,6 +737,7 @@ Args make_args(const Problem &p)
     a.LK = p.L * p.K;
     a.P = p.P;
     a.pix_bytes = (unsigned)(p.M * p.D * p.elem);
+    a.elem_bytes = p.elem;
     a.img_bytes = (unsigned)p.S * a.pix_bytes;
     a.gv_img_bytes = (unsigned)p.S * (unsigned)(p.M * p.D * 4);
     a.value_bytes = a.img_bytes * (unsigned)p.N;
@@ -803,7 +819,8 @@ hipError_t launch_bwd_loc_t(const Args &a, hipStream_t stream)
     const int upb = kThreads / (a.D / 8);
     const int blocks = (a.units + upb - 1) / upb;
     const size_t ga = (size_t)upb * a.LK * sizeof(float);
-    const size_t staged = ga + (size_t)upb * a.LK * (sizeof(unsigned) + sizeof(f32x4));
+    const size_t staged = ga + (size_t)upb * a.LK * (sizeof(unsigned) + sizeof(f32x4)) +
+                          (size_t)upb * a.P * (a.elem_bytes);
     if (staged <= 64 * 1024)
         return launch_bwd_loc_st<T, true>(a, blocks, staged, stream);
     return launch_bwd_loc_st<T, false>(a, blocks, ga, stream);
