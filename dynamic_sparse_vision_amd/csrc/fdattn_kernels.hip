@@ -60,6 +60,10 @@ using dcnv4::dev::xcd_tile;
 constexpr unsigned kOutOfRange = 0x80000000u;   // beyond any launch's buffer
 constexpr int kSortThreads = 1024;               // one block per (image, head) slice
 constexpr size_t kSortLdsMax = 150 * 1024;       // bin counters of one slice, LDS bytes
+#ifndef FDATTN_GATHER_CHANNELS
+#define FDATTN_GATHER_CHANNELS 4
+#endif
+constexpr int kGatherChannels = FDATTN_GATHER_CHANNELS;   // channels per lane in the grad_value gather (2 or 4)
 
 struct Args {
     const void *value;
@@ -116,6 +120,24 @@ __device__ __forceinline__ void ld2(const bf16_t *p, float &a, float &b)
     const unsigned w = *reinterpret_cast<const unsigned *>(p);
     a = Store<bf16_t>::from_bits(w & 0xffffu);
     b = Store<bf16_t>::from_bits(w >> 16);
+}
+
+// CPL (2 or 4) consecutive channels as floats; the address is aligned to
+// CPL elements.
+template <typename T, int CPL>
+__device__ __forceinline__ void load_channels(const T *p, float *out)
+{
+    if constexpr (CPL == 2) {
+        ld2(p, out[0], out[1]);
+    } else if constexpr (sizeof(T) == 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+        for (int c = 0; c < 4; ++c)
+            out[c] = v[c];
+    } else {
+        const u32x2 v = *reinterpret_cast<const u32x2 *>(p);
+        for (int c = 0; c < 4; ++c)
+            out[c] = Store<T>::from_bits((v[c >> 1] >> (16 * (c & 1))) & 0xffffu);
+    }
 }
 
 __device__ __forceinline__ void st2(float *p, float a, float b)
@@ -653,27 +675,29 @@ __global__ __launch_bounds__(kSortThreads) void fdattn_place(Args a)
     }
 }
 
-// D lanes per value cell (one channel each): the cell is the top-left,
+// D/CPL lanes per value cell (CPL channels each, so a wave holds several
+// cells and as many independent load chains): the cell is the top-left,
 // top-right, bottom-left and bottom-right corner of the samples in bins
 // (r, c), (r, c-1), (r-1, c) and (r-1, c-1); bins (r, c-1), (r, c) and
 // (r-1, c-1), (r-1, c) are adjacent, so the cell reads two runs.  A run is
 // read D records at a time, one per lane (coalesced), each reduced to (its
 // weight for this cell, its query) and staged in LDS, from where the unit's
 // lanes read them back as broadcasts.  Every cell is written once (no fill).
-template <typename T>
+template <typename T, int CPL>
 __global__ __launch_bounds__(kThreads) void fdattn_gather(Args a)
 {
-    extern __shared__ f32x2 stage_lds[];   // [units per block][D]: (weight, query)
+    extern __shared__ f32x2 stage_lds[];   // [units per block][D/CPL]: (weight, query)
     const int D = a.D;
-    const int upb = kThreads / D;
+    const int UL = D / CPL;   // lanes per cell
+    const int upb = kThreads / UL;
     const int blk = xcd_tile(blockIdx.x, gridDim.x);
-    const int lu = (int)threadIdx.x / D;
-    const int lane = (int)threadIdx.x - lu * D;
+    const int lu = (int)threadIdx.x / UL;
+    const int lane = (int)threadIdx.x - lu * UL;
     const int unit = blk * upb + lu;
     const int cells = a.units / a.Q * a.S;   // N*M*S
     if (unit >= cells)
         return;
-    f32x2 *stage = stage_lds + lu * D;
+    f32x2 *stage = stage_lds + lu * UL;
     const int slice = unit / a.S;
     const int s = unit - slice * a.S;
     const int n = slice / a.M;
@@ -686,43 +710,69 @@ __global__ __launch_bounds__(kThreads) void fdattn_gather(Args a)
     const int r = rc / W, c = rc - r * W;
     const size_t bin_lc = (size_t)slice * a.nbs + a.lvl_bin[l] + (size_t)(r + 1) * (W + 1) + c;   // bin (r, c-1)
     const size_t bin_ulc = bin_lc - (W + 1);                                                         // bin (r-1, c-1)
-    const T *gq = static_cast<const T *>(a.grad_out) + (size_t)n * a.Q * a.M * D + m * D + lane;
+    const T *gq = static_cast<const T *>(a.grad_out) + (size_t)n * a.Q * a.M * D + m * D + CPL * lane;
     const size_t qstride = (size_t)a.M * D;
-    float acc = 0.0f;
-    // run of bins b, b + 1: records of b have this cell as their right
-    // column (weight lx), those of b + 1 as their left column (1 - lx);
-    // row_part picks the weight of the records' upper or lower row
-    auto run = [&](size_t b, int row_part) {
-        const unsigned s0 = a.starts[b], mid = a.counts[b], e = a.counts[b + 1];
-        for (unsigned base = s0; base < e; base += (unsigned)D) {
-            const unsigned idx = base + (unsigned)lane;
-            f32x2 mine = {0.0f, 0.0f};
-            if (idx < e) {
-                const f32x4 rec = a.recs[idx];
-                const float wy = row_part == 0 ? rec[0] : rec[1];
-                mine[0] = wy * (idx < mid ? rec[2] : 1.0f - rec[2]);
-                mine[1] = rec[3];   // the query, as bits
-            }
-            // the unit's lanes are one wave: LDS accesses of a wave are
-            // performed in order, the barrier only keeps the compiler's order
-            __builtin_amdgcn_wave_barrier();
-            stage[lane] = mine;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const int cnt = (int)min((unsigned)D, e - base);
-#pragma unroll 4
-            for (int t = 0; t < cnt; ++t) {
-                const f32x2 wq = stage[t];
-                const unsigned q = __builtin_bit_cast(u32x2, wq)[1];   // whole-vector cast, then index
-                acc = __builtin_fmaf(wq[0], ld1(gq + q * qstride), acc);
-            }
-            __builtin_amdgcn_wave_barrier();
+    float acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+        acc[c] = 0.0f;
+    // The two runs -- bins (r, c-1), (r, c): the cell is in the records'
+    // upper row; bins (r-1, c-1), (r-1, c): in their lower row -- are read
+    // as one list, D/CPL records at a time: record j of the list is the j-th of
+    // run 1, then of run 2.  In each run the records of the first bin have
+    // this cell as their right column (weight lx), the others as their left
+    // (1 - lx).  The grad_out loads of a batch go out eight at a time.
+    const unsigned s1 = a.starts[bin_lc], m1 = a.counts[bin_lc], e1 = a.counts[bin_lc + 1];
+    const unsigned s2 = a.starts[bin_ulc], m2 = a.counts[bin_ulc], e2 = a.counts[bin_ulc + 1];
+    const unsigned n1 = e1 - s1, ntot = n1 + (e2 - s2);
+    for (unsigned base = 0; base < ntot; base += (unsigned)UL) {
+        const unsigned j = base + (unsigned)lane;
+        f32x2 mine = {0.0f, 0.0f};
+        if (j < ntot) {
+            const bool run1 = j < n1;
+            const unsigned idx = run1 ? s1 + j : s2 + (j - n1);
+            const f32x4 rec = a.recs[idx];
+            const float wy = run1 ? rec[0] : rec[1];
+            mine[0] = wy * (idx < (run1 ? m1 : m2) ? rec[2] : 1.0f - rec[2]);
+            mine[1] = rec[3];   // the query, as bits
         }
-    };
-    run(bin_lc, 0);    // bins (r, c-1), (r, c): the cell is in the records' upper row
-    run(bin_ulc, 1);   // bins (r-1, c-1), (r-1, c): the cell is in their lower row
-    a.grad_value[((size_t)n * a.S + s) * qstride + m * D + lane] = acc;
+        // the unit's lanes are one wave: LDS accesses of a wave are
+        // performed in order, the barriers only keep the compiler's order
+        __builtin_amdgcn_wave_barrier();
+        stage[lane] = mine;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int cnt = (int)min((unsigned)UL, ntot - base);
+        for (int t0 = 0; t0 < cnt; t0 += 8) {
+            float g[8][CPL], w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int t = min(t0 + u, cnt - 1);   // repeats the last record: a valid row
+                const f32x2 wq = stage[t];
+                w[u] = t0 + u < cnt ? wq[0] : 0.0f;
+                load_channels<T, CPL>(gq + __builtin_bit_cast(u32x2, wq)[1] * qstride, g[u]);   // whole-vector cast, then index
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c)
+                    acc[c] = t0 + u < cnt ? __builtin_fmaf(w[u], g[u][c], acc[c]) : acc[c];
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    float *gvp = a.grad_value + ((size_t)n * a.S + s) * qstride + m * D + CPL * lane;
+    if constexpr (CPL == 4) {
+        f32x4 out;
+        for (int c = 0; c < 4; ++c)
+            out[c] = acc[c];
+        *reinterpret_cast<f32x4 *>(gvp) = out;
+    } else {
+        f32x2 out;
+        out[0] = acc[0];
+        out[1] = acc[1];
+        *reinterpret_cast<f32x2 *>(gvp) = out;
+    }
 }
 
 Args make_args(const Problem &p)
@@ -865,7 +915,8 @@ hipError_t launch_bwd_t(const Args &a, hipStream_t stream)
     if (e != hipSuccess)
         return e;
     const int cells = slices * a.S;
-    hipLaunchKernelGGL((fdattn_gather<T>), dim3((cells + upb - 1) / upb), dim3(kThreads),
+    const int gupb = kThreads / (a.D / kGatherChannels);
+    hipLaunchKernelGGL((fdattn_gather<T, kGatherChannels>), dim3((cells + gupb - 1) / gupb), dim3(kThreads),
                        (size_t)kThreads * sizeof(f32x2), stream, a);
     return hipGetLastError();
 }
