@@ -17,18 +17,21 @@
 //   * Forward: D/8 lanes per unit, 8 channels per lane (the D' channels per
 //     thread and 128-bit loads of the walkthrough "DCNv4论文解析", section
 //     2.2); a corner is one (fp16/bf16) or two (fp32) 128-bit buffer loads.
-//   * Backward: D lanes per unit, one channel per lane; the location and
-//     logit gradients are lane sums (DPP).  grad_value takes one of two
-//     paths.  With a workspace it is a gather: one block per (image, head)
-//     slice counting-sorts the slice's live samples by the bin of their
-//     top-left corner cell in LDS (count with LDS atomics, scan, place a
-//     16-byte record per sample; the coarse levels put hundreds of samples
-//     on one bin, which device atomics would serialise), then every value
-//     cell sums the records of the four bins whose samples have it as a
-//     corner -- two runs of adjacent bins, eight records in flight at a time
-//     -- and is written once.  Without one (or when a slice's bins do not fit
-//     the LDS), every (sample, corner, channel) is a device fp32 atomic
-//     (N*Q*M*L*K*4*D of them), resolved beyond the L2 on this part.
+//   * Backward, with a caller workspace (the sorted path): the location and
+//     logit gradients in the forward's mapping (lane sums by DPP), which
+//     also emits each live sample's bin -- the cell of its top-left corner
+//     -- and a 16-byte record; a counting sort per (image, head) slice, its
+//     queries split over several blocks, each counting in LDS (the coarse
+//     levels put hundreds of samples on one bin, which device atomics would
+//     serialise) and merging into the slice's counts with one device atomic
+//     per bin, then a scan and a placement pass; finally every value cell
+//     sums the records of the four bins whose samples have it as a corner --
+//     two runs of adjacent bins -- with D/4 lanes of four channels, and is
+//     written once.
+//   * Backward without a workspace (or when a slice's bins do not fit the
+//     LDS): D lanes per unit, one channel each, and every (sample, corner,
+//     channel) is a device fp32 atomic (N*Q*M*L*K*4*D of them, resolved
+//     beyond the L2 on this part), coalesced over the D lanes.
 //   * Every corner outside its level's map gets an out-of-range buffer
 //     offset: its loads return 0 and its atomics are dropped by the buffer
 //     range check, exactly the zero padding of the definition.
@@ -679,10 +682,11 @@ __global__ __launch_bounds__(kSortThreads) void fdattn_place(Args a)
 // cells and as many independent load chains): the cell is the top-left,
 // top-right, bottom-left and bottom-right corner of the samples in bins
 // (r, c), (r, c-1), (r-1, c) and (r-1, c-1); bins (r, c-1), (r, c) and
-// (r-1, c-1), (r-1, c) are adjacent, so the cell reads two runs.  A run is
-// read D records at a time, one per lane (coalesced), each reduced to (its
-// weight for this cell, its query) and staged in LDS, from where the unit's
-// lanes read them back as broadcasts.  Every cell is written once (no fill).
+// (r-1, c-1), (r-1, c) are adjacent, so the cell reads two runs, taken as
+// one list D/CPL records at a time, one per lane (coalesced), each reduced
+// to (its weight for this cell, its query) and staged in LDS, from where the
+// unit's lanes read them back as broadcasts.  Every cell is written once (no
+// fill).
 template <typename T, int CPL>
 __global__ __launch_bounds__(kThreads) void fdattn_gather(Args a)
 {
