@@ -140,6 +140,29 @@ def test_parity_atomic_grad_value(w):
     run_case(w, sorted_grad_value=False)
 
 
+EDGE_CASES = [
+    # one query, one image, degenerate maps: 1x1, a single row and a single column
+    _w("tiny_maps_fp32", N=1, Q=1, M=1, D=8, K=3, shapes=((1, 1), (1, 7), (5, 1))),
+    _w("tiny_maps_many_q_fp32", N=1, Q=19, M=3, D=16, K=2, shapes=((1, 1), (2, 1), (1, 2))),
+    # a level whose corner bins (201 x 201) do not fit the per-slice sort in
+    # LDS: the backward takes the device-atomic path even with a workspace
+    _w("big_level_fp32", N=1, Q=50, M=1, D=8, K=2, shapes=((200, 200),), sigma_px=3.0),
+    # odd sizes everywhere
+    _w("odd_sizes_bf16", dtype="bf16", N=3, Q=23, M=3, D=16, K=5, shapes=((9, 13), (5, 7), (3, 3))),
+]
+
+
+@pytest.mark.parametrize("w", EDGE_CASES, ids=[c.name for c in EDGE_CASES])
+def test_parity_edge_cases(w):
+    say(f"[fdattn] {w.name} N={w.N} levels={w.shapes} Q={w.queries} M={w.M} D={w.D} K={w.K} {w.dtype}")
+    if w.name == "big_level_fp32":
+        v = torch.zeros((w.N, w.S, w.M, w.D), device="cuda")
+        la = torch.zeros((w.N, w.queries, w.M, w.P), device="cuda")
+        assert fda.flash_deform_attn_backward_workspace(v, w.shapes, la, num_points=w.K) == 0, \
+            "a slice of 40401 bins should not fit the LDS sort"
+    run_case(w)
+
+
 def test_forward_head_dim_128():
     w = _w("d128_fp32", D=128, M=2, Q=21)
     say(f"[fdattn] {w.name} forward only (the backward takes D <= 64)")
