@@ -222,6 +222,10 @@ constexpr int kForwardRmax = DCNV4_FWD_RMAX;   // largest halo of the forward ti
 constexpr int kBackwardRmax = DCNV4_BWD_RMAX;  // largest halo of the backward tiles (both kernels)
 constexpr int kTiledMaxLds = 80 * 1024;
 constexpr int kLdsPerCu = 160 * 1024;
+// A block's LDS is allocated in 1280-byte units: 7-wave forward blocks of
+// 54000 bytes averaged 10.5 resident waves per CU (two blocks fit, not three),
+// 8-wave blocks of 50112 bytes 16 (three fit).
+constexpr int kLdsGranule = 1280;
 constexpr int kTileThreads = 512;
 #ifndef DCNV4_CELL_LDS_KB
 #define DCNV4_CELL_LDS_KB 78
@@ -262,7 +266,7 @@ bool choose_out_tile(const Problem &p, int lanes, int dp, int ps, int R, int lds
             if (lds > lds_budget)
                 continue;
             const int waves = (threads + 63) / 64;
-            const int per_cu = std::min(kLdsPerCu / lds, 32 / waves);
+            const int per_cu = std::min(kLdsPerCu / ((lds + kLdsGranule - 1) / kLdsGranule * kLdsGranule), 32 / waves);
             const double occ = std::min(1.0, per_cu * waves / 24.0);
             const double blocks = (double)((p.Ho + h - 1) / h) * ((p.Wo + w - 1) / w);
             const double work = waves * 64.0 * p.K * (40 + 4 * dp) + (double)rh * rw * ps * 8;
