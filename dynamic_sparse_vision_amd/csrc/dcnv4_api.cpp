@@ -531,6 +531,31 @@ int hip_status(hipError_t e)
     return DCNV4_ERR_HIP;
 }
 
+hipError_t allow_dynamic_lds(const void *fn, size_t bytes)
+{
+    if (bytes <= 64 * 1024)
+        return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    struct Raised {
+        const void *fn;
+        int dev;
+        size_t bytes;
+    };
+    static std::mutex mu;
+    static std::vector<Raised> done;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Raised &r : done)
+        if (r.fn == fn && r.dev == dev && r.bytes >= bytes)
+            return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess)
+        done.push_back({fn, dev, bytes});
+    return e;
+}
+
 }  // namespace dcnv4
 
 using namespace dcnv4;

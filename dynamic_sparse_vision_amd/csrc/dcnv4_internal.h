@@ -90,6 +90,11 @@ dev::Geom make_geom(const Problem &p);
 void clear_hip_error();
 int hip_status(hipError_t e);
 
+// Raise a kernel's dynamic LDS limit to `bytes` on the current device when
+// above the default 64 KB (gfx950 has 160 KB per CU); done once per kernel
+// and device.
+hipError_t allow_dynamic_lds(const void *fn, size_t bytes);
+
 // Enqueue kernels for images [0, p.N) of the given tensors (the caller has
 // already offset the pointers).  Return hipError_t.
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);

@@ -42,10 +42,6 @@
 #include "dcnv4_device.h"
 #include "dcnv4_internal.h"
 
-#include <mutex>
-#include <utility>
-#include <vector>
-
 namespace dcnv4 {
 namespace {
 
@@ -1236,24 +1232,6 @@ __global__ __launch_bounds__(kCellThreads) __attribute__((amdgpu_waves_per_eu(4)
     }
 }
 
-// Launches above 64 KB of dynamic LDS need the kernel's limit raised once
-// (gfx950 has 160 KB per CU); remembered per kernel.
-hipError_t allow_lds(const void *fn, int bytes)
-{
-    if (bytes <= 64 * 1024)
-        return hipSuccess;
-    static std::mutex mu;
-    static std::vector<std::pair<const void *, int>> done;
-    std::lock_guard<std::mutex> lock(mu);
-    for (const auto &d : done)
-        if (d.first == fn && d.second >= bytes)
-            return hipSuccess;
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e == hipSuccess)
-        done.emplace_back(fn, bytes);
-    return e;
-}
-
 unsigned magic_for(int d)
 {
     // ceil(2^32 / d): mulhi(e, magic) == e / d for 0 <= e < 2^32 / d;
@@ -1340,7 +1318,8 @@ hipError_t launch_forward_tiled(const Problem &p, const TilePlan &tp, const void
     do {                                                                                             \
         void (*k_)(TArgs) = p.K <= 9 ? (p.softmax ? dcnv4_fwd_tiled<T, D, 9, true> : dcnv4_fwd_tiled<T, D, 9, false>) \
                                      : (p.softmax ? dcnv4_fwd_tiled<T, D, 25, true> : dcnv4_fwd_tiled<T, D, 25, false>); \
-        const hipError_t e_ = allow_lds(reinterpret_cast<const void *>(k_), tp.lds_bytes);           \
+        const hipError_t e_ =                                                                        \
+            allow_dynamic_lds(reinterpret_cast<const void *>(k_), (size_t)tp.lds_bytes);             \
         if (e_ != hipSuccess)                                                                        \
             return e_;                                                                               \
         hipLaunchKernelGGL(k_, grid, block, tp.lds_bytes, stream, a);                                \
@@ -1479,7 +1458,7 @@ hipError_t launch_backward_tiled(const Problem &p, const TilePlan &tp, const voi
     // 1) grad_value of near samples: every cell written once, plain stores
     {
         const int blocks = p.N * tp.ctiles_y * tp.ctiles_x * p.G;
-        hipError_t e = allow_lds(reinterpret_cast<const void *>(values), tp.splat_lds_bytes);
+        hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(values), (size_t)tp.splat_lds_bytes);
         if (e != hipSuccess)
             return e;
         hipLaunchKernelGGL(values, dim3(blocks), dim3(kCellThreads), tp.splat_lds_bytes, stream, a);
@@ -1490,7 +1469,7 @@ hipError_t launch_backward_tiled(const Problem &p, const TilePlan &tp, const voi
     // 2) grad_offset_mask, plus far samples' grad_value by device atomics
     {
         const int blocks = p.N * tp.tiles_y * tp.tiles_x * p.G;
-        const hipError_t e = allow_lds(reinterpret_cast<const void *>(offsets), tp.lds_bytes);
+        const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(offsets), (size_t)tp.lds_bytes);
         if (e != hipSuccess)
             return e;
         hipLaunchKernelGGL(offsets, dim3(blocks), dim3(tp.threads), tp.lds_bytes, stream, a);

@@ -44,9 +44,6 @@
 
 #include <algorithm>
 #include <climits>
-#include <mutex>
-#include <utility>
-#include <vector>
 
 namespace fdattn {
 namespace {
@@ -476,7 +473,6 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd_loc(Args a)
         const int H = a.lvl_h[l], W = a.lvl_w[l], start = a.lvl_start[l];
         const float Hf = (float)H, Wf = (float)W;
         const int i0 = l * a.K;
-#pragma unroll 4
         for (int k = 0; k < a.K; ++k) {
             const int i = i0 + k;
             float u, v;
@@ -836,24 +832,6 @@ hipError_t launch_fwd_t(const Args &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Dynamic LDS above 64 KB needs the kernel's limit raised once (gfx950 has
-// 160 KB per CU); remembered per kernel.
-hipError_t set_lds_limit(const void *fn, size_t bytes)
-{
-    if (bytes <= 64 * 1024)
-        return hipSuccess;
-    static std::mutex mu;
-    static std::vector<std::pair<const void *, size_t>> done;
-    std::lock_guard<std::mutex> lock(mu);
-    for (const auto &d : done)
-        if (d.first == fn && d.second >= bytes)
-            return hipSuccess;
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e == hipSuccess)
-        done.emplace_back(fn, bytes);
-    return e;
-}
-
 template <typename T, bool ST>
 hipError_t launch_bwd_loc_st(const Args &a, int blocks, size_t lds, hipStream_t stream)
 {
@@ -901,9 +879,9 @@ hipError_t launch_bwd_t(const Args &a, hipStream_t stream)
         return e;
     const int slices = a.units / a.Q;
     const size_t sort_lds = (size_t)a.nbs * sizeof(unsigned);
-    e = set_lds_limit(reinterpret_cast<const void *>(&fdattn_count), sort_lds);
+    e = dcnv4::allow_dynamic_lds(reinterpret_cast<const void *>(&fdattn_count), sort_lds);
     if (e == hipSuccess)
-        e = set_lds_limit(reinterpret_cast<const void *>(&fdattn_place), sort_lds);
+        e = dcnv4::allow_dynamic_lds(reinterpret_cast<const void *>(&fdattn_place), sort_lds);
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(fdattn_count, dim3(slices * a.sb), dim3(kSortThreads), sort_lds, stream, a);
