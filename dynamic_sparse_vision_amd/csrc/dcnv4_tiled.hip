@@ -947,7 +947,7 @@ __device__ __forceinline__ unsigned wave_inclusive_sum(unsigned v)
 // to exactly the cells that are its corners (non-finite inputs spread as in
 // the plain sum).
 template <typename T, int CG, int KMAX, bool SM>
-__global__ __launch_bounds__(kCellThreads) __attribute__((amdgpu_waves_per_eu(4))) void dcnv4_bwd_values_tiled(TArgs a)
+__global__ __launch_bounds__(kCellThreads) __attribute__((amdgpu_waves_per_eu(KMAX <= 9 ? 4 : 1))) void dcnv4_bwd_values_tiled(TArgs a)
 {
     extern __shared__ u32x4 smem[];
     constexpr int es = (int)sizeof(T);

@@ -1,0 +1,77 @@
+"""Seeded random geometries against the oracle, through the C ABI.
+
+Each case draws its batch, map size, channels per group, group count,
+kernel (1, 3 or 5 per axis), stride, padding, dilation, remove_center,
+offset_scale, offset spread, storage dtype and the DCNv3 softmax mode from
+one seeded generator, so
+the tile planner meets shapes that the named cases do not (rectangular and
+1-wide kernels with remove_center off, ragged tiles along both axes, tiny
+and wide maps, offsets far beyond the halo).  Forward for every case;
+backward for fp32, and for fp16/bf16 where the tiled backward exists
+(8, 16 or 32 channels per group).  Tolerances as in test_gpu_parity.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dynamic_sparse_vision_amd import dcnv4
+from dynamic_sparse_vision_amd.workloads import Workload
+from tests.test_gpu_parity import check, device_inputs, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _out_size(size, k, s, p, d):
+    return (size + 2 * p - (d * (k - 1) + 1)) // s + 1
+
+
+def _draw_cases(n_cases, seed=2024):
+    rng = np.random.RandomState(seed)
+    cases = []
+    while len(cases) < n_cases:
+        dtype = ["fp32", "fp16", "bf16"][rng.randint(3)]
+        cg = int(rng.choice([4, 8, 16, 32] if dtype == "fp32" else [8, 16, 32]))
+        g = int(rng.randint(1, 5))
+        kh, kw = int(rng.choice([1, 3, 5])), int(rng.choice([1, 3, 5]))
+        rc = bool(kh % 2 == 1 and kw % 2 == 1 and kh * kw > 1 and rng.rand() < 0.5)
+        sh, sw = int(rng.randint(1, 3)), int(rng.randint(1, 3))
+        dh, dw = int(rng.randint(1, 3)), int(rng.randint(1, 3))
+        ph, pw = int(rng.randint(0, 3)), int(rng.randint(0, 3))
+        H, W = int(rng.randint(1, 25)), int(rng.randint(1, 25))
+        if _out_size(H, kh, sh, ph, dh) < 1 or _out_size(W, kw, sw, pw, dw) < 1:
+            continue
+        i = len(cases)
+        softmax = bool(rng.rand() < 0.25)
+        cases.append((Workload(
+            f"rnd{i:02d}_{dtype}_{H}x{W}_g{g}c{cg}_k{kh}x{kw}{'rc' if rc else ''}"
+            f"_s{sh}{sw}_p{ph}{pw}_d{dh}{dw}",
+            N=int(rng.randint(1, 4)), H=H, W=W, C=g * cg, G=g, dtype=dtype,
+            seed=1000 + i, sigma_value=1.0, sigma_off=float(rng.choice([0.5, 2.0, 6.0, 12.0])),
+            sigma_m=0.7, direction="fwd", remove_center=rc,
+            integer_offsets=bool(rng.rand() < 0.2), kernel=(kh, kw), stride=(sh, sw),
+            pad=(ph, pw), dilation=(dh, dw), offset_scale=float(rng.choice([0.5, 1.0, 1.5]))), softmax))
+    return cases
+
+
+CASES = _draw_cases(160)
+
+
+@pytest.mark.parametrize("w,softmax", CASES, ids=lambda x: getattr(x, "name", None) or f"softmax={x}")
+def test_random_geometry(w, softmax):
+    say(f"[random] {w.name} N={w.N} sigma_off={w.sigma_off} scale={w.offset_scale} "
+        f"int={w.integer_offsets} softmax={softmax}")
+    d = device_inputs(w, with_grad=True)
+    out = dcnv4.forward(d["v"], d["om"], softmax=softmax, **w.kwargs())
+    torch.cuda.synchronize()
+    ref = oracle.forward(d["v_ref"], d["om_ref"], softmax=softmax, **w.kwargs())
+    check(out.float().cpu().numpy(), ref, w.dtype, f"{w.name} output")
+    if w.dtype != "fp32" and w.Cg not in (8, 16, 32):
+        return
+    gv, gom = dcnv4.backward(d["v"], d["om"], d["g"], softmax=softmax, **w.kwargs())
+    torch.cuda.synchronize()
+    rgv, rgom = oracle.backward(d["v_ref"], d["om_ref"], d["g_ref"], softmax=softmax, **w.kwargs())
+    check(gv.cpu().numpy(), rgv, "fp32", f"{w.name} grad_value")
+    gom32 = gom.float().cpu().numpy()
+    check(gom32, rgom, w.dtype, f"{w.name} grad_offset_mask")
+    assert np.all(gom32[..., 3 * w.G * w.K:] == 0), "padding gradient must be 0"
