@@ -6,7 +6,7 @@ offset_scale, offset spread, storage dtype and the DCNv3 softmax mode from
 one seeded generator, so
 the tile planner meets shapes that the named cases do not (rectangular and
 1-wide kernels with remove_center off, ragged tiles along both axes, tiny
-and wide maps, offsets far beyond the halo).  Forward for every case;
+and wide maps up to 96 pixels a side, offsets far beyond the halo).  Forward for every case;
 backward for fp32, and for fp16/bf16 where the tiled backward exists
 (8, 16 or 32 channels per group).  Tolerances as in test_gpu_parity.
 """
@@ -26,7 +26,7 @@ def _out_size(size, k, s, p, d):
     return (size + 2 * p - (d * (k - 1) + 1)) // s + 1
 
 
-def _draw_cases(n_cases, seed=2024):
+def _draw_cases(n_cases, seed=2024, size=(1, 25), batch=(1, 4), prefix="rnd"):
     rng = np.random.RandomState(seed)
     cases = []
     while len(cases) < n_cases:
@@ -38,15 +38,15 @@ def _draw_cases(n_cases, seed=2024):
         sh, sw = int(rng.randint(1, 3)), int(rng.randint(1, 3))
         dh, dw = int(rng.randint(1, 3)), int(rng.randint(1, 3))
         ph, pw = int(rng.randint(0, 3)), int(rng.randint(0, 3))
-        H, W = int(rng.randint(1, 25)), int(rng.randint(1, 25))
+        H, W = int(rng.randint(*size)), int(rng.randint(*size))
         if _out_size(H, kh, sh, ph, dh) < 1 or _out_size(W, kw, sw, pw, dw) < 1:
             continue
         i = len(cases)
         softmax = bool(rng.rand() < 0.25)
         cases.append((Workload(
-            f"rnd{i:02d}_{dtype}_{H}x{W}_g{g}c{cg}_k{kh}x{kw}{'rc' if rc else ''}"
+            f"{prefix}{i:02d}_{dtype}_{H}x{W}_g{g}c{cg}_k{kh}x{kw}{'rc' if rc else ''}"
             f"_s{sh}{sw}_p{ph}{pw}_d{dh}{dw}",
-            N=int(rng.randint(1, 4)), H=H, W=W, C=g * cg, G=g, dtype=dtype,
+            N=int(rng.randint(*batch)), H=H, W=W, C=g * cg, G=g, dtype=dtype,
             seed=1000 + i, sigma_value=1.0, sigma_off=float(rng.choice([0.5, 2.0, 6.0, 12.0])),
             sigma_m=0.7, direction="fwd", remove_center=rc,
             integer_offsets=bool(rng.rand() < 0.2), kernel=(kh, kw), stride=(sh, sw),
@@ -55,6 +55,9 @@ def _draw_cases(n_cases, seed=2024):
 
 
 CASES = _draw_cases(160)
+# maps of 25 to 96 pixels a side: several output and cell tiles per image,
+# ragged along both axes
+CASES += _draw_cases(32, seed=2025, size=(25, 97), batch=(1, 3), prefix="big")
 
 
 @pytest.mark.parametrize("w,softmax", CASES, ids=lambda x: getattr(x, "name", None) or f"softmax={x}")
