@@ -16,6 +16,7 @@ import torch
 
 import oracle
 from dynamic_sparse_vision_amd import dcnv4
+from dynamic_sparse_vision_amd.dcnv4 import Dcnv4Error
 from dynamic_sparse_vision_amd.workloads import Workload
 from tests.test_gpu_parity import check, device_inputs, say
 
@@ -26,14 +27,25 @@ def _out_size(size, k, s, p, d):
     return (size + 2 * p - (d * (k - 1) + 1)) // s + 1
 
 
-def _draw_cases(n_cases, seed=2024, size=(1, 25), batch=(1, 4), prefix="rnd"):
+def _draw_cases(n_cases, seed=2024, size=(1, 25), batch=(1, 4), prefix="rnd", general=False):
     rng = np.random.RandomState(seed)
     cases = []
     while len(cases) < n_cases:
         dtype = ["fp32", "fp16", "bf16"][rng.randint(3)]
-        cg = int(rng.choice([4, 8, 16, 32] if dtype == "fp32" else [8, 16, 32]))
+        if general and rng.rand() < 0.5:
+            dtype = "fp32"   # the general backward is fp32 only
+        kernels = [1, 3, 5]
+        if not general:
+            cg = int(rng.choice([4, 8, 16, 32] if dtype == "fp32" else [8, 16, 32]))
+        elif rng.rand() < 0.5:
+            # channel rows of 3, 5 or 6 vectors (not a power of two)
+            cg = int(rng.choice([12, 20, 24] if dtype == "fp32" else [24, 40, 48]))
+        else:
+            # more than 25 points
+            cg = int(rng.choice([4, 8, 16] if dtype == "fp32" else [8, 16]))
+            kernels = [7]
         g = int(rng.randint(1, 5))
-        kh, kw = int(rng.choice([1, 3, 5])), int(rng.choice([1, 3, 5]))
+        kh, kw = int(rng.choice(kernels)), int(rng.choice(kernels if len(kernels) > 1 else [5, 7]))
         rc = bool(kh % 2 == 1 and kw % 2 == 1 and kh * kw > 1 and rng.rand() < 0.5)
         sh, sw = int(rng.randint(1, 3)), int(rng.randint(1, 3))
         dh, dw = int(rng.randint(1, 3)), int(rng.randint(1, 3))
@@ -58,6 +70,34 @@ CASES = _draw_cases(160)
 # maps of 25 to 96 pixels a side: several output and cell tiles per image,
 # ragged along both axes
 CASES += _draw_cases(32, seed=2025, size=(25, 97), batch=(1, 3), prefix="big")
+# shapes the tiled kernels decline (channel rows that are not a power of two
+# of 16-byte vectors, more than 25 points): the general kernels
+CASES += _draw_cases(48, seed=2026, size=(1, 30), batch=(1, 3), prefix="gen", general=True)
+
+
+def _tiled(w, backward):
+    """The tiled kernels take K <= 25 points and channel rows of a power of
+    two of 16-byte vectors; their backward 4 (fp32), 8, 16 or 32 channels
+    per group."""
+    es = 4 if w.dtype == "fp32" else 2
+    nvp = w.Cg * es // 16
+    ok = w.K <= 25 and (w.Cg * es) % 16 == 0 and nvp & (nvp - 1) == 0
+    return ok and (not backward or w.Cg in (8, 16, 32) or (w.Cg == 4 and es == 4))
+
+
+def _supported(w, softmax, backward):
+    """Whether the library takes the call: the tiled kernels in every dtype
+    and mode; else the general kernels, without the softmax mode: the forward
+    for 16-byte channel rows, the backward in fp32 with lanes of 4, 8 or 16
+    channels, a power of two of them per group."""
+    if _tiled(w, backward):
+        return True
+    es = 4 if w.dtype == "fp32" else 2
+    if softmax or (w.Cg * es) % 16 != 0:
+        return False
+    if not backward:
+        return True
+    return w.dtype == "fp32" and any(w.Cg % d == 0 and (w.Cg // d) & (w.Cg // d - 1) == 0 for d in (4, 8, 16))
 
 
 @pytest.mark.parametrize("w,softmax", CASES, ids=lambda x: getattr(x, "name", None) or f"softmax={x}")
@@ -65,11 +105,17 @@ def test_random_geometry(w, softmax):
     say(f"[random] {w.name} N={w.N} sigma_off={w.sigma_off} scale={w.offset_scale} "
         f"int={w.integer_offsets} softmax={softmax}")
     d = device_inputs(w, with_grad=True)
+    if not _supported(w, softmax, backward=False):
+        with pytest.raises(Dcnv4Error, match="UNSUPPORTED"):
+            dcnv4.forward(d["v"], d["om"], softmax=softmax, **w.kwargs())
+        return
     out = dcnv4.forward(d["v"], d["om"], softmax=softmax, **w.kwargs())
     torch.cuda.synchronize()
     ref = oracle.forward(d["v_ref"], d["om_ref"], softmax=softmax, **w.kwargs())
     check(out.float().cpu().numpy(), ref, w.dtype, f"{w.name} output")
-    if w.dtype != "fp32" and w.Cg not in (8, 16, 32):
+    if not _supported(w, softmax, backward=True):
+        with pytest.raises(Dcnv4Error, match="UNSUPPORTED"):
+            dcnv4.backward(d["v"], d["om"], d["g"], softmax=softmax, **w.kwargs())
         return
     gv, gom = dcnv4.backward(d["v"], d["om"], d["g"], softmax=softmax, **w.kwargs())
     torch.cuda.synchronize()
