@@ -519,7 +519,7 @@ __device__ __forceinline__ float pixel_sum(float x, int lanes)
 // whole wave.  At the end the value rows are no longer needed and their LDS
 // holds the tile's gradient rows, which are written back row by row.
 template <typename T, int DP, int KMAX, bool SM>
-__global__ __launch_bounds__(kMaxTileThreads) __attribute__((amdgpu_waves_per_eu(4))) void dcnv4_bwd_offsets_tiled(TArgs a)
+__global__ __launch_bounds__(kMaxTileThreads) __attribute__((amdgpu_waves_per_eu(KMAX <= 9 ? 4 : 1))) void dcnv4_bwd_offsets_tiled(TArgs a)
 {
     extern __shared__ u32x4 smem[];
     constexpr int es = (int)sizeof(T);
