@@ -1,14 +1,16 @@
 """Seeded random geometries against the oracle, through the C ABI.
 
 Each case draws its batch, map size, channels per group, group count,
-kernel (1, 3 or 5 per axis), stride, padding, dilation, remove_center,
+kernel (1, 3, 5 or 7 per axis), stride, padding, dilation, remove_center,
 offset_scale, offset spread, storage dtype and the DCNv3 softmax mode from
-one seeded generator, so
-the tile planner meets shapes that the named cases do not (rectangular and
-1-wide kernels with remove_center off, ragged tiles along both axes, tiny
-and wide maps up to 96 pixels a side, offsets far beyond the halo).  Forward for every case;
-backward for fp32, and for fp16/bf16 where the tiled backward exists
-(8, 16 or 32 channels per group).  Tolerances as in test_gpu_parity.
+one seeded generator, so the tile planner meets shapes that the named cases
+do not: rectangular and 1-wide kernels, ragged tiles along both axes, maps
+from 1 to 96 pixels a side, offsets far beyond the halo, and shapes the
+tiled kernels decline (channel rows that are not a power of two of 16-byte
+vectors, more than 25 points), which go to the general kernels.  Forward
+and backward wherever the library takes the call; where it declines (the
+general kernels have no softmax mode and no 16-bit backward) the call must
+fail with UNSUPPORTED.  Tolerances as in test_gpu_parity.
 """
 import numpy as np
 import pytest
