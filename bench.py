@@ -20,10 +20,12 @@ is timed on the host on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
 import statistics
+import subprocess
 import sys
 import time
 
@@ -33,7 +35,9 @@ sys.path.insert(0, ROOT)
 METRIC = "DCNv4 fwd/bwd sampled points/s (N·H·W·G·K·C') + achieved HBM GB/s % of peak"
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SRCS = {op: [os.path.join(ROOT, "dynamic_sparse_vision_amd", "csrc", n) for n in names]
-               for op, names in (("dcnv4", ("dcnv4_device.h", "dcnv4_kernels.hip", "dcnv4_tiled.hip")),
+               for op, names in (("dcnv4", ("dcnv4_device.h", "dcnv4_kernels.hip", "dcnv4_tiled.h",
+                                            "dcnv4_tiled_fwd.hip", "dcnv4_tiled_bwd_offsets.hip",
+                                            "dcnv4_tiled_bwd_values.hip", "dcnv4_tiled_launch.hip")),
                                  ("fdattn", ("dcnv4_device.h", "dcnv4_kernels.hip", "fdattn_kernels.hip")))}
 FDA_METRIC = "flash deformable attention fwd/bwd sampled points/s (N·Q·M·L·K·D) + achieved HBM GB/s % of peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -94,31 +98,64 @@ def set_bytes_of(w):
     return es * (nv + 2 * nom + 2 * no) + 4 * nv
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, arrays, seconds):
-    """The oracle as it stands, forward + backward, one image at a time
-    (cycling over the batch's images) until the time budget is spent: a
-    bounded sample of the same workload."""
+    """The oracle as it stands, forward + backward, on a bounded sample of
+    the same workload: batches of images (the forward threads over output
+    rows, the backward over images, so a batch of ``nthreads`` images keeps
+    every thread busy in both).  Runs are repeated until about ``seconds``
+    have passed (at least 3), and the median run is reported; a single-thread
+    figure on one image is reported beside it."""
     import oracle
 
     v32, om32, g32 = arrays
     nthreads = min(int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), os.cpu_count() or 1)
     lib = oracle.load()
-    passes = 0
-    t0 = time.perf_counter()
-    elapsed = 0.0
-    while elapsed < seconds:
-        i = passes % w.N
-        sl = slice(i, i + 1)
-        oracle.forward(v32[sl], om32[sl], nthreads=nthreads, lib=lib, **w.kwargs())
-        oracle.backward(v32[sl], om32[sl], g32[sl], nthreads=nthreads, lib=lib, **w.kwargs())
-        passes += 1
-        elapsed = time.perf_counter() - t0
-    pts = passes * w.Ho * w.Wo * w.G * w.K * w.Cg
-    return {"value": pts / elapsed, "unit": "sampled points/s", "cores": nthreads,
+    pts_per_image = w.Ho * w.Wo * w.G * w.K * w.Cg
+
+    def runs(batch, threads, budget, min_runs=3):
+        rates, n0 = [], 0
+        t_start = time.perf_counter()
+        while len(rates) < min_runs or time.perf_counter() - t_start < budget:
+            idx = [(n0 + i) % w.N for i in range(batch)]
+            n0 += batch
+            v, om, g = v32[idx], om32[idx], g32[idx]
+            t0 = time.perf_counter()
+            oracle.forward(v, om, nthreads=threads, lib=lib, **w.kwargs())
+            oracle.backward(v, om, g, nthreads=threads, lib=lib, **w.kwargs())
+            rates.append(batch * pts_per_image / (time.perf_counter() - t0))
+            if len(rates) >= 50:
+                break
+        return rates
+
+    all_rates = runs(nthreads, nthreads, 0.75 * seconds)
+    one_rates = runs(1, 1, 0.25 * seconds)
+    return {"value": statistics.median(all_rates), "unit": "sampled points/s", "cores": nthreads,
             "kind": "oracle",
-            "sample": f"{passes} single-image forward + backward passes over the {w.N} images "
-                      f"of the same workload (oracle threads parallel over output rows), "
-                      f"{elapsed:.1f} s"}
+            "sample": f"median of {len(all_rates)} runs, each forward + backward over a batch of {nthreads} images "
+                      f"of the same workload ({nthreads * pts_per_image} points; forward threaded over output "
+                      f"rows, backward over images, {nthreads} threads each)",
+            "single_thread": {"value": statistics.median(one_rates), "runs": len(one_rates),
+                              "sample": "forward + backward of one image, 1 thread"},
+            "cpu_model": cpu_model(), "hardware_threads": os.cpu_count()}
 
 
 def time_configs(path, steps, warmup):
@@ -354,8 +391,8 @@ def run_fdattn(args):
         step(args.warmup + i, events[i])
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    fwd_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in events)
-    bwd_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in events)
+    fwd_ms = statistics.median(e[0].elapsed_time(e[1]) for e in events)
+    bwd_ms = statistics.median(e[1].elapsed_time(e[2]) for e in events)
     print(f"bench: {ms_per_step:.4f} ms/step (forward {fwd_ms:.4f} ms, backward {bwd_ms:.4f} ms)",
           file=sys.stderr, flush=True)
     calls = {"flash_deform_attn_forward": (fwd_ms, w.fwd_bytes()),
@@ -407,6 +444,8 @@ def main():
                          "with --op fdattn)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-detail", action="store_true",
+                    help="skip the cold per-workload forward timings and the batch-share timings")
     ap.add_argument("--configs-out", default=None,
                     help="also time every workload alone and write JSON lines there")
     ap.add_argument("--copy-probe", action="store_true",
@@ -425,7 +464,154 @@ def main():
         run_fdattn(args)
         return
     args.workload = args.workload or "c2_fwd_fp32_56x56_b64"
+    run_dcnv4(args)
 
+
+def measured_kernel(workload: str, call: str):
+    """The dominant single kernel of ``call`` on ``workload`` as the committed
+    rocprofv3 kernel trace reports it (name, average duration), if the kernel
+    sources have not changed since the trace was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    wl = t.get("workloads", {}).get(workload, {})
+    if wl.get("kernel_source_sha256") != kernel_source_hash("dcnv4"):
+        return None
+    entry = wl.get(call) or {}
+    return entry.get("dominant_kernel")
+
+
+def cold_ms(call, flush, stream, calls=20, warmup=3):
+    """Median duration (ms, HIP events on ``stream``) of ``calls`` calls, each
+    after a 512 MB fill that evicts the L2 and Infinity Cache, so every call
+    reads its inputs from HBM."""
+    import torch
+
+    times = []
+    for i in range(warmup + calls):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        e1.synchronize()
+        if i >= warmup:
+            times.append(e0.elapsed_time(e1))
+    return statistics.median(times)
+
+
+def forward_detail(flush, stream):
+    """Every forward workload of the benchmark configurations other than the
+    step's own, alone and cold (median of 20 calls): ms, compulsory GB/s and
+    the fraction of 8 TB/s; plus the bytes-weighted aggregate of the four
+    fp16 stage shapes."""
+    import torch
+
+    from dynamic_sparse_vision_amd import dcnv4, synth
+    from dynamic_sparse_vision_amd.workloads import WORKLOADS
+
+    dev = torch.device("cuda")
+    out = {}
+    agg_bytes, agg_ms = 0, 0.0
+    for name in ("c3a_fwd_fp16_56x56x64_g4", "c3b_fwd_fp16_28x28x128_g8", "c3c_fwd_fp16_14x14x256_g16",
+                 "c3d_fwd_fp16_7x7x512_g32", "c4_fwd_bf16_270x480_k9", "c4_fwd_bf16_270x480_k8",
+                 "c1_fwd_fp32_14x14"):
+        w = WORKLOADS[name]
+        print(f"bench: forward {name}", file=sys.stderr, flush=True)
+        v32, om32 = w.make_inputs(pad_fill=0.0)
+        v = synth.to_storage(v32, w.dtype)[0].to(dev)
+        om = synth.to_storage(om32, w.dtype)[0].to(dev)
+        y = torch.empty((w.N, w.Ho, w.Wo, w.C), dtype=v.dtype, device=dev)
+        ms = cold_ms(lambda: dcnv4.dcnv4_forward(v, om, y, **w.kwargs()), flush, stream)
+        nbytes = w.fwd_bytes()
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"dtype": w.dtype, "ms": round(ms, 5), "points_per_s": w.points / (ms * 1e-3),
+                     "compulsory_bytes": nbytes, "gbps": round(gbps, 1),
+                     "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+        if name.startswith("c3"):
+            agg_bytes += nbytes
+            agg_ms += ms
+        del v, om, y
+    gbps = agg_bytes / (agg_ms * 1e-3) / 1e9
+    out["c3_aggregate_fwd_fp16"] = {"ms": round(agg_ms, 5), "compulsory_bytes": agg_bytes, "gbps": round(gbps, 1),
+                                    "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                                    "note": "the four fp16 stage shapes, sum of bytes / sum of times"}
+    torch.cuda.empty_cache()
+    return out
+
+
+def share_detail(flush, stream):
+    """The step's workload at the batch share one GPU of 8 (N=8) or 4 (N=16)
+    would hold, cold: forward and backward ms and fractions of 8 TB/s."""
+    import torch
+
+    from dynamic_sparse_vision_amd import dcnv4
+    from dynamic_sparse_vision_amd.workloads import WORKLOADS
+
+    base = WORKLOADS["c2_fwd_fp32_56x56_b64"]
+    out = {}
+    for n in (8, 16, 64):
+        w = dataclasses.replace(base, N=n)
+        gen = torch.Generator(device="cuda").manual_seed(n)
+        v = torch.randn((n, w.H, w.W, w.C), device="cuda", generator=gen)
+        om = 2.0 * torch.randn((n, w.Ho, w.Wo, w.P), device="cuda", generator=gen)
+        g = torch.randn((n, w.Ho, w.Wo, w.C), device="cuda", generator=gen)
+        y = torch.empty_like(g)
+        gv, gom = torch.empty_like(v), torch.empty_like(om)
+        f_ms = cold_ms(lambda: dcnv4.dcnv4_forward(v, om, y, **w.kwargs()), flush, stream)
+        b_ms = cold_ms(lambda: dcnv4.dcnv4_backward(v, om, g, gv, gom, **w.kwargs()), flush, stream)
+        out[f"N={n}"] = {"forward_ms": round(f_ms, 5), "backward_ms": round(b_ms, 5),
+                         "forward_frac_of_peak": round(w.fwd_bytes() / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "backward_frac_of_peak": round(w.bwd_bytes() / (b_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        del v, om, g, y, gv, gom
+    torch.cuda.empty_cache()
+    return out
+
+
+def launch_floor(stream):
+    """Launch-latency floor on the launch stream: a one-element fill kernel,
+    median of 50 calls."""
+    import torch
+
+    x = torch.empty(1, device="cuda")
+    times = []
+    for i in range(60):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        x.fill_(float(i))
+        e1.record(stream)
+        e1.synchronize()
+        if i >= 10:
+            times.append(e0.elapsed_time(e1))
+    return round(statistics.median(times), 5)
+
+
+def first_call_parity(w, s, arrays):
+    """The first step's forward and backward on the first and last image of
+    the batch against the oracle (fp32 tolerance 1e-5 + 1e-5 |ref|)."""
+    import numpy as np
+
+    import oracle
+
+    v32, om32, g32 = arrays
+    worst = 0.0
+    ok = True
+    for n in (0, w.N - 1):
+        sl = slice(n, n + 1)
+        ref = oracle.forward(v32[sl], om32[sl], **w.kwargs())
+        rgv, rgom = oracle.backward(v32[sl], om32[sl], g32[sl], **w.kwargs())
+        for got, want in ((s["out"][sl], ref), (s["gv"][sl], rgv), (s["gom"][sl], rgom)):
+            a = got.float().cpu().numpy().astype(np.float64)
+            err = np.abs(a - want)
+            worst = max(worst, float(err.max()))
+            ok = ok and bool((err <= 1e-5 + 1e-5 * np.abs(want)).all())
+    return {"images": [0, w.N - 1], "max_abs_err": worst, "ok": ok,
+            "tolerance": "1e-5 + 1e-5*|ref| (forward, grad_value, grad_offset_mask)"}
+
+
+def run_dcnv4(args):
     import torch
 
     from dynamic_sparse_vision_amd import dcnv4
@@ -452,6 +638,13 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
+    # the first call of the run, checked against the oracle
+    step(0)
+    torch.cuda.synchronize()
+    parity = first_call_parity(w, sets[0], arrays) if w.dtype == "fp32" else None
+    print(f"bench: first-call parity {parity}", file=sys.stderr, flush=True)
+    if parity is not None and not parity["ok"]:
+        raise SystemExit("bench.py: the first call disagrees with the oracle")
     print(f"bench: {nsets} buffer sets of {per_set / 1e6:.0f} MB; warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
@@ -464,9 +657,10 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    fwd_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in events)
-    bwd_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in events)
-    print(f"bench: {ms_per_step:.4f} ms/step (forward {fwd_ms:.4f} ms, backward {bwd_ms:.4f} ms)",
+    fwd_times = [e[0].elapsed_time(e[1]) for e in events]
+    bwd_times = [e[1].elapsed_time(e[2]) for e in events]
+    fwd_ms, bwd_ms = statistics.median(fwd_times), statistics.median(bwd_times)
+    print(f"bench: {ms_per_step:.4f} ms/step (forward {fwd_ms:.4f} ms, backward {bwd_ms:.4f} ms, medians)",
           file=sys.stderr, flush=True)
 
     fwd_bytes = w.fwd_bytes()
@@ -480,20 +674,31 @@ def main():
                 "traffic": measured_traffic(w.name, dom),
                 "kernel": dom,
                 "algorithmic_bytes_per_launch": dom_bytes,
-                "avg_launch_ms": round(dom_ms, 5)}
+                "avg_launch_ms": round(dom_ms, 5),
+                "launch_ms_stat": "median over the timed steps",
+                "dominant_kernel": measured_kernel(w.name, dom)}
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, arrays, args.cpu_seconds)
-
+    del sets
+    torch.cuda.empty_cache()
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     detail = {
         "forward_ms": round(fwd_ms, 5), "backward_ms": round(bwd_ms, 5),
         "forward_gbps": round(fwd_bytes / (fwd_ms * 1e-3) / 1e9, 1),
         "backward_gbps": round(bwd_bytes / (bwd_ms * 1e-3) / 1e9, 1),
         "forward_bytes": fwd_bytes, "backward_bytes": bwd_bytes,
         "buffer_sets": nsets, "set_bytes": per_set,
+        "first_call_parity": parity,
     }
+    if not args.no_detail:
+        detail["launch_floor_ms"] = launch_floor(stream)
+        detail["forward_workloads_cold"] = forward_detail(flush, stream)
+        detail["one_gpu_share_cold"] = share_detail(flush, stream)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, arrays, args.cpu_seconds)
+
     line = {
         "metric": METRIC,
         "value": w.points / (ms_per_step * 1e-3),

@@ -376,7 +376,8 @@ int tile_lds(const Problem &p, TilePlan *tp, int R, int pixel_bytes)
 
 int plan_tiled_common(const Problem &p, int elem, int row_elems, int pixel_bytes, int r_max, int lds_budget, TilePlan *tp)
 {
-    if ((p.Cg * elem) % 16 != 0 || p.K > kMaxTiledK)
+    // near-sample addresses take floors below 2^22 in magnitude
+    if ((p.Cg * elem) % 16 != 0 || p.K > kMaxTiledK || p.H > (1 << 21) || p.W > (1 << 21))
         return DCNV4_ERR_UNSUPPORTED;
     tp->nvp = p.Cg * elem / 16;
     if (!pow2(tp->nvp))
@@ -389,7 +390,7 @@ int plan_tiled_common(const Problem &p, int elem, int row_elems, int pixel_bytes
 #ifndef DCNV4_DP_FIRST
 #define DCNV4_DP_FIRST 8
 #endif
-    for (int cand : {DCNV4_DP_FIRST, 8, 16, 4}) {
+    for (int cand : {DCNV4_DP_FIRST, 8, 4}) {
         if (p.Cg % cand == 0 && (cand * elem) % 16 == 0) {
             dp = cand;
             break;

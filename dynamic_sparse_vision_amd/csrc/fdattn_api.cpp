@@ -166,10 +166,17 @@ int flash_deform_attn_backward_workspace(const int *spatial_shapes, int num_leve
     return DCNV4_OK;
 }
 
-int flash_deform_attn_backward(const void *value, const int *spatial_shapes, int num_levels, const void *loc_attn,
-                               const void *grad_output, void *grad_value, void *grad_loc_attn, void *workspace,
-                               size_t workspace_bytes, int N, int num_value, int num_query, int num_heads,
-                               int head_dim, int num_points, int loc_attn_channels, int dtype, void *stream)
+}  // extern "C"
+
+namespace {
+
+// The backward with the caller's workspace (workspace / workspace_bytes,
+// or NULL: the device-atomic path), or, with `noalloc`, with the library's
+// own scratch array, in as many launches as the array's size requires.
+int backward_call(const void *value, const int *spatial_shapes, int num_levels, const void *loc_attn,
+                  const void *grad_output, void *grad_value, void *grad_loc_attn, void *workspace,
+                  size_t workspace_bytes, bool noalloc, int N, int num_value, int num_query, int num_heads,
+                  int head_dim, int num_points, int loc_attn_channels, int dtype, void *stream)
 {
     dcnv4::clear_hip_error();
     fdattn::Problem p;
@@ -186,7 +193,17 @@ int flash_deform_attn_backward(const void *value, const int *spatial_shapes, int
         !aligned16(grad_loc_attn) || !aligned16(workspace))
         return DCNV4_ERR_ALIGN;
     size_t need = 0;
-    if (workspace && num_query > 0) {
+    if (noalloc && num_query > 0) {
+        // the largest number of images per launch whose workspace fits the
+        // scratch array (none fits: refused)
+        int fit = std::min(N, per_launch);
+        while (fit > 0 && workspace_need(p, fit, fit) > fdattn::kNoAllocScratchBytes)
+            --fit;
+        if (fit == 0)
+            return DCNV4_ERR_UNSUPPORTED;
+        per_launch = fit;
+        need = workspace_need(p, N, per_launch);
+    } else if (workspace && num_query > 0) {
         need = workspace_need(p, N, per_launch);
         if (workspace_bytes < need)
             return DCNV4_ERR_PARAM;
@@ -202,7 +219,7 @@ int flash_deform_attn_backward(const void *value, const int *spatial_shapes, int
     }
     if (overlap(grad_value, img_gv * N, grad_loc_attn, img_la * N))
         return DCNV4_ERR_PARAM;
-    if (need > 0) {
+    if (need > 0 && !noalloc) {
         const int64_t nw = (int64_t)need;
         for (int i = 0; i < 3; ++i) {
             if (overlap(workspace, nw, ins[i], in_sz[i]))
@@ -212,6 +229,12 @@ int flash_deform_attn_backward(const void *value, const int *spatial_shapes, int
             return DCNV4_ERR_PARAM;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (noalloc && need > 0) {
+        // every argument is checked: now the first HIP call
+        const hipError_t e = fdattn::noalloc_scratch(&workspace);
+        if (e != hipSuccess)
+            return dcnv4::hip_status(e);
+    }
     for (int n0 = 0; n0 < N; n0 += per_launch) {
         fdattn::Problem q = p;
         q.N = std::min(per_launch, N - n0);
@@ -231,6 +254,30 @@ int flash_deform_attn_backward(const void *value, const int *spatial_shapes, int
             return dcnv4::hip_status(e);
     }
     return DCNV4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flash_deform_attn_backward(const void *value, const int *spatial_shapes, int num_levels, const void *loc_attn,
+                               const void *grad_output, void *grad_value, void *grad_loc_attn, void *workspace,
+                               size_t workspace_bytes, int N, int num_value, int num_query, int num_heads,
+                               int head_dim, int num_points, int loc_attn_channels, int dtype, void *stream)
+{
+    return backward_call(value, spatial_shapes, num_levels, loc_attn, grad_output, grad_value, grad_loc_attn,
+                         workspace, workspace_bytes, false, N, num_value, num_query, num_heads, head_dim,
+                         num_points, loc_attn_channels, dtype, stream);
+}
+
+int flash_deform_attn_backward_noalloc(const void *value, const int *spatial_shapes, int num_levels,
+                                       const void *loc_attn, const void *grad_output, void *grad_value,
+                                       void *grad_loc_attn, int N, int num_value, int num_query, int num_heads,
+                                       int head_dim, int num_points, int loc_attn_channels, int dtype, void *stream)
+{
+    return backward_call(value, spatial_shapes, num_levels, loc_attn, grad_output, grad_value, grad_loc_attn,
+                         nullptr, 0, true, N, num_value, num_query, num_heads, head_dim, num_points,
+                         loc_attn_channels, dtype, stream);
 }
 
 }  // extern "C"

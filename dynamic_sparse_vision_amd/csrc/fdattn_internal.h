@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "flash_deform_attn.h"
+
 #include <cstdint>
 
 namespace fdattn {
@@ -27,9 +29,17 @@ struct Problem {
 // grad_value; with workspace == nullptr it zero-fills grad_value and adds to
 // it with device atomics.  Return hipError_t.
 size_t workspace_bytes(const Problem &p);
+
 hipError_t launch_forward(const Problem &p, const void *value, const void *loc_attn, void *output,
                           hipStream_t stream);
 hipError_t launch_backward(const Problem &p, const void *value, const void *loc_attn, const void *grad_output,
                            float *grad_value, void *grad_loc_attn, void *workspace, hipStream_t stream);
+
+// flash_deform_attn_backward_noalloc: its workspace is a library-owned
+// device array of this many bytes per device (fdattn_noalloc.hip).
+constexpr size_t kNoAllocScratchBytes = FLASH_DEFORM_ATTN_NOALLOC_SCRATCH_BYTES;
+// Device address of that array on the current device, looked up on the
+// first call per device (hipGetSymbolAddress) and kept; no allocation.
+hipError_t noalloc_scratch(void **ptr);
 
 }  // namespace fdattn

@@ -315,7 +315,9 @@ __global__ __launch_bounds__(kThreads) void fdattn_fwd(Args a)
             const float y = __builtin_fmaf(v, Hf, -0.5f);
             const bool in = live(y, x, Hf, Wf);
             const float att = expf(ld1(row + 2 * LK + i) - mx) * inv;
-            Corners c = corners(y, x, H, W, start, a.pix_bytes, base);
+            // a dead sample (huge or NaN location included) is placed at
+            // (-1, -1): only bounded floors are converted to integers
+            Corners c = corners(in ? y : -1.0f, in ? x : -1.0f, H, W, start, a.pix_bytes, base);
             float v0[8], v1[8], v2[8], v3[8];
             load8<T>(vr, in ? c.o[0] : kOutOfRange, v0);
             load8<T>(vr, in ? c.o[1] : kOutOfRange, v1);
@@ -481,7 +483,9 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd_loc(Args a)
             const float y = __builtin_fmaf(v, Hf, -0.5f);
             const bool in = live(y, x, Hf, Wf);
             const float att = expf(ld1(row + 2 * LK + i) - mx) * inv;
-            const Corners c = corners(y, x, H, W, start, a.pix_bytes, base);
+            // a dead sample (huge or NaN location included) is placed at
+            // (-1, -1): only bounded floors are converted to integers
+            const Corners c = corners(in ? y : -1.0f, in ? x : -1.0f, H, W, start, a.pix_bytes, base);
             float v0[8], v1[8], v2[8], v3[8];
             load8<T>(vr, in ? c.o[0] : kOutOfRange, v0);
             load8<T>(vr, in ? c.o[1] : kOutOfRange, v1);

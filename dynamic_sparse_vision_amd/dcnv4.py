@@ -74,6 +74,8 @@ def load() -> ctypes.CDLL:
     lib.flash_deform_attn_backward.restype = i
     lib.flash_deform_attn_backward_workspace.argtypes = [ip, i] + [i] * 8 + [ctypes.POINTER(ctypes.c_size_t)]
     lib.flash_deform_attn_backward_workspace.restype = i
+    lib.flash_deform_attn_backward_noalloc.argtypes = [p, ip, i, p, p, p, p] + dims
+    lib.flash_deform_attn_backward_noalloc.restype = i
     _lib = lib
     return lib
 
@@ -123,6 +125,39 @@ def _check(t, name):
         raise ValueError(f"{name} must be contiguous (channel-last, dense)")
 
 
+def _expect_shape(t, name, want):
+    if tuple(t.shape) != tuple(want):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(want)}")
+
+
+def _check_geometry(value, offset_mask, outs, *, kernel_h, kernel_w, stride_h, stride_w, pad_h, pad_w,
+                    dilation_h, dilation_w, group, group_channels, remove_center):
+    """Every tensor's full shape against the call's geometry, before any
+    launch (the library sizes its buffer ranges from the geometry, so a
+    wrongly sized tensor would be read or written out of bounds).  ``outs``:
+    (tensor, name, "pixel" | "value" | "offset_mask") triples: per output
+    pixel (N,Ho,Wo,C), like value, or like offset_mask.  Invalid scalar
+    parameters, and offset_mask's entry count P (passed to the library as
+    om_channels), are left to the library, which reports their status code."""
+    if value.dim() != 4:
+        raise ValueError(f"value must be 4-D (N,H,W,C), got shape {tuple(value.shape)}")
+    N, H, W, C = value.shape
+    if C != group * group_channels:
+        raise ValueError(f"value has C={C} channels, expected group*group_channels = "
+                         f"{group}*{group_channels}")
+    try:
+        Ho, Wo = dcnv4_output_size(H, W, kernel_h, kernel_w, stride_h, stride_w, pad_h, pad_w,
+                                   dilation_h, dilation_w)
+    except Dcnv4Error:
+        return   # the library rejects the parameters with its own status
+    if offset_mask.dim() != 4 or tuple(offset_mask.shape[:3]) != (N, Ho, Wo):
+        raise ValueError(f"offset_mask has shape {tuple(offset_mask.shape)}, expected ({N}, {Ho}, {Wo}, P)")
+    for t, name, kind in outs:
+        want = {"pixel": (N, Ho, Wo, C), "value": tuple(value.shape),
+                "offset_mask": tuple(offset_mask.shape)}[kind]
+        _expect_shape(t, name, want)
+
+
 def _stream_ptr(stream):
     import torch
 
@@ -148,6 +183,10 @@ def dcnv4_forward_ex(value, offset_mask, output, *, kernel_h=3, kernel_w=3, stri
                      offset_scale=1.0, remove_center=False, softmax=False, stream=None,
                      _name="dcnv4_forward_ex") -> None:
     """dcnv4_forward with the DCNv3 softmax over the K masks when ``softmax``."""
+    _check_geometry(value, offset_mask, [(output, "output", "pixel")], kernel_h=kernel_h, kernel_w=kernel_w,
+                    stride_h=stride_h, stride_w=stride_w, pad_h=pad_h, pad_w=pad_w, dilation_h=dilation_h,
+                    dilation_w=dilation_w, group=group, group_channels=group_channels,
+                    remove_center=remove_center)
     for t, nm in ((value, "value"), (offset_mask, "offset_mask"), (output, "output")):
         _check(t, nm)
         if t.dtype != value.dtype:
@@ -188,6 +227,11 @@ def dcnv4_backward_ex(value, offset_mask, grad_output, grad_value, grad_offset_m
     (the mask gradient is then taken with respect to the logits)."""
     import torch
 
+    _check_geometry(value, offset_mask, [(grad_output, "grad_output", "pixel"), (grad_value, "grad_value", "value"),
+                                         (grad_offset_mask, "grad_offset_mask", "offset_mask")],
+                    kernel_h=kernel_h, kernel_w=kernel_w, stride_h=stride_h, stride_w=stride_w, pad_h=pad_h,
+                    pad_w=pad_w, dilation_h=dilation_h, dilation_w=dilation_w, group=group,
+                    group_channels=group_channels, remove_center=remove_center)
     for t, nm in ((value, "value"), (offset_mask, "offset_mask"), (grad_output, "grad_output"),
                   (grad_value, "grad_value"), (grad_offset_mask, "grad_offset_mask")):
         _check(t, nm)

@@ -21,6 +21,26 @@ def _shapes_arg(spatial_shapes):
     return arr, len(flat) // 2
 
 
+def _check_shapes(value, spatial_shapes, loc_attn, outs):
+    """Every tensor's full shape, before any launch: value (N,S,M,D) with
+    S = sum of H_l*W_l; loc_attn (N,Q,M,P) (P, passed as loc_attn_channels,
+    is checked by the library); ``outs``: (tensor, name, "query" | "value" |
+    "loc_attn") triples, shaped (N,Q,M,D), like value, or like loc_attn."""
+    if value.dim() != 4:
+        raise ValueError(f"value must be 4-D (N,S,M,D), got shape {tuple(value.shape)}")
+    N, S, M, D = value.shape
+    want_s = sum(int(h) * int(w) for h, w in spatial_shapes)
+    if S != want_s:
+        raise ValueError(f"value has S={S} rows, the levels hold {want_s} pixels")
+    if loc_attn.dim() != 4 or loc_attn.shape[0] != N or loc_attn.shape[2] != M:
+        raise ValueError(f"loc_attn has shape {tuple(loc_attn.shape)}, expected ({N}, Q, {M}, P)")
+    Q = loc_attn.shape[1]
+    for t, name, kind in outs:
+        want = {"query": (N, Q, M, D), "value": tuple(value.shape), "loc_attn": tuple(loc_attn.shape)}[kind]
+        if tuple(t.shape) != want:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want}")
+
+
 def flash_deform_attn_channels(num_levels: int, num_points: int) -> int:
     st = load().flash_deform_attn_channels(num_levels, num_points)
     if st < 0:
@@ -32,6 +52,7 @@ def flash_deform_attn_forward(value, spatial_shapes, loc_attn, output, *, num_po
     """value (N,S,M,D), loc_attn (N,Q,M,P), output (N,Q,M,D): device tensors
     of one dtype.  Enqueues the forward on ``stream`` (default: torch's
     current stream)."""
+    _check_shapes(value, spatial_shapes, loc_attn, [(output, "output", "query")])
     for t, nm in ((value, "value"), (loc_attn, "loc_attn"), (output, "output")):
         _check(t, nm)
         if t.dtype != value.dtype:
@@ -70,6 +91,9 @@ def flash_deform_attn_backward(value, spatial_shapes, loc_attn, grad_output, gra
     (gather) grad_value path; None selects the device-atomic path."""
     import torch
 
+    _check_shapes(value, spatial_shapes, loc_attn, [(grad_output, "grad_output", "query"),
+                                                    (grad_value, "grad_value", "value"),
+                                                    (grad_loc_attn, "grad_loc_attn", "loc_attn")])
     for t, nm in ((value, "value"), (loc_attn, "loc_attn"), (grad_output, "grad_output"),
                   (grad_value, "grad_value"), (grad_loc_attn, "grad_loc_attn")):
         _check(t, nm)
@@ -90,6 +114,35 @@ def flash_deform_attn_backward(value, spatial_shapes, loc_attn, grad_output, gra
         int(num_points), P, _dtype_code(value), _stream_ptr(stream))
     if st != DCNV4_OK:
         raise Dcnv4Error(st, "flash_deform_attn_backward")
+
+
+def flash_deform_attn_backward_noalloc(value, spatial_shapes, loc_attn, grad_output, grad_value, grad_loc_attn, *,
+                                       num_points, stream=None) -> None:
+    """flash_deform_attn_backward without a workspace argument and without
+    any allocation: the library's own per-device scratch array stands in for
+    the workspace.  Calls that overlap on one device race (they share the
+    array); calls ordered on one stream do not."""
+    import torch
+
+    _check_shapes(value, spatial_shapes, loc_attn, [(grad_output, "grad_output", "query"),
+                                                    (grad_value, "grad_value", "value"),
+                                                    (grad_loc_attn, "grad_loc_attn", "loc_attn")])
+    for t, nm in ((value, "value"), (loc_attn, "loc_attn"), (grad_output, "grad_output"),
+                  (grad_value, "grad_value"), (grad_loc_attn, "grad_loc_attn")):
+        _check(t, nm)
+        want = torch.float32 if nm == "grad_value" else value.dtype
+        if t.dtype != want:
+            raise TypeError(f"{nm} dtype {t.dtype} != {want}")
+    N, S, M, D = value.shape
+    Q, P = loc_attn.shape[1], loc_attn.shape[3]
+    arr, L = _shapes_arg(spatial_shapes)
+    st = load().flash_deform_attn_backward_noalloc(
+        ctypes.c_void_p(value.data_ptr()), arr, L, ctypes.c_void_p(loc_attn.data_ptr()),
+        ctypes.c_void_p(grad_output.data_ptr()), ctypes.c_void_p(grad_value.data_ptr()),
+        ctypes.c_void_p(grad_loc_attn.data_ptr()), N, S, Q, M, D, int(num_points), P, _dtype_code(value),
+        _stream_ptr(stream))
+    if st != DCNV4_OK:
+        raise Dcnv4Error(st, "flash_deform_attn_backward_noalloc")
 
 
 def forward(value, spatial_shapes, loc_attn, num_points):

@@ -45,14 +45,20 @@
  * Ownership and execution, all entry points:
  *   - The caller allocates every buffer (device memory for tensors), dense,
  *     with 16-byte aligned base pointers.  The library allocates nothing,
- *     frees nothing and keeps no pointer after returning.
+ *     frees nothing and keeps no pointer after returning.  (One static
+ *     device array exists, the scratch of flash_deform_attn_backward_noalloc
+ *     in flash_deform_attn.h; no DCNv4 entry point uses it.)
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *     the null stream) and the call returns without waiting; results are
  *     valid once the stream has completed the work.
  *   - Outputs must not overlap inputs or each other.
  *   - Reentrant.  Process state: a per-thread copy of the last HIP error
- *     message, and a record of the kernels whose dynamic-LDS limit has
- *     been raised (hipFuncSetAttribute, once per kernel, under a lock).
+ *     message; a record of the kernels whose dynamic-LDS limit has been
+ *     raised (hipFuncSetAttribute, once per kernel and device, under a
+ *     lock); and two caches of tile plans (forward, backward), each of up
+ *     to 64 geometries, keyed by the call's scalar arguments (not by
+ *     pointers), filled on first use and shared by all threads under a
+ *     lock.  None of it holds device memory or caller pointers.
  *
  * Errors: every entry point returns DCNV4_OK (0) or a negative status.  All
  * argument checks run before any HIP call, so a rejected call has no side
@@ -102,7 +108,9 @@ DCNV4_API const char *dcnv4_status_string(int status);
 DCNV4_API const char *dcnv4_last_hip_error(void);
 
 /*
- * Output size of the sampling grid, as for a regular convolution:
+ * Output size of the sampling grid, as for a regular convolution (the
+ * sampling grid p0 + p_k is that of a regular convolution when the offsets
+ * are zero: walkthrough "DCNv4论文解析", section 1.2):
  *   Ho = floor((H + 2*pad_h - (dilation_h*(kernel_h-1) + 1)) / stride_h) + 1
  * and likewise Wo.  Writes *Ho, *Wo.  Errors: NULL, PARAM (kernel, stride,
  * dilation < 1 or pad < 0), SHAPE (H, W < 1 or Ho, Wo < 1).

@@ -136,6 +136,37 @@ DCNV4_API int flash_deform_attn_backward(const void *value, const int *spatial_s
                                          int num_value, int num_query, int num_heads, int head_dim, int num_points,
                                          int loc_attn_channels, int dtype, void *stream);
 
+/*
+ * flash_deform_attn_backward with no allocation and no workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * sorted grad_value path runs in a library-owned device array of
+ * FLASH_DEFORM_ATTN_NOALLOC_SCRATCH_BYTES per device (a static device
+ * variable, held by every device the library runs on until the process
+ * ends) instead of a caller workspace; the call itself allocates and frees
+ * nothing.  The caller still allocates value, loc_attn, grad_output,
+ * grad_value and grad_loc_attn, as for flash_deform_attn_backward.
+ *
+ * Arguments, layouts, results and errors as flash_deform_attn_backward with
+ * a workspace, except: the images of a call are processed in launches of
+ * as many images as the array holds; UNSUPPORTED when one image alone needs
+ * more than FLASH_DEFORM_ATTN_NOALLOC_SCRATCH_BYTES of workspace (the size
+ * flash_deform_attn_backward_workspace reports for N = 1).  When a slice's
+ * bins do not fit the on-chip sort, the device-atomic path runs, which
+ * needs no workspace.  Every call on one device uses that device's one
+ * array, so calls that overlap on one device (concurrent streams or host
+ * threads) race and give wrong results; calls ordered on one stream are
+ * safe.  The array keeps the last call's contents; what must start at zero
+ * is cleared by each call (with a fill kernel, not a memset).
+ */
+#define FLASH_DEFORM_ATTN_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+DCNV4_API int flash_deform_attn_backward_noalloc(const void *value, const int *spatial_shapes, int num_levels,
+                                                 const void *loc_attn, const void *grad_output, void *grad_value,
+                                                 void *grad_loc_attn, int N, int num_value, int num_query,
+                                                 int num_heads, int head_dim, int num_points, int loc_attn_channels,
+                                                 int dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,7 +36,7 @@ def test_header_declares_the_abi():
         "dcnv4_output_size", "dcnv4_om_channels", "dcnv4_forward", "dcnv4_backward",
         "dcnv4_forward_ex", "dcnv4_backward_ex",
         "flash_deform_attn_channels", "flash_deform_attn_forward", "flash_deform_attn_backward",
-        "flash_deform_attn_backward_workspace"])
+        "flash_deform_attn_backward_workspace", "flash_deform_attn_backward_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -205,3 +205,49 @@ def test_valid_call_without_a_device_reports_hip_error():
     st = fwd()
     assert st == HIP
     assert dcnv4.load().dcnv4_last_hip_error() != b""
+
+
+def test_binding_checks_every_shape_before_a_launch():
+    """Each tensor's full shape is compared with the geometry in the binding:
+    the library sizes its buffer ranges from the geometry, so a wrongly
+    shaped tensor must be refused before it is handed over.  (Meta tensors:
+    shapes only; a correctly shaped call then stops at the device check.)"""
+    import torch
+
+    def t(*shape, dtype=torch.float32):
+        return torch.empty(shape, dtype=dtype, device="meta")
+
+    geo = dict(group=4, group_channels=16)
+    v, om, out = t(2, 6, 5, 64), t(2, 6, 5, 112), t(2, 6, 5, 64)
+    gv, gom = t(2, 6, 5, 64), t(2, 6, 5, 112)
+    with pytest.raises(ValueError, match="device tensor"):
+        dcnv4.dcnv4_forward(v, om, out, **geo)
+    with pytest.raises(ValueError, match="device tensor"):
+        dcnv4.dcnv4_backward(v, om, out, gv, gom, **geo)
+    bad_fwd = [
+        (t(2, 6, 5, 48), om, out, "channels"),          # C != G * C'
+        (t(2, 6, 5), om, out, "4-D"),
+        (v, t(2, 6, 4, 112), out, "offset_mask"),        # wrong Wo
+        (v, t(1, 6, 5, 112), out, "offset_mask"),        # wrong N
+        (v, om, t(2, 6, 5, 32), "output"),
+        (v, om, t(2, 5, 5, 64), "output"),
+    ]
+    for vv, oo, yy, what in bad_fwd:
+        with pytest.raises(ValueError, match=what):
+            dcnv4.dcnv4_forward(vv, oo, yy, **geo)
+        with pytest.raises(ValueError, match=what):
+            dcnv4.dcnv4_forward_ex(vv, oo, yy, softmax=True, **geo)
+    # stride 2: the output grid is 3 x 3
+    s2 = dict(geo, stride_h=2, stride_w=2)
+    with pytest.raises(ValueError, match="offset_mask"):
+        dcnv4.dcnv4_forward(v, om, out, **s2)
+    with pytest.raises(ValueError, match="device tensor"):
+        dcnv4.dcnv4_forward(v, t(2, 3, 3, 112), t(2, 3, 3, 64), **s2)
+    bad_bwd = [
+        (out[:, :, :4], gv, gom, "grad_output"),
+        (out, t(2, 6, 5, 32), gom, "grad_value"),
+        (out, gv, t(2, 6, 5, 104), "grad_offset_mask"),
+    ]
+    for go, g1, g2, what in bad_bwd:
+        with pytest.raises(ValueError, match=what):
+            dcnv4.dcnv4_backward(v, om, go, g1, g2, **geo)

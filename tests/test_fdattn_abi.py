@@ -2,13 +2,14 @@
 every rejected argument is refused before any HIP call (the pointers are
 fake, 16-byte aligned addresses that are never dereferenced)."""
 import ctypes
+import os
 
 import pytest
 
 from dynamic_sparse_vision_amd import dcnv4
 from dynamic_sparse_vision_amd import flash_deform_attn as fda
 
-OK, NULL, SHAPE, PARAM, DTYPE, ALIGN, UNSUP, OVERFLOW = 0, -1, -2, -3, -4, -5, -6, -7
+OK, NULL, SHAPE, PARAM, DTYPE, ALIGN, UNSUP, OVERFLOW, HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 A, B, Cp, D, E = (ctypes.c_void_p(x) for x in (0x100000000, 0x200000000, 0x300000000,
                                                0x400000000, 0x500000000))
@@ -125,3 +126,76 @@ def test_workspace_size_and_checks():
     assert bwd(ws=ctypes.c_void_p(0x600000008), ws_bytes=n) == ALIGN
     assert bwd(ws=ctypes.c_void_p(0x100000000 + 64), ws_bytes=n) == PARAM  # overlaps value
     assert bwd(ws=ctypes.c_void_p(0x400000000 + 64), ws_bytes=n) == PARAM  # overlaps grad_value
+
+
+def test_binding_checks_every_shape_before_a_launch():
+    """Every tensor's full shape is compared in the binding before the
+    library is called (meta tensors: shapes only; a correctly shaped call
+    stops at the device check)."""
+    import torch
+
+    from dynamic_sparse_vision_amd import flash_deform_attn as fda
+
+    def t(*shape, dtype=torch.float32):
+        return torch.empty(shape, dtype=dtype, device="meta")
+
+    shapes = ((8, 10), (4, 5))                       # S = 100
+    v, la, out = t(2, 100, 2, 32), t(2, 7, 2, 24), t(2, 7, 2, 32)
+    gv, gla = t(2, 100, 2, 32), t(2, 7, 2, 24)
+    with pytest.raises(ValueError, match="device tensor"):
+        fda.flash_deform_attn_forward(v, shapes, la, out, num_points=4)
+    with pytest.raises(ValueError, match="device tensor"):
+        fda.flash_deform_attn_backward(v, shapes, la, out, gv, gla, num_points=4)
+    for vv, ll, yy, what in [(t(2, 99, 2, 32), la, out, "rows"), (v, t(1, 7, 2, 24), out, "loc_attn"),
+                             (v, t(2, 7, 3, 24), out, "loc_attn"), (v, la, t(2, 6, 2, 32), "output"),
+                             (v, la, t(2, 7, 2, 16), "output")]:
+        with pytest.raises(ValueError, match=what):
+            fda.flash_deform_attn_forward(vv, shapes, ll, yy, num_points=4)
+    for go, g1, g2, what in [(t(2, 7, 2, 16), gv, gla, "grad_output"), (out, t(2, 100, 2, 16), gla, "grad_value"),
+                             (out, gv, t(2, 7, 2, 16), "grad_loc_attn")]:
+        with pytest.raises(ValueError, match=what):
+            fda.flash_deform_attn_backward(v, shapes, la, go, g1, g2, num_points=4)
+
+
+def bwd_noalloc(ptrs=(A, B, Cp, D, E), shapes=SHAPES, L=None, N=2, S=100, Q=7, M=2, Dh=32, K=4, P=24, dtype=0):
+    arr, nl = shapes_arr(shapes)
+    return dcnv4.load().flash_deform_attn_backward_noalloc(ptrs[0], arr, nl if L is None else L, ptrs[1], ptrs[2],
+                                                           ptrs[3], ptrs[4], N, S, Q, M, Dh, K, P, dtype, None)
+
+
+def test_noalloc_argument_checks():
+    """The no-allocation backward validates like the backward with a
+    workspace, before any HIP call."""
+    assert bwd_noalloc(dtype=7) == DTYPE
+    assert bwd_noalloc(S=99) == SHAPE
+    assert bwd_noalloc(P=20) == PARAM
+    assert bwd_noalloc(Dh=128) == UNSUP            # the backward takes D <= 64
+    assert bwd_noalloc(N=0, ptrs=(None,) * 5) == OK
+    for i in range(5):
+        ptrs = [A, B, Cp, D, E]
+        ptrs[i] = None
+        assert bwd_noalloc(ptrs=tuple(ptrs)) == NULL
+    assert bwd_noalloc(ptrs=(A, B, Cp, ctypes.c_void_p(0x400000004), E)) == ALIGN
+    assert bwd_noalloc(ptrs=(A, B, Cp, ctypes.c_void_p(0x100000040), E)) == PARAM   # grad_value overlaps value
+
+
+def test_noalloc_refuses_images_larger_than_its_scratch():
+    """One image whose sorted-path workspace exceeds the 128 MiB array is
+    refused (UNSUPPORTED) before any HIP call; the size limit is the
+    workspace the caller-workspace entry point reports for N = 1."""
+    limit = 128 << 20
+    # one 64x64 level, 8 heads, 4 points: 16 bytes x 2 per sample plus keys
+    shapes = [(64, 64)]
+    S = 64 * 64
+    for Q, expect_fit in ((100_000, True), (300_000, False)):
+        st, need = ws_bytes(shapes=shapes, N=1, S=S, Q=Q, M=8, Dh=32, K=4, P=16)
+        assert st == OK and (need <= limit) == expect_fit, (Q, need)
+    # only the refused call is made (a valid one would reach the runtime)
+    assert bwd_noalloc(shapes=shapes, N=1, S=S, Q=300_000, M=8, Dh=32, K=4, P=16) == UNSUP
+    assert bwd_noalloc(shapes=shapes, N=3, S=S, Q=300_000, M=8, Dh=32, K=4, P=16) == UNSUP
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="only meaningful where no GPU device exists")
+def test_noalloc_valid_call_without_a_device_reports_hip_error():
+    assert bwd_noalloc() == HIP
+    assert dcnv4.load().dcnv4_last_hip_error() != b""

@@ -2,16 +2,21 @@
 buffer) is split into launches of whole images.  The split must not change
 any result: N = 10 images of 256x256x512 fp32 (G = 32, C' = 16; 226 MB of
 offset_mask per image, so nine images per launch) against the same images
-called one at a time, forward and backward.  The single-image calls use the
-kernels whose parity with the oracle the other tests establish; the output
-and grad_offset_mask agree bit for bit, grad_value (summed in an order that
-depends on wave timing) within the fp32 parity bound.
+called one at a time, forward and backward: the output and
+grad_offset_mask agree bit for bit, grad_value (summed in an order that
+depends on wave timing) within the fp32 parity bound.  The first and the
+last image of the split call (one in each launch) are also compared with
+the oracle, forward and backward, at the fp32 parity tolerance.  The flash
+deformable attention case is GPU against GPU only (split call against
+single-image calls), whose parity with the oracle the other tests establish.
 """
+import numpy as np
 import pytest
 import torch
 
+import oracle
 from dynamic_sparse_vision_amd import dcnv4
-from tests.test_gpu_parity import say
+from tests.test_gpu_parity import check, say
 
 pytestmark = pytest.mark.gpu
 
@@ -40,6 +45,14 @@ def test_split_launches_match_single_images():
         assert torch.equal(gom[n:n + 1], gom1), f"image {n}: grad_offset_mask differs"
         assert bool(((gv[n:n + 1] - gv1).abs() <= 1e-5 + 1e-5 * gv1.abs()).all()), f"image {n}: grad_value differs"
     say(f"  {N} images: the split call agrees with the single-image calls")
+    for n in (0, N - 1):
+        vn, omn, gon = (t[n:n + 1].cpu().numpy() for t in (v, om, go))
+        say(f"  image {n} against the oracle")
+        check(out[n:n + 1].cpu().numpy(), oracle.forward(vn, omn, **kw), "fp32", f"image {n} forward")
+        rgv, rgom = oracle.backward(vn, omn, gon, **kw)
+        check(gv[n:n + 1].cpu().numpy(), rgv, "fp32", f"image {n} grad_value")
+        check(gom[n:n + 1].cpu().numpy(), rgom, "fp32", f"image {n} grad_offset_mask")
+        assert np.all(gom[n:n + 1, ..., 3 * G * K:].cpu().numpy() == 0)
 
 
 def test_flash_deform_attn_split_launches_match_single_images():

@@ -1,0 +1,84 @@
+"""flash_deform_attn_backward_noalloc (the library's own scratch array in
+place of a caller workspace) against flash_deform_attn_backward with a
+caller workspace, through the C ABI: two calls in a row, the second on a
+smaller problem (the array keeps the first call's contents, so what must
+start at zero has to be cleared by the call).  grad_loc_attn is
+deterministic on both paths and must agree bit for bit; grad_value is
+summed in an order that depends on wave timing and must agree within the
+fp32 parity bound (|a - b| <= 1e-5 + 1e-5 |b|).  The smaller call is also
+compared with the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dynamic_sparse_vision_amd import flash_deform_attn as fda
+from dynamic_sparse_vision_amd import synth
+from dynamic_sparse_vision_amd.workloads import FDA_WORKLOADS
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def _inputs(w, N):
+    v32, la32, g32 = w.make_inputs(N=N)
+    v, la, g = (synth.to_storage(a, w.dtype)[0].cuda() for a in (v32, la32, g32))
+    return (v32, la32, g32), (v, la, g)
+
+
+def _both(w, N):
+    host, (v, la, g) = _inputs(w, N)
+    gv_ws, gla_ws = fda.backward(v, w.shapes, la, g, w.K)            # caller workspace
+    gv_na = torch.full(v.shape, float("nan"), dtype=torch.float32, device="cuda")
+    gla_na = torch.full_like(la, float("nan"))
+    fda.flash_deform_attn_backward_noalloc(v, w.shapes, la, g, gv_na, gla_na, num_points=w.K)
+    torch.cuda.synchronize()
+    return host, (gv_ws, gla_ws), (gv_na, gla_na)
+
+
+def _agree(ws, na, what):
+    gv_ws, gla_ws = ws
+    gv_na, gla_na = na
+    assert torch.equal(gla_ws, gla_na), f"{what}: grad_loc_attn differs"
+    a, b = gv_na.cpu().numpy().astype(np.float64), gv_ws.cpu().numpy().astype(np.float64)
+    assert np.isfinite(a).all(), f"{what}: grad_value not fully written"
+    err = np.abs(a - b)
+    say(f"  {what}: grad_loc_attn bitwise equal, grad_value max|diff| {err.max():.3e}")
+    assert (err <= 1e-5 + 1e-5 * np.abs(b)).all(), f"{what}: grad_value differs"
+
+
+def test_noalloc_matches_workspace_entry_two_calls():
+    big = FDA_WORKLOADS["fda_enc_800x1280_b4_fp32"]
+    small = FDA_WORKLOADS["fda_small_fp32"]
+    say(f"[noalloc] 1: {big.name} N=2 (one image per launch in the 128 MiB array)")
+    _, ws, na = _both(big, 2)
+    _agree(ws, na, "first call")
+    say(f"[noalloc] 2: {small.name} N=1 (smaller, right after)")
+    (v32, la32, g32), ws, na = _both(small, 1)
+    _agree(ws, na, "second call")
+    rgv, rgla = oracle.fdattn_backward(v32, small.shapes, la32, g32, small.K)
+    a = na[0].cpu().numpy().astype(np.float64)
+    assert (np.abs(a - rgv) <= 1e-5 + 1e-5 * np.abs(rgv)).all(), "second call: grad_value vs oracle"
+    LK = small.L * small.K
+    b = na[1].cpu().numpy().astype(np.float64)[..., 2 * LK:3 * LK]
+    r = rgla[..., 2 * LK:3 * LK]
+    assert (np.abs(b - r) <= 1e-5 + 1e-5 * np.abs(r)).all(), "second call: logit gradients vs oracle"
+
+
+def test_noalloc_16bit_and_empty_queries():
+    w = FDA_WORKLOADS["fda_enc_800x1280_b4_fp16"]
+    say(f"[noalloc] {w.name} N=1 fp16")
+    _, ws, na = _both(w, 1)
+    _agree(ws, na, "fp16 call")
+    # no query: grad_value is all zeros, the array is not touched
+    v = torch.randn((1, w.S, w.M, w.D), device="cuda").half()
+    la = torch.zeros((1, 0, w.M, w.P), device="cuda").half()
+    g = torch.zeros((1, 0, w.M, w.D), device="cuda").half()
+    gv = torch.full(v.shape, 7.0, dtype=torch.float32, device="cuda")
+    gla = torch.empty_like(la)
+    fda.flash_deform_attn_backward_noalloc(v, w.shapes, la, g, gv, gla, num_points=w.K)
+    torch.cuda.synchronize()
+    assert bool((gv == 0).all())
