@@ -213,7 +213,7 @@ bool pow2(int v)
 constexpr int kRowSlots = 512;        // a staged LDS row spans at most 8 x 64 slots
 constexpr int kMaxTiledK = 25;        // grid points of the tiled kernels
 #ifndef DCNV4_FWD_RMAX
-#define DCNV4_FWD_RMAX 7
+#define DCNV4_FWD_RMAX 5
 #endif
 constexpr int kForwardRmax = DCNV4_FWD_RMAX;   // largest halo of the forward tiles
 #ifndef DCNV4_BWD_RMAX
@@ -417,15 +417,127 @@ int plan_tiled_common(const Problem &p, int elem, int row_elems, int pixel_bytes
     return DCNV4_ERR_UNSUPPORTED;
 }
 
+// The forward's LDS region of a tile along one axis: the tile's grid span
+// plus a halo of R, clamped to the image plus a one-pixel zero border
+// (-1 .. size); the kernel computes the same bounds (fwd_region).
+int fwd_region_len(int t0, int t, int stride, int pad, int kern, int dil, int R, int size)
+{
+    const int lo_u = t0 * stride - pad - R;
+    const int span = (t - 1) * stride + (kern - 1) * dil + 2 * R + 2;
+    return std::min(lo_u + span, size + 1) - std::max(lo_u, -1);
+}
+
+// Largest region length over the tiles of one axis, and the sum of the
+// region lengths (the staged pixels along that axis).
+// The allocation holds at least 2 x 2 pixels: samples that are not near
+// read the region's first footprint (with zero weights), also in a block
+// whose clamped region is empty (a tile that sees only padding).
+void fwd_region_stats(int out, int t, int stride, int pad, int kern, int dil, int R, int size, int *maxlen, long *sum)
+{
+    *maxlen = 2;
+    *sum = 0;
+    for (int t0 = 0; t0 < out; t0 += t) {
+        const int len = fwd_region_len(t0, t, stride, pad, kern, dil, R, size);
+        *maxlen = std::max(*maxlen, len);
+        *sum += std::max(len, 0);
+    }
+}
+
+// Forward tiles: th x tw pixels of gb groups, `lanes` threads of dp
+// channels per pixel and group, at most kTileThreads threads; the LDS holds
+// the widest clamped region at pst 16-byte slots per pixel.  Modelled time,
+// summed over the tiles of an image: a lane-sample costs ~30 instructions
+// plus one FMA per channel and corner, a staged region slot ~8; blocks run
+// concurrently until `max_waves` share a CU (fewer when the LDS limits them).
+bool choose_fwd_tile(const Problem &p, int lanes, int dp, int gb, int pst, int R, int lds_budget, int max_waves,
+                     int *th, int *tw, int *rh, int *rw)
+{
+    double best = -1;
+    for (int w = 1; w <= 64 && w <= p.Wo; ++w) {
+        int rwm;
+        long rws;
+        fwd_region_stats(p.Wo, w, p.sw, p.pw, p.kw, p.dw, R, p.W, &rwm, &rws);
+        if (rwm * pst > kRowSlots)
+            break;
+        for (int h = 1; h <= 64 && h <= p.Ho; ++h) {
+            const int threads = h * w * gb * lanes;
+            if (threads > kTileThreads)
+                break;
+            int rhm;
+            long rhs;
+            fwd_region_stats(p.Ho, h, p.sh, p.ph, p.kh, p.dh, R, p.H, &rhm, &rhs);
+            const int lds = rhm * rwm * pst * 16;
+            if (lds > lds_budget)
+                continue;
+            const int waves = (threads + 63) / 64;
+            const int per_cu = std::min(kLdsPerCu / ((lds + kLdsGranule - 1) / kLdsGranule * kLdsGranule),
+                                        max_waves / waves);
+            if (per_cu < 1)
+                continue;
+            const double occ = std::min(1.0, per_cu * waves / (double)max_waves);
+            const double blocks = (double)((p.Ho + h - 1) / h) * ((p.Wo + w - 1) / w) * (p.G / gb);
+            const double work = blocks * waves * 64.0 * p.K * (30 + 4 * dp) + (double)rhs * rws * pst * 8 * (p.G / gb);
+            const double cost = work / occ;
+            if (best < 0 || cost < best) {
+                best = cost;
+                *th = h;
+                *tw = w;
+                *rh = rhm;
+                *rw = rwm;
+            }
+        }
+    }
+    return best >= 0;
+}
+
 int compute_forward_tiled(const Problem &p, TilePlan *tp)
 {
     *tp = TilePlan{};
-    // offsets and masks go to registers, the LDS holds the value rows only
-    const int st = plan_tiled_common(p, p.elem, 0, 0, kForwardRmax, kTiledMaxLds, tp);
-    if (st != DCNV4_OK)
-        return st;
-    tp->images_per_launch = (int)(kMaxBytesPerLaunch / image_bytes_max(p, false));
-    return DCNV4_OK;
+    // near-sample addresses take floors below 2^22 in magnitude
+    if ((p.Cg * p.elem) % 16 != 0 || p.K > kMaxTiledK || p.H > (1 << 21) || p.W > (1 << 21))
+        return DCNV4_ERR_UNSUPPORTED;
+    tp->nvp = p.Cg * p.elem / 16;
+    if (!pow2(tp->nvp))
+        return DCNV4_ERR_UNSUPPORTED;
+    // channels per lane: 16-bit pixels of 16 channels take one lane (two
+    // 128-bit vectors per corner); fp32 takes 8 channels per lane
+    int dp = 0;
+    const int cands16[] = {16, 8}, cands32[] = {8, 4};
+    for (int cand : (p.elem == 2 ? cands16 : cands32)) {
+        if (p.Cg % cand == 0 && (cand * p.elem) % 16 == 0) {
+            dp = cand;
+            break;
+        }
+    }
+    if (dp == 0)
+        return DCNV4_ERR_UNSUPPORTED;
+    tp->dp = dp;
+    tp->lanes = p.Cg / dp;
+    if (!pow2(tp->lanes) || tp->lanes > 64)
+        return DCNV4_ERR_UNSUPPORTED;
+    // groups per block: the largest power of two dividing G whose slices of
+    // a pixel make at most one 128-byte line, so that staging, offset/mask
+    // loads and output stores cover whole lines
+    tp->gb = 1;
+    while (p.G % (2 * tp->gb) == 0 && 2 * tp->gb * tp->nvp * 16 <= 128)
+        tp->gb *= 2;
+    const int nvb = tp->gb * tp->nvp;
+    tp->ps = nvb | 1;   // odd LDS pixel stride: random pixel reads spread over the banks
+    const int max_waves = 24;
+    for (int R = kForwardRmax; R >= 1; --R) {
+        if (!choose_fwd_tile(p, tp->lanes, dp, tp->gb, tp->ps, R, kTiledMaxLds, max_waves, &tp->th, &tp->tw, &tp->rh,
+                             &tp->rw))
+            continue;
+        tp->R = R;
+        tp->lds_bytes = tp->rh * tp->rw * tp->ps * 16;
+        // whole waves: the staging loop takes rows per wave
+        tp->threads = (tp->th * tp->tw * tp->gb * tp->lanes + 63) / 64 * 64;
+        tp->tiles_y = (p.Ho + tp->th - 1) / tp->th;
+        tp->tiles_x = (p.Wo + tp->tw - 1) / tp->tw;
+        tp->images_per_launch = (int)(kMaxBytesPerLaunch / image_bytes_max(p, false));
+        return DCNV4_OK;
+    }
+    return DCNV4_ERR_UNSUPPORTED;
 }
 
 int compute_backward_tiled(const Problem &p, TilePlan *tp)

@@ -57,6 +57,7 @@ struct TilePlan {
     // output tiles (forward, backward grad_offset_mask): th x tw pixels of
     // one (image, group); lanes threads of dp channels per pixel
     int dp, lanes, th, tw, threads;
+    int gb;              // forward: groups per block (their slices of a pixel are contiguous)
     int tiles_y, tiles_x;
     int R;
     int rh, rw;          // LDS value region, pixels

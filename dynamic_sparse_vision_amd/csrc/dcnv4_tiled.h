@@ -75,9 +75,13 @@ struct TArgs {
     unsigned k3_magic;           // ceil(2^32 / (3K))
     // output tiles
     int th, tw, tiles_y, tiles_x, lanes_shift;
+    int gb, gb_shift;            // forward: groups per block (a power of two), log2
+    int nvb, pst;                // forward: 16-byte vectors of a block's pixel slice; LDS pixel stride (slots)
+    unsigned pst_magic;
     int R, rh, rw;               // halo radius; LDS value region, pixels
     int ps, nvp;                 // LDS pixel stride; data vectors per pixel (16-byte units)
     unsigned ps_magic;
+    unsigned rw_magic;           // ceil(2^32 / rw)
     unsigned tw_magic;
     unsigned npad_magic;         // ceil(2^32 / (P - 3GK)), padding entries per pixel
     // cell tiles (backward grad_value)
@@ -544,6 +548,12 @@ inline TArgs make_targs(const Problem &p, const TilePlan &tp)
     a.ps = tp.ps;
     a.nvp = tp.nvp;
     a.ps_magic = magic_for(tp.ps);
+    a.rw_magic = magic_for(tp.rw);
+    a.gb = tp.gb > 0 ? tp.gb : 1;
+    a.gb_shift = log2i(a.gb);
+    a.nvb = a.gb * tp.nvp;
+    a.pst = a.nvb | 1;
+    a.pst_magic = magic_for(a.pst);
     a.npad_magic = magic_for(p.P - 3 * p.G * p.K);
     a.tw_magic = magic_for(tp.tw);
     for (int k = 0; k < p.K && k < kMaxTiledPoints; ++k) {

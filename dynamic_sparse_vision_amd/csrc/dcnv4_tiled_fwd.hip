@@ -42,111 +42,337 @@ __device__ __forceinline__ void far_sample_fwd(const Geom &geo, __amdgpu_buffer_
     }
 }
 
-// A block owns a th x tw output tile of one (image, group); `lanes` threads
-// per pixel, DP channels each.  The value rows of the tile plus a halo of R
-// pixels are staged in LDS while each lane loads its pixel's offsets and
-// masks into registers; the K samples are unrolled (KMAX >= K).  A far
-// sample (rare once R covers the offsets' spread) is taken on the spot from
-// global memory.
+// The LDS region of a forward block: the value rows and columns its
+// samples can reach within a halo of R pixels of the tile's grid, clamped
+// to the image plus a border of one pixel of zeros (rows -1 .. H, columns
+// -1 .. W): corners beyond that border only belong to samples that are not
+// live.  Region pixel (rr, cc) is image pixel (y0 + rr, x0 + cc).  A block
+// covers gb consecutive groups, whose channels of a pixel are one contiguous
+// slice of nvb 16-byte vectors (128 bytes, a whole cache line, where the
+// channel count allows); the LDS holds the slice of region pixel (rr, cc)
+// from 16-byte slot (rr * rw + cc) * pst, pst = nvb rounded up to odd (an
+// odd pixel stride spreads random pixel reads over the LDS banks), rw being
+// the region width the plan allocates (the widest region of any block).
+struct Region {
+    int y0, x0, rows, cols;
+};
+
+__device__ __forceinline__ Region fwd_region(const TArgs &a, const Tile &t)
+{
+    const Geom &g = a.geo;
+    const int y0u = t.oy0 * g.sh - g.ph - a.R, x0u = t.ox0 * g.sw - g.pw - a.R;
+    const int hspan = (a.th - 1) * g.sh + (g.kh - 1) * g.dh + 2 * a.R + 2;
+    const int wspan = (a.tw - 1) * g.sw + (g.kw - 1) * g.dw + 2 * a.R + 2;
+    Region r;
+    r.y0 = max(y0u, -1);
+    r.x0 = max(x0u, -1);
+    r.rows = min(y0u + hspan, g.H + 1) - r.y0;
+    r.cols = min(x0u + wspan, g.W + 1) - r.x0;
+    return r;
+}
+
+// Block -> (image, tile row, tile column, group block), group block
+// fastest; t.g is the block's first group.
+__device__ __forceinline__ Tile fwd_tile(const TArgs &a)
+{
+    int b = xcd_tile(blockIdx.x, gridDim.x);
+    const int gblocks = a.G >> a.gb_shift;
+    Tile t;
+    t.g = (b % gblocks) << a.gb_shift;
+    b /= gblocks;
+    const int tx = b % a.tiles_x;
+    b /= a.tiles_x;
+    const int ty = b % a.tiles_y;
+    t.n = b / a.tiles_y;
+    t.oy0 = ty * a.th;
+    t.ox0 = tx * a.tw;
+    return t;
+}
+
+// Stage the block's slice of the region's pixels (zeros outside the image)
+// with direct-to-LDS loads: consecutive lanes read consecutive 16-byte
+// vectors of a pixel's slice, so a wave instruction covers whole cache lines.
+// Waves take whole rows.
+__device__ __forceinline__ void stage_region(const TArgs &a, const Tile &t, const Region &rg, char *lds, int es)
+{
+    const Geom &geo = a.geo;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    const int row_slots = rg.cols * a.pst;
+    const unsigned cs = (unsigned)(geo.C * es), goff = (unsigned)(t.g * a.Cg * es);
+    // slot j of a row: region column j / pst, vector j % pst (the last of an
+    // even slice is the padding slot, zero)
+    unsigned lo[kMaxRowChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxRowChunks; ++c) {
+        lo[c] = kOutOfRange;
+        const int j = c * 64 + lane;
+        if (j < row_slots) {
+            const int cc = (int)divm((unsigned)j, a.pst_magic);
+            const int v = j - cc * a.pst;
+            const int x = rg.x0 + cc;
+            if (v < a.nvb && (unsigned)x < (unsigned)geo.W)
+                lo[c] = (unsigned)x * cs + goff + 16u * (unsigned)v;
+        }
+    }
+    const __amdgpu_buffer_rsrc_t r = rsrc(a.value, a.value_bytes);
+    const unsigned row_bytes = (unsigned)geo.W * cs;
+    const int row_stride = a.rw * a.pst * 16;
+    for (int rr = wave; rr < rg.rows; rr += nwaves) {
+        const int y = rg.y0 + rr;
+        const unsigned base = (unsigned)y < (unsigned)geo.H ? (unsigned)(t.n * geo.H + y) * row_bytes : kOutOfRange;
+        char *dst = lds + rr * row_stride;
+#pragma unroll
+        for (int c = 0; c < kMaxRowChunks; ++c) {
+            if (c * 64 < row_slots && c * 64 + lane < row_slots)
+                dma<16>(r, dst + c * 64 * 16, (base == kOutOfRange || lo[c] == kOutOfRange) ? kOutOfRange : base + lo[c]);
+        }
+    }
+}
+
+// A block owns a th x tw output tile of one image and gb groups; per pixel,
+// gb x `lanes` threads (groups, then channel chunks, fastest), DP channels
+// each (one lane per group of a 16-bit pixel of 16 channels), so that a
+// wave's loads of offsets and masks and its output stores cover contiguous
+// pixel rows.  The region's value rows are staged in LDS while each lane
+// loads its pixel's offsets and masks into registers; the K samples are unrolled
+// (KMAX >= K) into one straight-line loop: a sample whose 2x2 footprint lies
+// in the region ("near", a test against the block's region bounds) reads its
+// corners from LDS, any other gets zero weights there and, if it is live, a
+// bit in `far`; after the loop the lanes with far samples take them from
+// global memory.  Straight-line code lets the compiler overlap one sample's
+// LDS reads with another's arithmetic.
+#ifndef DCNV4_FWD_PIPE
+#define DCNV4_FWD_PIPE 0
+#endif
+#ifndef DCNV4_FWD_WAVES
+#define DCNV4_FWD_WAVES 4
+#endif
 template <typename T, int DP, int KMAX, bool SM>
-__global__ __launch_bounds__(kMaxTileThreads) void dcnv4_fwd_tiled(TArgs a)
+__global__ __launch_bounds__(kMaxTileThreads) __attribute__((amdgpu_waves_per_eu(KMAX <= 9 ? DCNV4_FWD_WAVES : 1))) void dcnv4_fwd_tiled(TArgs a)
 {
     extern __shared__ u32x4 smem[];
     constexpr int es = (int)sizeof(T);
     constexpr int NV = DP * es / 16;
     const Geom &geo = a.geo;
-    const Tile t = out_tile(a);
+    const Tile t = fwd_tile(a);
+    const Region rg = fwd_region(a, t);
     char *val_s = reinterpret_cast<char *>(smem);
-    stage_values(a, t, val_s, es);
+    stage_region(a, t, rg, val_s, es);
 
-    const int q = threadIdx.x >> a.lanes_shift;
-    const int chunk = threadIdx.x & ((1 << a.lanes_shift) - 1);
+    const int per_pixel_shift = a.lanes_shift + a.gb_shift;
+    const int q = threadIdx.x >> per_pixel_shift;
+    const int r_in = threadIdx.x & ((1 << per_pixel_shift) - 1);
+    const int gl = r_in >> a.lanes_shift;   // group within the block
+    const int chunk = r_in & ((1 << a.lanes_shift) - 1);
+    const int g = t.g + gl;
     const int py = (int)divm((unsigned)q, a.tw_magic);
     const int px = q - py * a.tw;
     const int oy = t.oy0 + py, ox = t.ox0 + px;
     const bool valid = py < a.th && oy < geo.Ho && ox < geo.Wo;
-    OmVectors<T, KMAX> omv;
-    omv.load(rsrc(a.om, a.om_bytes),
-             valid ? (unsigned)((t.n * geo.Ho + oy) * geo.Wo + ox) * (unsigned)(a.P * es) : kOutOfRange, t.g, a.K);
+    // this lane's group slice of the pixel's offsets and masks: aligned
+    // 16-byte vectors from the one holding its first entry; the shift inside
+    // the vectors differs between the groups of a wave, so it is taken with
+    // bit masks, not a branch
+    constexpr int EPV = 16 / es;
+    constexpr int NVO = (2 * KMAX + 2 * (EPV - 1)) / EPV;
+    constexpr int NVM = (KMAX + 2 * (EPV - 1)) / EPV;
+    const int eo = g * 3 * a.K, em = eo + 2 * a.K;
+    const int mis_o = eo & (EPV - 1), mis_m = em & (EPV - 1);
+    u32x4 vov[NVO], vmv[NVM];
+    {
+        const __amdgpu_buffer_rsrc_t omr = rsrc(a.om, a.om_bytes);
+        const unsigned pix = valid ? (unsigned)((t.n * geo.Ho + oy) * geo.Wo + ox) * (unsigned)(a.P * es) : kOutOfRange;
+        const unsigned bo = (unsigned)((eo - mis_o) * es), bm = (unsigned)((em - mis_m) * es);
+#pragma unroll
+        for (int j = 0; j < NVO; ++j)
+            vov[j] = load16(omr, pix == kOutOfRange ? kOutOfRange : pix + bo + 16u * j);
+#pragma unroll
+        for (int j = 0; j < NVM; ++j)
+            vmv[j] = load16(omr, pix == kOutOfRange ? kOutOfRange : pix + bm + 16u * j);
+    }
+    // the grid table, uniform: for up to 9 points loaded once, outside the
+    // sample loop (25 points would crowd the scalar registers; they are
+    // read where used)
+    constexpr int KG = KMAX <= 9 ? KMAX : 1;
+    float gdh_r[KG], gdw_r[KG];
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+        gdh_r[k] = a.gdh[k];
+        gdw_r[k] = a.gdw[k];
+    }
+    auto gdh = [&](int k) { return KMAX <= 9 ? gdh_r[k < KG ? k : 0] : a.gdh[k]; };
+    auto gdw = [&](int k) { return KMAX <= 9 ? gdw_r[k < KG ? k : 0] : a.gdw[k]; };
     staging_done();
     if (!valid)
         return;   // no barrier follows
 
+    // offsets and masks (probabilities in softmax mode: exp(m - sm_max) *
+    // sm_inv) from the loaded vectors
     float offs[2 * KMAX], msk[KMAX];
-    omv.get(offs, msk);
+    entries_of<T>(vov, mis_o, offs);
+    entries_of<T>(vmv, mis_m, msk);
+    float sm_max = 0.0f, sm_inv = 1.0f;
     if (SM) {
-        float mx = msk[0];
+        sm_max = msk[0];
 #pragma unroll
         for (int k = 1; k < KMAX; ++k)
-            mx = k < a.K ? fmaxf(mx, msk[k]) : mx;
+            sm_max = k < a.K ? fmaxf(sm_max, msk[k]) : sm_max;
         float sum = 0.0f;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-            msk[k] = k < a.K ? expf(msk[k] - mx) : 0.0f;
+            msk[k] = k < a.K ? expf(msk[k] - sm_max) : 0.0f;
             sum += msk[k];
         }
-        const float inv = 1.0f / sum;
+        sm_inv = 1.0f / sum;
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-            msk[k] *= inv;
+            msk[k] *= sm_inv;
     }
-    const NearFrame nf = near_frame(a, t, oy, ox);
-    const char *vb = val_s + chunk * NV * 16;
-    const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
-    const int chan_off = (t.g * a.Cg + chunk * DP) * es;
+    const float bh0 = (float)(oy * geo.sh - geo.ph), bw0 = (float)(ox * geo.sw - geo.pw);
+    // footprints (fh, fw) .. (fh + 1, fw + 1) inside the region
+    const float lo_h = (float)rg.y0, hi_h = (float)(rg.y0 + rg.rows - 2);
+    const float lo_w = (float)rg.x0, hi_w = (float)(rg.x0 + rg.cols - 2);
+    const unsigned colb = (unsigned)a.pst * 16u, rowb = (unsigned)a.rw * colb;
+    const unsigned abias = 0u - (unsigned)rg.y0 * rowb - (unsigned)rg.x0 * colb - (1u << 22) * (rowb + colb);
+    // this lane's vectors inside a pixel's slice
+    const char *vb = val_s + (gl * a.nvp + chunk * NV) * 16;
+    const float Hf = (float)geo.H, Wf = (float)geo.W;
 
     float acc[DP];
 #pragma unroll
     for (int c = 0; c < DP; ++c)
         acc[c] = 0.0f;
+    unsigned far = 0;
+    // One sample: its placement (near test, weights with the mask folded
+    // in, LDS address) and the loads of its four corners.  No branch: points
+    // k >= K (KMAX > K) are neither near nor far, and a sample that is not
+    // near reads slot 0 with zero weights.
+    struct Fetched {
+        float w00, w01, w10, w11;
+        u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
+    };
+    auto fetch = [&](int k, Fetched &f) {
+        const bool in_k = k < a.K;
+        const float lh = __builtin_fmaf(geo.scale, offs[2 * k + 1], bh0 + gdh(k));
+        const float lw = __builtin_fmaf(geo.scale, offs[2 * k], bw0 + gdw(k));
+        const float fh = __builtin_floorf(lh), fw = __builtin_floorf(lw);
+        // false for NaN; huge and infinite coordinates fail as well
+        const bool nr = in_k && fh >= lo_h && fh <= hi_h && fw >= lo_w && fw <= hi_w;
+        const bool live = in_k && lh >= -1.0f && lh < Hf && lw >= -1.0f && lw < Wf;
+        far |= (!nr && live) ? (1u << k) : 0u;
+        // floors become integers by bit pattern (defined for every float;
+        // see biased_int)
+        const unsigned addr = __umul24(biased_int(fh), rowb) + __umul24(biased_int(fw), colb) + abias;
+        const unsigned ad = nr ? addr : 0u;
+        const float ah = nr ? lh - fh : 0.0f, aw = nr ? lw - fw : 0.0f;
+        const float mm = nr ? msk[k] : 0.0f;
+        const float mh = __builtin_fmaf(-mm, ah, mm), ml = mm * ah;
+        f.w00 = __builtin_fmaf(-mh, aw, mh);
+        f.w01 = mh * aw;
+        f.w10 = __builtin_fmaf(-ml, aw, ml);
+        f.w11 = ml * aw;
+        const u32x4 *q00 = reinterpret_cast<const u32x4 *>(vb + ad);
+        const u32x4 *q01 = reinterpret_cast<const u32x4 *>(vb + ad + colb);
+        const u32x4 *q10 = reinterpret_cast<const u32x4 *>(vb + ad + rowb);
+        const u32x4 *q11 = reinterpret_cast<const u32x4 *>(vb + ad + rowb + colb);
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        if (k < a.K) {
-            const float m = msk[k];
-            const float bh = nf.bh0 + a.gdh[k], bw = nf.bw0 + a.gdw[k];
-            const NearSample s = near_sample(nf, geo.scale, bh, bw, offs[2 * k], offs[2 * k + 1]);
-            if (!s.nr && live_loc(geo, s.lh, s.lw))
-                far_sample_fwd<T, DP>(geo, vr, t.n, chan_off, s, m, acc);
-            // a sample that is not near gets zero weights (its reads hit slot 0)
-            const float ah = s.nr ? s.lh - s.fh : 0.0f, aw = s.nr ? s.lw - s.fw : 0.0f;
-            const float mm = s.nr ? m : 0.0f;
-            const float mh = __builtin_fmaf(-mm, ah, mm), ml = mm * ah;
-            const float w00 = __builtin_fmaf(-mh, aw, mh), w01 = mh * aw;
-            const float w10 = __builtin_fmaf(-ml, aw, ml), w11 = ml * aw;
-            const u32x4 *q00 = reinterpret_cast<const u32x4 *>(vb + s.addr);
-            const u32x4 *q01 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.colb);
-            const u32x4 *q10 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.rowb);
-            const u32x4 *q11 = reinterpret_cast<const u32x4 *>(vb + s.addr + nf.rowb + nf.colb);
-            u32x4 v00[NV], v01[NV], v10[NV], v11[NV];
+        for (int v = 0; v < NV; ++v) {
+            f.v00[v] = q00[v];
+            f.v01[v] = q01[v];
+            f.v10[v] = q10[v];
+            f.v11[v] = q11[v];
+        }
+    };
+    auto accumulate = [&](const Fetched &f) {
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                v00[v] = q00[v];
-                v01[v] = q01[v];
-                v10[v] = q10[v];
-                v11[v] = q11[v];
-            }
+        for (int c = 0; c < DP; ++c) {
+            float x = acc[c];
+            x = __builtin_fmaf(f.w00, Store<T>::get(f.v00, c), x);
+            x = __builtin_fmaf(f.w01, Store<T>::get(f.v01, c), x);
+            x = __builtin_fmaf(f.w10, Store<T>::get(f.v10, c), x);
+            x = __builtin_fmaf(f.w11, Store<T>::get(f.v11, c), x);
+            acc[c] = x;
+        }
+    };
+    // Keeps the code in program order around it: the accumulators are
+    // complete here (no FMA is deferred past it) and no LDS read moves
+    // across it, so at most the reads of one sample ahead are in flight and
+    // in registers (left alone, the compiler issues every sample's reads
+    // first and runs out of registers).
+    // The inputs of sample `next` pass through it as well, so its placement
+    // is not computed ahead of the fence either.
+    auto fence = [&](int next) {
 #pragma unroll
-            for (int c = 0; c < DP; ++c) {
-                float x = acc[c];
-                x = __builtin_fmaf(w00, Store<T>::get(v00, c), x);
-                x = __builtin_fmaf(w01, Store<T>::get(v01, c), x);
-                x = __builtin_fmaf(w10, Store<T>::get(v10, c), x);
-                x = __builtin_fmaf(w11, Store<T>::get(v11, c), x);
-                acc[c] = x;
-            }
+        for (int c = 0; c < DP; ++c)
+            asm volatile("" : "+v"(acc[c])::"memory");
+        if (next < KMAX)
+            asm volatile("" : "+v"(offs[2 * next]), "+v"(offs[2 * next + 1]), "+v"(msk[next]));
+    };
+    if constexpr (DCNV4_FWD_PIPE == 0) {
+        // one sample at a time
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            Fetched f;
+            fetch(k, f);
+            accumulate(f);
+            fence(k + 1);
+        }
+    } else {
+        // the next sample's corners are read while this one's are summed
+        Fetched f[2];
+        fetch(0, f[0]);
+        fence(1);
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (k + 1 < KMAX)
+                fetch(k + 1, f[(k + 1) & 1]);
+            accumulate(f[k & 1]);
+            fence(k + 2);
+        }
+    }
+    if (far) {
+        // live samples beyond the region: corners from global memory.  A far
+        // sample's offsets and mask are loaded again, one by one (rare; so
+        // the entries need not stay in registers through the main loop, and
+        // no register array is indexed by a run-time k).
+        const __amdgpu_buffer_rsrc_t omr = rsrc(a.om, a.om_bytes);
+        const unsigned row = (unsigned)((t.n * geo.Ho + oy) * geo.Wo + ox) * (unsigned)(a.P * es) +
+                             (unsigned)(g * 3 * a.K * es);
+        auto entry = [&](int idx) -> float {
+            if constexpr (es == 4)
+                return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(omr, row + 4u * (unsigned)idx, 0, 0));
+            else
+                return Store<T>::from_bits(__builtin_amdgcn_raw_buffer_load_b16(omr, row + 2u * (unsigned)idx, 0, 0));
+        };
+        const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, a.value_bytes);
+        const int chan_off = (g * a.Cg + chunk * DP) * es;
+        while (far) {
+            const int k = __builtin_ctz(far);
+            far &= far - 1;
+            const float dx = entry(2 * k), dy = entry(2 * k + 1), m0 = entry(2 * a.K + k);
+            const float m = SM ? expf(m0 - sm_max) * sm_inv : m0;
+            // the grid point from k (a run-time index: no table lookup, which
+            // would copy the table to scratch memory)
+            int gi, gj;
+            grid_point(geo, k, gi, gj);
+            NearSample s;
+            s.lh = __builtin_fmaf(geo.scale, dy, bh0 + (float)(gj * geo.dh));
+            s.lw = __builtin_fmaf(geo.scale, dx, bw0 + (float)(gi * geo.dw));
+            s.fh = __builtin_floorf(s.lh);
+            s.fw = __builtin_floorf(s.lw);
+            far_sample_fwd<T, DP>(geo, vr, t.n, chan_off, s, m, acc);
         }
     }
 
     u32x4 res[NV];
     Store<T>::pack(acc, res, NV);
     u32x4 *dst = reinterpret_cast<u32x4 *>(static_cast<T *>(a.out) +
-                                           ((size_t)(t.n * geo.Ho + oy) * geo.Wo + ox) * geo.C + t.g * a.Cg +
+                                           ((size_t)(t.n * geo.Ho + oy) * geo.Wo + ox) * geo.C + g * a.Cg +
                                            chunk * DP);
 #pragma unroll
     for (int v = 0; v < NV; ++v)
         dst[v] = res[v];
 }
-
 
 }  // namespace
 
@@ -168,9 +394,9 @@ Kernel fwd_kernel(int dtype, int dp, bool small_k, bool sm)
     case DCNV4_FP32:
         return dp == 8 ? fwd_for<float, 8>(small_k, sm) : dp == 4 ? fwd_for<float, 4>(small_k, sm) : nullptr;
     case DCNV4_FP16:
-        return dp == 8 ? fwd_for<_Float16, 8>(small_k, sm) : nullptr;
+        return dp == 16 ? fwd_for<_Float16, 16>(small_k, sm) : dp == 8 ? fwd_for<_Float16, 8>(small_k, sm) : nullptr;
     case DCNV4_BF16:
-        return dp == 8 ? fwd_for<bf16_t, 8>(small_k, sm) : nullptr;
+        return dp == 16 ? fwd_for<bf16_t, 16>(small_k, sm) : dp == 8 ? fwd_for<bf16_t, 8>(small_k, sm) : nullptr;
     default:
         return nullptr;
     }

@@ -12,7 +12,13 @@ using namespace tiled;
 hipError_t launch_forward_tiled(const Problem &p, const TilePlan &tp, const void *value, const void *offset_mask,
                                 void *output, hipStream_t stream)
 {
-    if (!out_tiles_ok(p, tp))
+    // gb groups per block (a power of two dividing G); the region (rh rows
+    // of rw pixels at an odd stride of at least gb * nvp slots, at least
+    // 2 x 2 pixels) fits the block's LDS and one staged row
+    const int gb = tp.gb;
+    if (tp.threads % 64 != 0 || tp.threads > kMaxTileThreads || gb < 1 || (gb & (gb - 1)) != 0 || p.G % gb != 0 ||
+        tp.threads < tp.th * tp.tw * gb * tp.lanes || p.K > 25 || tp.ps != ((gb * tp.nvp) | 1) || tp.rh < 2 ||
+        tp.rw < 2 || tp.ps * tp.rw > 64 * kMaxRowChunks || tp.lds_bytes < tp.rh * tp.rw * tp.ps * 16)
         return hipErrorInvalidConfiguration;
     const Kernel k = fwd_kernel(p.dtype, tp.dp, p.K <= 9, p.softmax != 0);
     if (!k)
@@ -24,7 +30,7 @@ hipError_t launch_forward_tiled(const Problem &p, const TilePlan &tp, const void
     a.value_bytes = p.N * p.H * p.W * p.C * p.elem;
     a.om_bytes = p.N * p.Ho * p.Wo * p.P * p.elem;
     a.out_bytes = p.N * p.Ho * p.Wo * p.C * p.elem;
-    const int blocks = p.N * tp.tiles_y * tp.tiles_x * p.G;
+    const int blocks = p.N * tp.tiles_y * tp.tiles_x * (p.G / gb);
     const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k), (size_t)tp.lds_bytes);
     if (e != hipSuccess)
         return e;
