@@ -49,6 +49,13 @@ int output_size_1d(int in, int k, int s, int p, int d, int *out)
     return DCNV4_OK;
 }
 
+// a * b for non-negative a, b, or INT64_MAX when that overflows
+int64_t mul_sat(int64_t a, int64_t b)
+{
+    int64_t r;
+    return __builtin_mul_overflow(a, b, &r) ? INT64_MAX : r;
+}
+
 // Validate scalar arguments and fill a Problem.  No pointer is looked at.
 int describe(int N, int H, int W, int kh, int kw, int sh, int sw, int ph, int pw, int dh, int dw,
              int group, int group_channels, float offset_scale, int remove_center, int om_channels,
@@ -88,10 +95,11 @@ int describe(int N, int H, int W, int kh, int kw, int sh, int sw, int ph, int pw
         return DCNV4_ERR_PARAM;
     const int es = elem_size(dtype);
     // one image of each tensor must be addressable with 31-bit byte offsets
-    const int64_t img_value = (int64_t)H * W * C * es;
-    const int64_t img_om = (int64_t)Ho * Wo * om_channels * es;
-    const int64_t img_out = (int64_t)Ho * Wo * C * es;
-    const int64_t img_grad_om = (int64_t)Ho * Wo * om_channels * 4;
+    // (products saturate: H * W * C alone can exceed 64 bits)
+    const int64_t img_value = mul_sat(mul_sat(H, W), C * es);
+    const int64_t img_om = mul_sat(mul_sat(Ho, Wo), (int64_t)om_channels * es);
+    const int64_t img_out = mul_sat(mul_sat(Ho, Wo), C * es);
+    const int64_t img_grad_om = mul_sat(mul_sat(Ho, Wo), (int64_t)om_channels * 4);
     if (img_value > kMaxBytesPerLaunch || img_om > kMaxBytesPerLaunch || img_out > kMaxBytesPerLaunch ||
         img_grad_om > kMaxBytesPerLaunch)
         return DCNV4_ERR_OVERFLOW;
@@ -736,7 +744,10 @@ int dcnv4_om_channels(int group, int kernel_h, int kernel_w, int remove_center)
     if (remove_center && (kernel_h % 2 == 0 || kernel_w % 2 == 0 || kernel_h * (int64_t)kernel_w == 1))
         return DCNV4_ERR_PARAM;
     const int64_t K = (int64_t)kernel_h * kernel_w - remove_center;
-    const int64_t P = (3 * group * K + 7) / 8 * 8;
+    const int64_t n = mul_sat(3 * (int64_t)group, K);
+    if (n > INT32_MAX)
+        return DCNV4_ERR_PARAM;
+    const int64_t P = (n + 7) / 8 * 8;
     if (P > INT32_MAX)
         return DCNV4_ERR_PARAM;
     return (int)P;
