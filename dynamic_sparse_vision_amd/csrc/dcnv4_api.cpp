@@ -227,7 +227,11 @@ constexpr int kForwardRmax = DCNV4_FWD_RMAX;   // largest halo of the forward ti
 #ifndef DCNV4_BWD_RMAX
 #define DCNV4_BWD_RMAX 7
 #endif
-constexpr int kBackwardRmax = DCNV4_BWD_RMAX;  // largest halo of the backward tiles (both kernels)
+constexpr int kBackwardRmax = DCNV4_BWD_RMAX;  // near radius of the backward's grad_value cell tiles
+#ifndef DCNV4_BWD_REGION_RMAX
+#define DCNV4_BWD_REGION_RMAX 5
+#endif
+constexpr int kBackwardRegionRmax = DCNV4_BWD_REGION_RMAX;   // largest halo of the grad_offset_mask tiles
 constexpr int kTiledMaxLds = 80 * 1024;
 constexpr int kLdsPerCu = 160 * 1024;
 // A block's LDS is allocated in 1280-byte units: 7-wave forward blocks of
@@ -240,54 +244,6 @@ constexpr int kTileThreads = 512;
 #endif
 constexpr int kCellTileLds = DCNV4_CELL_LDS_KB * 1024;   // two cell-tile blocks per CU
 constexpr int kCellBinBytes = kCellBinSlots * 4 + (kCellThreads / 64) * 4;   // counters, scan scratch
-
-int region_rows(const Problem &p, int th, int R)
-{
-    return (th - 1) * p.sh + (p.kh - 1) * p.dh + 2 * R + 2;
-}
-
-int region_cols(const Problem &p, int tw, int R)
-{
-    return (tw - 1) * p.sw + (p.kw - 1) * p.dw + 2 * R + 2;
-}
-
-// Output tile for halo radius R: th x tw pixels with `lanes` threads per
-// pixel, at most kTileThreads threads, staged value rows and written-back
-// rows (row_elems entries per pixel) within the row limit; the LDS also
-// holds pixel_bytes per tile pixel at the end (0: nothing).
-// Modelled time: per block, a lane-sample costs ~40 instructions plus one
-// FMA per channel and corner, a staged region slot ~8; blocks run
-// concurrently until 24 waves share a CU (fewer when LDS limits them).
-bool choose_out_tile(const Problem &p, int lanes, int dp, int ps, int R, int lds_budget, int row_elems,
-                     int pixel_bytes, int *th, int *tw)
-{
-    double best = -1;
-    for (int w = 1; w <= 64 && w <= p.Wo; ++w) {
-        if (w * row_elems > kRowSlots || region_cols(p, w, R) * ps > kRowSlots)
-            break;
-        for (int h = 1; h <= 64 && h <= p.Ho; ++h) {
-            const int threads = h * w * lanes;
-            if (threads > kTileThreads)
-                break;
-            const int rh = region_rows(p, h, R), rw = region_cols(p, w, R);
-            const int lds = std::max(rh * rw * ps * 16, h * w * pixel_bytes);
-            if (lds > lds_budget)
-                continue;
-            const int waves = (threads + 63) / 64;
-            const int per_cu = std::min(kLdsPerCu / ((lds + kLdsGranule - 1) / kLdsGranule * kLdsGranule), 32 / waves);
-            const double occ = std::min(1.0, per_cu * waves / 24.0);
-            const double blocks = (double)((p.Ho + h - 1) / h) * ((p.Wo + w - 1) / w);
-            const double work = waves * 64.0 * p.K * (40 + 4 * dp) + (double)rh * rw * ps * 8;
-            const double cost = blocks * work / occ;
-            if (best < 0 || cost < best) {
-                best = cost;
-                *th = h;
-                *tw = w;
-            }
-        }
-    }
-    return best >= 0;
-}
 
 // Upper bound of the source window width of a cell tile cw cells wide.
 int window_cols(const Problem &p, int cw, int R)
@@ -372,59 +328,6 @@ bool choose_cell_tile(const Problem &p, int R, int src_cap, int gps, int *ch, in
     return best >= 0;
 }
 
-// Fill the LDS geometry for halo radius R; returns total LDS bytes.
-int tile_lds(const Problem &p, TilePlan *tp, int R, int pixel_bytes)
-{
-    tp->R = R;
-    tp->rh = region_rows(p, tp->th, R);
-    tp->rw = region_cols(p, tp->tw, R);
-    tp->lds_bytes = std::max(tp->rh * tp->rw * tp->ps * 16, tp->th * tp->tw * pixel_bytes);
-    return tp->lds_bytes;
-}
-
-int plan_tiled_common(const Problem &p, int elem, int row_elems, int pixel_bytes, int r_max, int lds_budget, TilePlan *tp)
-{
-    // near-sample addresses take floors below 2^22 in magnitude
-    if ((p.Cg * elem) % 16 != 0 || p.K > kMaxTiledK || p.H > (1 << 21) || p.W > (1 << 21))
-        return DCNV4_ERR_UNSUPPORTED;
-    tp->nvp = p.Cg * elem / 16;
-    if (!pow2(tp->nvp))
-        return DCNV4_ERR_UNSUPPORTED;
-    // an odd pixel stride spreads random pixel reads over the 16-byte banks
-    tp->ps = tp->nvp | 1;
-    // 8 channels per lane: two lanes share a 16-channel pixel, which doubles
-    // the waves that hide LDS latency at little extra per-sample work
-    int dp = 0;
-#ifndef DCNV4_DP_FIRST
-#define DCNV4_DP_FIRST 8
-#endif
-    for (int cand : {DCNV4_DP_FIRST, 8, 4}) {
-        if (p.Cg % cand == 0 && (cand * elem) % 16 == 0) {
-            dp = cand;
-            break;
-        }
-    }
-    if (dp == 0)
-        return DCNV4_ERR_UNSUPPORTED;
-    tp->dp = dp;
-    tp->lanes = p.Cg / dp;
-    if (!pow2(tp->lanes) || tp->lanes > 64)
-        return DCNV4_ERR_UNSUPPORTED;
-    // the largest halo radius that has a tile within the LDS budget
-    for (int R = r_max; R >= 1; --R) {
-        if (!choose_out_tile(p, tp->lanes, dp, tp->ps, R, lds_budget, row_elems, pixel_bytes, &tp->th, &tp->tw))
-            continue;
-        tile_lds(p, tp, R, pixel_bytes);
-        // whole waves: the staging loops take rows per wave
-        tp->threads = (tp->th * tp->tw * tp->lanes + 63) / 64 * 64;
-        tp->tiles_y = (p.Ho + tp->th - 1) / tp->th;
-        tp->tiles_x = (p.Wo + tp->tw - 1) / tp->tw;
-        tp->images_per_launch = 0;
-        return DCNV4_OK;
-    }
-    return DCNV4_ERR_UNSUPPORTED;
-}
-
 // The forward's LDS region of a tile along one axis: the tile's grid span
 // plus a halo of R, clamped to the image plus a one-pixel zero border
 // (-1 .. size); the kernel computes the same bounds (fwd_region).
@@ -451,14 +354,16 @@ void fwd_region_stats(int out, int t, int stride, int pad, int kern, int dil, in
     }
 }
 
-// Forward tiles: th x tw pixels of gb groups, `lanes` threads of dp
+// Output tiles: th x tw pixels of gb groups, `lanes` threads of dp
 // channels per pixel and group, at most kTileThreads threads; the LDS holds
-// the widest clamped region at pst 16-byte slots per pixel.  Modelled time,
-// summed over the tiles of an image: a lane-sample costs ~30 instructions
-// plus one FMA per channel and corner, a staged region slot ~8; blocks run
-// concurrently until `max_waves` share a CU (fewer when the LDS limits them).
-bool choose_fwd_tile(const Problem &p, int lanes, int dp, int gb, int pst, int R, int lds_budget, int max_waves,
-                     int *th, int *tw, int *rh, int *rw)
+// the widest clamped region at pst 16-byte slots per pixel, and at least
+// pixel_bytes per tile pixel (the backward's gradient rows; 0 for the
+// forward).  Modelled time, summed over the tiles of an image: a lane-sample
+// costs ~30 instructions plus one FMA per channel and corner, a staged
+// region slot ~8; blocks run concurrently until `max_waves` share a CU
+// (fewer when the LDS limits them).
+bool choose_tile(const Problem &p, int lanes, int dp, int gb, int pst, int R, int lds_budget, int max_waves,
+                 int pixel_bytes, int *th, int *tw, int *rh, int *rw)
 {
     double best = -1;
     for (int w = 1; w <= 64 && w <= p.Wo; ++w) {
@@ -474,7 +379,7 @@ bool choose_fwd_tile(const Problem &p, int lanes, int dp, int gb, int pst, int R
             int rhm;
             long rhs;
             fwd_region_stats(p.Ho, h, p.sh, p.ph, p.kh, p.dh, R, p.H, &rhm, &rhs);
-            const int lds = rhm * rwm * pst * 16;
+            const int lds = std::max(rhm * rwm * pst * 16, h * w * pixel_bytes);
             if (lds > lds_budget)
                 continue;
             const int waves = (threads + 63) / 64;
@@ -498,9 +403,13 @@ bool choose_fwd_tile(const Problem &p, int lanes, int dp, int gb, int pst, int R
     return best >= 0;
 }
 
-int compute_forward_tiled(const Problem &p, TilePlan *tp)
+// Output tiles of the forward and of the backward's grad_offset_mask
+// kernel: channels per lane, groups per block, halo radius (the largest up
+// to r_max with a tile in the LDS budget) and the tile.  group_row_bytes:
+// LDS per pixel and group beyond the value region (the backward's gradient
+// rows; 0 for the forward).
+int plan_out_tiles(const Problem &p, int r_max, int max_waves, int group_row_bytes, TilePlan *tp)
 {
-    *tp = TilePlan{};
     // near-sample addresses take floors below 2^22 in magnitude
     if ((p.Cg * p.elem) % 16 != 0 || p.K > kMaxTiledK || p.H > (1 << 21) || p.W > (1 << 21))
         return DCNV4_ERR_UNSUPPORTED;
@@ -531,21 +440,29 @@ int compute_forward_tiled(const Problem &p, TilePlan *tp)
         tp->gb *= 2;
     const int nvb = tp->gb * tp->nvp;
     tp->ps = nvb | 1;   // odd LDS pixel stride: random pixel reads spread over the banks
-    const int max_waves = 24;
-    for (int R = kForwardRmax; R >= 1; --R) {
-        if (!choose_fwd_tile(p, tp->lanes, dp, tp->gb, tp->ps, R, kTiledMaxLds, max_waves, &tp->th, &tp->tw, &tp->rh,
-                             &tp->rw))
+    for (int R = r_max; R >= 1; --R) {
+        if (!choose_tile(p, tp->lanes, dp, tp->gb, tp->ps, R, kTiledMaxLds, max_waves, tp->gb * group_row_bytes,
+                         &tp->th, &tp->tw, &tp->rh, &tp->rw))
             continue;
         tp->R = R;
-        tp->lds_bytes = tp->rh * tp->rw * tp->ps * 16;
+        tp->lds_bytes = std::max(tp->rh * tp->rw * tp->ps * 16, tp->th * tp->tw * tp->gb * group_row_bytes);
         // whole waves: the staging loop takes rows per wave
         tp->threads = (tp->th * tp->tw * tp->gb * tp->lanes + 63) / 64 * 64;
         tp->tiles_y = (p.Ho + tp->th - 1) / tp->th;
         tp->tiles_x = (p.Wo + tp->tw - 1) / tp->tw;
-        tp->images_per_launch = (int)(kMaxBytesPerLaunch / image_bytes_max(p, false));
         return DCNV4_OK;
     }
     return DCNV4_ERR_UNSUPPORTED;
+}
+
+int compute_forward_tiled(const Problem &p, TilePlan *tp)
+{
+    *tp = TilePlan{};
+    const int st = plan_out_tiles(p, kForwardRmax, 24, 0, tp);
+    if (st != DCNV4_OK)
+        return st;
+    tp->images_per_launch = (int)(kMaxBytesPerLaunch / image_bytes_max(p, false));
+    return DCNV4_OK;
 }
 
 int compute_backward_tiled(const Problem &p, TilePlan *tp)
@@ -555,22 +472,21 @@ int compute_backward_tiled(const Problem &p, TilePlan *tp)
     const bool cg_ok = p.Cg == 8 || p.Cg == 16 || p.Cg == 32 || (p.Cg == 4 && p.elem == 4);
     if (!cg_ok)
         return DCNV4_ERR_UNSUPPORTED;
-    // offsets and masks go to registers; the gradient write-back stores the
-    // 3K entries of a tile row slot by slot from rows padded to the kernel's
-    // K bound (9 or 25) in whole 16-byte vectors, in the value rows' LDS
-    const int kmax = p.K <= 9 ? 9 : 25;
-    const int pixel_bytes = (3 * kmax * p.elem + 15) / 16 * 16;
-    int st = plan_tiled_common(p, p.elem, 3 * p.K, pixel_bytes, kBackwardRmax, kTiledMaxLds, tp);
+    // grad_offset_mask tiles: as the forward's, with the tile's gradient rows
+    // (3K fp32 per pixel and group) in the same LDS at the end; the kernel
+    // keeps more registers, so fewer waves share a CU
+    int st = plan_out_tiles(p, kBackwardRegionRmax, 16, 3 * p.K * 4, tp);
     if (st != DCNV4_OK)
         return st;
     // cell tiles for grad_value: LDS holds the bins, up to src_cap*K sorted
     // samples of 16 bytes and src_cap staged grad_output pixels
+    tp->Rc = kBackwardRmax;
     tp->gps = (p.Cg * p.elem / 16) | 1;
     tp->rec_offset = kCellBinBytes;
     tp->src_cap = std::min(kCellThreads, (kCellTileLds - kCellBinBytes) / (16 * (p.K + tp->gps)));
     if (tp->src_cap < 1)
         return DCNV4_ERR_UNSUPPORTED;
-    if (!choose_cell_tile(p, tp->R, tp->src_cap, tp->gps, &tp->ch, &tp->cw))
+    if (!choose_cell_tile(p, tp->Rc, tp->src_cap, tp->gps, &tp->ch, &tp->cw))
         return DCNV4_ERR_UNSUPPORTED;
     tp->gs_offset = tp->rec_offset + tp->src_cap * p.K * 16;
     tp->splat_lds_bytes = tp->gs_offset + tp->src_cap * tp->gps * 16;

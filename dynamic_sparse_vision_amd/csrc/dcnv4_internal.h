@@ -49,20 +49,24 @@ constexpr int kCellThreads = DCNV4_CELL_THREADS;
 constexpr int kCellBinSlots = 2048;
 static_assert(4 * kCellThreads >= kCellBinSlots, "scan covers the bins");
 
-// Tiled path.  A sample (output pixel, group, grid point k) is "near" when
-// the integer part of its displacement is within R pixels on both axes:
-// floor(loc) - (integer grid position) in [-R, R].  Every near sample's four
-// corners lie in an LDS region of rh x rw pixels around the block's tile.
+// Tiled path.  An output-tile block stages the value rows its samples can
+// reach within a halo of R pixels of the tile's grid (an LDS region of at
+// most rh x rw pixels); a sample whose footprint lies in the region reads
+// its corners there.  The backward's grad_value cell tiles take the samples
+// whose integer displacement floor(loc) - (integer grid position) is within
+// Rc pixels on both axes; the grad_offset_mask kernel adds the others with
+// device atomics.
 struct TilePlan {
     // output tiles (forward, backward grad_offset_mask): th x tw pixels of
-    // one (image, group); lanes threads of dp channels per pixel
+    // one image and gb groups; lanes threads of dp channels per pixel and group
     int dp, lanes, th, tw, threads;
-    int gb;              // forward: groups per block (their slices of a pixel are contiguous)
+    int gb;              // groups per block (their slices of a pixel are contiguous)
     int tiles_y, tiles_x;
-    int R;
-    int rh, rw;          // LDS value region, pixels
+    int R;               // halo of the LDS value region of an output tile
+    int Rc;              // backward: near radius of the grad_value cell tiles
+    int rh, rw;          // LDS value region, pixels (the largest of any block)
     int nvp;             // 16-byte vectors per region pixel (Cg * elem / 16)
-    int ps;              // LDS pixel stride, 16-byte slots (nvp rounded up to odd)
+    int ps;              // LDS pixel stride, 16-byte slots ((gb * nvp) rounded up to odd)
     int lds_bytes;       // total LDS of an output-tile block (value rows; the backward's
                          // gradient rows reuse it at the end)
     // cell tiles (backward grad_value): ch x cw input cells of one (image, group)

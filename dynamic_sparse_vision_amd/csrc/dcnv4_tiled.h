@@ -16,33 +16,35 @@
 // cost one cache-tag lookup per distinct line and top out near 37 B/clk/CU,
 // while random 128-bit LDS reads reach ~77 B/clk/CU when a pixel's vectors
 // start on an odd 16-byte slot.  So a block owns a 2-D tile of output pixels
-// of one (image, group), stages the group's value rows of the tile plus a
-// halo of R pixels into LDS once (zeros outside the image: the zero-extended
-// image), and gathers corners from LDS.
+// of one image and gb consecutive groups (whose channels of a pixel make one
+// 128-byte line where the channel count allows), stages those channels of
+// the value rows under the tile's sampling grid plus a halo of R pixels into
+// LDS once (zeros outside the image: the zero-extended image), and gathers
+// corners from LDS.
 //
-// A sample is "near" when its integer displacement is within R pixels on
-// both axes (|floor(loc) - grid position| <= R); its four corners then lie in
-// the staged region, so it needs no bounds test at all (corners outside the
-// image read the staged zeros).  Other samples are "far" and read their
-// corners from global memory where they occur; with R = 7 and offsets of a
-// few pixels they are rare.  The R the LDS allows is set by the value rows
-// alone: each lane keeps its pixel's offsets and masks in registers.
+// A sample whose 2x2 footprint lies in the staged region reads its corners
+// there with no bounds test (corners outside the image read the staged
+// zeros); any other live sample reads its corners from global memory after
+// the main loop.  With R up to 5 and offsets of a few pixels these are a
+// small share.  Each lane keeps its pixel's offsets and masks in registers,
+// so the LDS holds value rows only.
 //
 // Staging uses direct-to-LDS buffer loads, one LDS row per group of wave
 // instructions: slot j of every row comes from the row's base plus a
 // per-lane offset that is the same for all rows, so a slot costs one add.
 //
 // Backward: device-scope fp32 atomics on this multi-XCD part are resolved
-// beyond L2 and LDS fp32 atomics are slow, so grad_value of near samples is
-// computed without float atomics: a block owns a tile of *input* cells,
-// evaluates the near samples of the output pixels that can reach it, sorts
-// them by their top-left corner cell (a counting sort with integer LDS
-// atomics), and every thread sums in registers, for a vertical pair of
-// cells, the lists of the corner cells that reach them; the tile is then
-// written with plain stores.
-// grad_offset_mask is forward-shaped; it also adds the contributions of far
-// samples to grad_value with device atomics (a whole-wave instruction per far
-// sample and lane), after the cell-tile kernel has written every cell.
+// beyond L2 and LDS fp32 atomics are slow, so grad_value of the samples
+// within Rc of their grid position (|floor(loc) - grid position| <= Rc on
+// both axes) is computed without float atomics: a block owns a tile of
+// *input* cells, evaluates those samples of the output pixels that can
+// reach it, sorts them by their top-left corner cell (a counting sort with
+// integer LDS atomics), and every thread sums in registers, for a vertical
+// pair of cells, the lists of the corner cells that reach them; the tile is
+// then written with plain stores.  grad_offset_mask is forward-shaped; it
+// also adds the grad_value contributions of the other live samples with
+// device atomics (one wave instruction per sample), after the cell-tile
+// kernel has written every cell.
 
 #pragma once
 
@@ -72,16 +74,17 @@ struct TArgs {
     // grid point k sits at (j*dh, i*dw) from the window origin (as floats,
     // exact small integers): a table instead of a division by kernel_h
     float gdh[kMaxTiledPoints], gdw[kMaxTiledPoints];
-    unsigned k3_magic;           // ceil(2^32 / (3K))
     // output tiles
     int th, tw, tiles_y, tiles_x, lanes_shift;
-    int gb, gb_shift;            // forward: groups per block (a power of two), log2
-    int nvb, pst;                // forward: 16-byte vectors of a block's pixel slice; LDS pixel stride (slots)
+    int gb, gb_shift;            // groups per block (a power of two), log2
+    int nvb, pst;                // 16-byte vectors of a block's pixel slice; LDS pixel stride (slots)
     unsigned pst_magic;
-    int R, rh, rw;               // halo radius; LDS value region, pixels
-    int ps, nvp;                 // LDS pixel stride; data vectors per pixel (16-byte units)
-    unsigned ps_magic;
-    unsigned rw_magic;           // ceil(2^32 / rw)
+    int R, rh, rw;               // halo radius of the LDS value region; its allocated size, pixels
+    int Rc;                      // backward: near radius of the cell-tile kernel (see dcnv4_bwd_offsets_tiled)
+    int cg_shift;                // log2(Cg) (the backward's Cg is a power of two)
+    unsigned run_magic;          // ceil(2^32 / (gb * 3K)): a pixel's gradient run of a block
+    unsigned half_magic;         // ceil(2^32 / (gb * 3K / 2))
+    int nvp;                     // data vectors of a pixel and group (16-byte units)
     unsigned tw_magic;
     unsigned npad_magic;         // ceil(2^32 / (P - 3GK)), padding entries per pixel
     // cell tiles (backward grad_value)
@@ -106,23 +109,6 @@ __device__ __forceinline__ unsigned divm(unsigned e, unsigned magic)
 struct Tile {
     int n, g, oy0, ox0;
 };
-
-// Block -> (image, tile row, tile column, group), group fastest: the groups
-// of one tile read the same offset/mask lines and neighbouring value bytes.
-__device__ __forceinline__ Tile out_tile(const TArgs &a)
-{
-    int b = xcd_tile(blockIdx.x, gridDim.x);
-    Tile t;
-    t.g = b % a.G;
-    b /= a.G;
-    const int tx = b % a.tiles_x;
-    b /= a.tiles_x;
-    const int ty = b % a.tiles_y;
-    t.n = b / a.tiles_y;
-    t.oy0 = ty * a.th;
-    t.ox0 = tx * a.tw;
-    return t;
-}
 
 // ---- staging ----------------------------------------------------------------
 
@@ -169,145 +155,92 @@ __device__ __forceinline__ void staging_done()
     __syncthreads();
 }
 
-// Value rows of group g for the tile plus the halo: region pixel (rr, cc) is
-// image pixel (ry0 + rr, rx0 + cc) and starts at 16-byte slot
-// (rr*rw + cc)*ps; zeros outside the image.
-__device__ __forceinline__ void stage_values(const TArgs &a, const Tile &t, char *val_s, int es)
+// The LDS region of an output-tile block (forward, grad_offset_mask): the
+// value rows and columns its samples can reach within a halo of R pixels of
+// the tile's grid, clamped
+// to the image plus a border of one pixel of zeros (rows -1 .. H, columns
+// -1 .. W): corners beyond that border only belong to samples that are not
+// live.  Region pixel (rr, cc) is image pixel (y0 + rr, x0 + cc).  A block
+// covers gb consecutive groups, whose channels of a pixel are one contiguous
+// slice of nvb 16-byte vectors (128 bytes, a whole cache line, where the
+// channel count allows); the LDS holds the slice of region pixel (rr, cc)
+// from 16-byte slot (rr * rw + cc) * pst, pst = nvb rounded up to odd (an
+// odd pixel stride spreads random pixel reads over the LDS banks), rw being
+// the region width the plan allocates (the widest region of any block).
+struct Region {
+    int y0, x0, rows, cols;
+};
+
+__device__ __forceinline__ Region tile_region(const TArgs &a, const Tile &t)
+{
+    const Geom &g = a.geo;
+    const int y0u = t.oy0 * g.sh - g.ph - a.R, x0u = t.ox0 * g.sw - g.pw - a.R;
+    const int hspan = (a.th - 1) * g.sh + (g.kh - 1) * g.dh + 2 * a.R + 2;
+    const int wspan = (a.tw - 1) * g.sw + (g.kw - 1) * g.dw + 2 * a.R + 2;
+    Region r;
+    r.y0 = max(y0u, -1);
+    r.x0 = max(x0u, -1);
+    r.rows = min(y0u + hspan, g.H + 1) - r.y0;
+    r.cols = min(x0u + wspan, g.W + 1) - r.x0;
+    return r;
+}
+
+// Block -> (image, tile row, tile column, group block), group block
+// fastest; t.g is the block's first group.
+__device__ __forceinline__ Tile block_tile(const TArgs &a)
+{
+    int b = xcd_tile(blockIdx.x, gridDim.x);
+    const int gblocks = a.G >> a.gb_shift;
+    Tile t;
+    t.g = (b % gblocks) << a.gb_shift;
+    b /= gblocks;
+    const int tx = b % a.tiles_x;
+    b /= a.tiles_x;
+    const int ty = b % a.tiles_y;
+    t.n = b / a.tiles_y;
+    t.oy0 = ty * a.th;
+    t.ox0 = tx * a.tw;
+    return t;
+}
+
+// Stage the block's slice of the region's pixels (zeros outside the image)
+// with direct-to-LDS loads: consecutive lanes read consecutive 16-byte
+// vectors of a pixel's slice, so a wave instruction covers whole cache lines.
+// Waves take whole rows.
+__device__ __forceinline__ void stage_region(const TArgs &a, const Tile &t, const Region &rg, char *lds, int es)
 {
     const Geom &geo = a.geo;
-    const int lane = threadIdx.x & 63;
-    {
-        unsigned lo[kMaxRowChunks];
-        const int row_slots = a.rw * a.ps;
-        const int rx0 = t.ox0 * geo.sw - geo.pw - a.R;
-        const unsigned cs = (unsigned)(geo.C * es), goff = (unsigned)(t.g * a.Cg * es);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+    const int row_slots = rg.cols * a.pst;
+    const unsigned cs = (unsigned)(geo.C * es), goff = (unsigned)(t.g * a.Cg * es);
+    // slot j of a row: region column j / pst, vector j % pst (the last of an
+    // even slice is the padding slot, zero)
+    unsigned lo[kMaxRowChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxRowChunks; ++c) {
+        lo[c] = kOutOfRange;
+        const int j = c * 64 + lane;
+        if (j < row_slots) {
+            const int cc = (int)divm((unsigned)j, a.pst_magic);
+            const int v = j - cc * a.pst;
+            const int x = rg.x0 + cc;
+            if (v < a.nvb && (unsigned)x < (unsigned)geo.W)
+                lo[c] = (unsigned)x * cs + goff + 16u * (unsigned)v;
+        }
+    }
+    const __amdgpu_buffer_rsrc_t r = rsrc(a.value, a.value_bytes);
+    const unsigned row_bytes = (unsigned)geo.W * cs;
+    const int row_stride = a.rw * a.pst * 16;
+    for (int rr = wave; rr < rg.rows; rr += nwaves) {
+        const int y = rg.y0 + rr;
+        const unsigned base = (unsigned)y < (unsigned)geo.H ? (unsigned)(t.n * geo.H + y) * row_bytes : kOutOfRange;
+        char *dst = lds + rr * row_stride;
 #pragma unroll
         for (int c = 0; c < kMaxRowChunks; ++c) {
-            lo[c] = kOutOfRange;
-            if (c * 64 < row_slots) {
-                const int j = c * 64 + lane;
-                const int cc = (int)divm((unsigned)j, a.ps_magic);
-                const int v = j - cc * a.ps;
-                const int x = rx0 + cc;
-                if (v < a.nvp && cc < a.rw && (unsigned)x < (unsigned)geo.W)
-                    lo[c] = (unsigned)x * cs + goff + 16u * (unsigned)v;
-            }
+            if (c * 64 < row_slots && c * 64 + lane < row_slots)
+                dma<16>(r, dst + c * 64 * 16, (base == kOutOfRange || lo[c] == kOutOfRange) ? kOutOfRange : base + lo[c]);
         }
-        const int ry0 = t.oy0 * geo.sh - geo.ph - a.R;
-        const unsigned row_bytes = (unsigned)geo.W * cs;
-        stage_rows<16>(rsrc(a.value, a.value_bytes), val_s, a.rh, row_slots, lo, [&](int rr) {
-            const int y = ry0 + rr;
-            return (unsigned)y < (unsigned)geo.H ? (unsigned)(t.n * geo.H + y) * row_bytes : kOutOfRange;
-        });
     }
-}
-
-// ---- offsets and masks in registers ------------------------------------------
-//
-// A pixel's group slice of offset_mask starts at the same element offset in
-// every pixel row, so its misalignment inside a 16-byte vector (mis) is the
-// same for the whole block.  A lane loads the aligned vectors that cover the
-// slice, and the shift is a register renaming chosen once per block (a
-// switch on mis) rather than per-lane arithmetic.
-
-template <typename T, int NVEC, int NOUT, int MIS>
-__device__ __forceinline__ void take_entries(const u32x4 (&v)[NVEC], float (&out)[NOUT])
-{
-    constexpr int EPV = 16 / (int)sizeof(T);
-    static_assert(MIS + NOUT <= EPV * NVEC, "vectors too short");
-    // keeps the cases of entries_at apart: merged, they would become one
-    // dynamically indexed array in scratch memory
-    asm volatile("; entries shifted by %0" ::"n"(MIS));
-    unsigned w[4 * NVEC];
-#pragma unroll
-    for (int i = 0; i < NVEC; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            w[4 * i + e] = v[i][e];
-#pragma unroll
-    for (int e = 0; e < NOUT; ++e) {
-        const int idx = e + MIS;
-        if constexpr (sizeof(T) == 4)
-            out[e] = __builtin_bit_cast(float, w[idx]);
-        else
-            out[e] = Store<T>::from_bits((idx & 1) ? w[idx >> 1] >> 16 : w[idx >> 1]);
-    }
-}
-
-template <typename T, int NVEC, int NOUT>
-__device__ __forceinline__ void entries_at(const u32x4 (&v)[NVEC], int mis, float (&out)[NOUT])
-{
-    switch (mis) {
-    case 0: take_entries<T, NVEC, NOUT, 0>(v, out); break;
-    case 1: take_entries<T, NVEC, NOUT, 1>(v, out); break;
-    case 2: take_entries<T, NVEC, NOUT, 2>(v, out); break;
-    case 3: take_entries<T, NVEC, NOUT, 3>(v, out); break;
-    default:
-        if constexpr (sizeof(T) == 2) {
-            switch (mis) {
-            case 4: take_entries<T, NVEC, NOUT, 4>(v, out); break;
-            case 5: take_entries<T, NVEC, NOUT, 5>(v, out); break;
-            case 6: take_entries<T, NVEC, NOUT, 6>(v, out); break;
-            default: take_entries<T, NVEC, NOUT, 7>(v, out); break;
-            }
-        }
-        break;
-    }
-}
-
-// Vectors covering a pixel's 2K offsets and K masks (group g, entries from
-// element g*3K of the pixel's row).
-template <typename T, int KMAX>
-struct OmVectors {
-    static constexpr int EPV = 16 / (int)sizeof(T);
-    static constexpr int NVO = (2 * KMAX + 2 * (EPV - 1)) / EPV;
-    static constexpr int NVM = (KMAX + 2 * (EPV - 1)) / EPV;
-    u32x4 o[NVO], m[NVM];
-    int mis_o, mis_m;
-
-    // pix: byte offset of the pixel's row, or kOutOfRange (zeros)
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, unsigned pix, int g, int K)
-    {
-        const int eo = g * 3 * K, em = eo + 2 * K;
-        mis_o = eo & (EPV - 1);
-        mis_m = em & (EPV - 1);
-        const unsigned bo = (unsigned)((eo - mis_o) * (int)sizeof(T)), bm = (unsigned)((em - mis_m) * (int)sizeof(T));
-#pragma unroll
-        for (int j = 0; j < NVO; ++j)
-            o[j] = load16(r, pix == kOutOfRange ? kOutOfRange : pix + bo + 16u * j);
-#pragma unroll
-        for (int j = 0; j < NVM; ++j)
-            m[j] = load16(r, pix == kOutOfRange ? kOutOfRange : pix + bm + 16u * j);
-    }
-
-    __device__ __forceinline__ void get(float (&offs)[2 * KMAX], float (&msk)[KMAX]) const
-    {
-        entries_at<T>(o, mis_o, offs);
-        entries_at<T>(m, mis_m, msk);
-    }
-};
-
-// Per-pixel constants of the near test and of LDS corner addresses.
-struct NearFrame {
-    float bh0, bw0;   // integer base of grid point (0, 0), as floats
-    float Rf;
-    int rowb, colb;   // LDS bytes per region row / pixel
-    unsigned abias;   // LDS byte address of image pixel (0, 0) relative to the
-                      // region, less 2^22 * (rowb + colb) (see biased_int)
-};
-
-__device__ __forceinline__ NearFrame near_frame(const TArgs &a, const Tile &t, int oy, int ox)
-{
-    const Geom &geo = a.geo;
-    NearFrame f;
-    f.bh0 = (float)(oy * geo.sh - geo.ph);
-    f.bw0 = (float)(ox * geo.sw - geo.pw);
-    f.Rf = (float)a.R;
-    f.colb = a.ps * 16;
-    f.rowb = a.rw * f.colb;
-    const int ry0 = t.oy0 * geo.sh - geo.ph - a.R, rx0 = t.ox0 * geo.sw - geo.pw - a.R;
-    f.abias = 0u - (unsigned)(ry0 * f.rowb + rx0 * f.colb) - (1u << 22) * (unsigned)(f.rowb + f.colb);
-    return f;
 }
 
 // An integer-valued float x with |x| < 2^22 as 2^22 + x in the low 24 bits
@@ -318,40 +251,10 @@ __device__ __forceinline__ unsigned biased_int(float x)
     return __builtin_bit_cast(unsigned, x + 12582912.0f);
 }
 
-// One sample in the main loops: location, floor, near test (false for NaN),
-// and the LDS byte address of the top-left corner when near (of the grid
-// position otherwise).
-struct NearSample {
+// A sample's location and its floor.
+struct SampleLoc {
     float lh, lw, fh, fw;
-    bool nr;
-    int addr;
 };
-
-__device__ __forceinline__ NearSample near_sample(const NearFrame &f, float scale, float bh, float bw, float dx,
-                                                  float dy)
-{
-    NearSample s;
-    s.lh = __builtin_fmaf(scale, dy, bh);
-    s.lw = __builtin_fmaf(scale, dx, bw);
-    s.fh = __builtin_floorf(s.lh);
-    s.fw = __builtin_floorf(s.lw);
-    // fh - bh and fw - bw are differences of integers below 2^24 (or huge)
-    s.nr = __builtin_fabsf(s.fh - bh) <= f.Rf && __builtin_fabsf(s.fw - bw) <= f.Rf;
-    // Floors are turned into integers by bit pattern (biased_int), which is
-    // defined for any float: huge, infinite and NaN coordinates give some
-    // address that the select then discards.  Near floors are below 2^22 in
-    // magnitude (the tiled planner takes maps of at most 2^21 pixels a
-    // side), so the biased addresses are exact modulo 2^32.
-    const unsigned addr = __umul24(biased_int(s.fh), (unsigned)f.rowb) + __umul24(biased_int(s.fw), (unsigned)f.colb) +
-                          f.abias;
-    s.addr = s.nr ? (int)addr : 0;
-    return s;
-}
-
-__device__ __forceinline__ bool live_loc(const Geom &g, float lh, float lw)
-{
-    return lh >= -1.0f && lh < (float)g.H && lw >= -1.0f && lw < (float)g.W;
-}
 
 // Corners of a far sample from global memory: loads only (the caller uses
 // the registers later, so the loads overlap other work).
@@ -536,7 +439,6 @@ inline TArgs make_targs(const Problem &p, const TilePlan &tp)
     a.Cg = p.Cg;
     a.K = p.K;
     a.P = p.P;
-    a.k3_magic = magic_for(3 * p.K);
     a.th = tp.th;
     a.tw = tp.tw;
     a.tiles_y = tp.tiles_y;
@@ -545,12 +447,13 @@ inline TArgs make_targs(const Problem &p, const TilePlan &tp)
     a.R = tp.R;
     a.rh = tp.rh;
     a.rw = tp.rw;
-    a.ps = tp.ps;
     a.nvp = tp.nvp;
-    a.ps_magic = magic_for(tp.ps);
-    a.rw_magic = magic_for(tp.rw);
     a.gb = tp.gb > 0 ? tp.gb : 1;
     a.gb_shift = log2i(a.gb);
+    a.Rc = tp.Rc;
+    a.cg_shift = log2i(p.Cg);
+    a.run_magic = magic_for(a.gb * 3 * p.K);
+    a.half_magic = magic_for(a.gb * 3 * p.K / 2);
     a.nvb = a.gb * tp.nvp;
     a.pst = a.nvb | 1;
     a.pst_magic = magic_for(a.pst);
@@ -575,14 +478,6 @@ inline TArgs make_targs(const Problem &p, const TilePlan &tp)
     a.gs_offset = tp.gs_offset;
     return a;
 }
-
-// Shapes every tiled launch relies on (the planner only produces these).
-inline bool out_tiles_ok(const Problem &p, const TilePlan &tp)
-{
-    return tp.threads % 64 == 0 && tp.threads <= kMaxTileThreads && tp.threads >= tp.th * tp.tw * tp.lanes &&
-           tp.rw * tp.ps <= 64 * kMaxRowChunks && p.K <= 25 && tp.ps >= tp.nvp;
-}
-
 
 typedef void (*Kernel)(TArgs);
 

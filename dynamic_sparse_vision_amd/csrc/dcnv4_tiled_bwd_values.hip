@@ -36,12 +36,12 @@ __global__ __launch_bounds__(kCellThreads) __attribute__((amdgpu_waves_per_eu(KM
     const int cy0 = cty * a.ch, cx0 = ctx * a.cw;
 
     // output pixels whose near samples can touch rows [cy0, cy0+ch): a near
-    // sample's top row h0 lies in [bh - R, bh + R] with bh = oy*sh - ph + j*dh,
+    // sample's top row h0 lies in [bh - Rc, bh + Rc] with bh = oy*sh - ph + j*dh,
     // and touching needs h0 in [cy0 - 1, cy0 + ch - 1]
-    const int sy0 = max(0, ceil_div(cy0 - 1 - a.R + geo.ph - (geo.kh - 1) * geo.dh, geo.sh));
-    const int sy1 = min(geo.Ho, floor_div(cy0 + a.ch - 1 + a.R + geo.ph, geo.sh) + 1);
-    const int sx0 = max(0, ceil_div(cx0 - 1 - a.R + geo.pw - (geo.kw - 1) * geo.dw, geo.sw));
-    const int sx1 = min(geo.Wo, floor_div(cx0 + a.cw - 1 + a.R + geo.pw, geo.sw) + 1);
+    const int sy0 = max(0, ceil_div(cy0 - 1 - a.Rc + geo.ph - (geo.kh - 1) * geo.dh, geo.sh));
+    const int sy1 = min(geo.Ho, floor_div(cy0 + a.ch - 1 + a.Rc + geo.ph, geo.sh) + 1);
+    const int sx0 = max(0, ceil_div(cx0 - 1 - a.Rc + geo.pw - (geo.kw - 1) * geo.dw, geo.sw));
+    const int sx1 = min(geo.Wo, floor_div(cx0 + a.cw - 1 + a.Rc + geo.pw, geo.sw) + 1);
     const int SW = sx1 - sx0;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kCellThreads) __attribute__((amdgpu_waves_per_eu(KM
     const int eo = g * 3 * a.K, em = eo + 2 * a.K;
     const int mis_o = eo & (EPV - 1), mis_m = em & (EPV - 1);
     const unsigned vo = (unsigned)((eo - mis_o) * es), vm = (unsigned)((em - mis_m) * es);
-    const float Rf = (float)a.R, chf = (float)a.ch, cwf = (float)a.cw;
+    const float Rf = (float)a.Rc, chf = (float)a.ch, cwf = (float)a.cw;
     const float ylo = (float)(cy0 - 1), xlo = (float)(cx0 - 1);
     // LDS byte offset of this thread's source in the staged grad_out
     const unsigned my_gs = (unsigned)a.gs_offset + (unsigned)tid * (unsigned)(a.gps * 16);

@@ -13,7 +13,7 @@ namespace {
 // the image weighted 0 (the buffer range check zero-fills reads past the end).
 template <typename T, int DP>
 __device__ __forceinline__ void far_sample_fwd(const Geom &geo, __amdgpu_buffer_rsrc_t vr, int n, int chan_off,
-                                               const NearSample &s, float m, float (&acc)[DP])
+                                               const SampleLoc &s, float m, float (&acc)[DP])
 {
     constexpr int es = (int)sizeof(T);
     constexpr int NV = DP * es / 16;
@@ -42,93 +42,6 @@ __device__ __forceinline__ void far_sample_fwd(const Geom &geo, __amdgpu_buffer_
     }
 }
 
-// The LDS region of a forward block: the value rows and columns its
-// samples can reach within a halo of R pixels of the tile's grid, clamped
-// to the image plus a border of one pixel of zeros (rows -1 .. H, columns
-// -1 .. W): corners beyond that border only belong to samples that are not
-// live.  Region pixel (rr, cc) is image pixel (y0 + rr, x0 + cc).  A block
-// covers gb consecutive groups, whose channels of a pixel are one contiguous
-// slice of nvb 16-byte vectors (128 bytes, a whole cache line, where the
-// channel count allows); the LDS holds the slice of region pixel (rr, cc)
-// from 16-byte slot (rr * rw + cc) * pst, pst = nvb rounded up to odd (an
-// odd pixel stride spreads random pixel reads over the LDS banks), rw being
-// the region width the plan allocates (the widest region of any block).
-struct Region {
-    int y0, x0, rows, cols;
-};
-
-__device__ __forceinline__ Region fwd_region(const TArgs &a, const Tile &t)
-{
-    const Geom &g = a.geo;
-    const int y0u = t.oy0 * g.sh - g.ph - a.R, x0u = t.ox0 * g.sw - g.pw - a.R;
-    const int hspan = (a.th - 1) * g.sh + (g.kh - 1) * g.dh + 2 * a.R + 2;
-    const int wspan = (a.tw - 1) * g.sw + (g.kw - 1) * g.dw + 2 * a.R + 2;
-    Region r;
-    r.y0 = max(y0u, -1);
-    r.x0 = max(x0u, -1);
-    r.rows = min(y0u + hspan, g.H + 1) - r.y0;
-    r.cols = min(x0u + wspan, g.W + 1) - r.x0;
-    return r;
-}
-
-// Block -> (image, tile row, tile column, group block), group block
-// fastest; t.g is the block's first group.
-__device__ __forceinline__ Tile fwd_tile(const TArgs &a)
-{
-    int b = xcd_tile(blockIdx.x, gridDim.x);
-    const int gblocks = a.G >> a.gb_shift;
-    Tile t;
-    t.g = (b % gblocks) << a.gb_shift;
-    b /= gblocks;
-    const int tx = b % a.tiles_x;
-    b /= a.tiles_x;
-    const int ty = b % a.tiles_y;
-    t.n = b / a.tiles_y;
-    t.oy0 = ty * a.th;
-    t.ox0 = tx * a.tw;
-    return t;
-}
-
-// Stage the block's slice of the region's pixels (zeros outside the image)
-// with direct-to-LDS loads: consecutive lanes read consecutive 16-byte
-// vectors of a pixel's slice, so a wave instruction covers whole cache lines.
-// Waves take whole rows.
-__device__ __forceinline__ void stage_region(const TArgs &a, const Tile &t, const Region &rg, char *lds, int es)
-{
-    const Geom &geo = a.geo;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-    const int row_slots = rg.cols * a.pst;
-    const unsigned cs = (unsigned)(geo.C * es), goff = (unsigned)(t.g * a.Cg * es);
-    // slot j of a row: region column j / pst, vector j % pst (the last of an
-    // even slice is the padding slot, zero)
-    unsigned lo[kMaxRowChunks];
-#pragma unroll
-    for (int c = 0; c < kMaxRowChunks; ++c) {
-        lo[c] = kOutOfRange;
-        const int j = c * 64 + lane;
-        if (j < row_slots) {
-            const int cc = (int)divm((unsigned)j, a.pst_magic);
-            const int v = j - cc * a.pst;
-            const int x = rg.x0 + cc;
-            if (v < a.nvb && (unsigned)x < (unsigned)geo.W)
-                lo[c] = (unsigned)x * cs + goff + 16u * (unsigned)v;
-        }
-    }
-    const __amdgpu_buffer_rsrc_t r = rsrc(a.value, a.value_bytes);
-    const unsigned row_bytes = (unsigned)geo.W * cs;
-    const int row_stride = a.rw * a.pst * 16;
-    for (int rr = wave; rr < rg.rows; rr += nwaves) {
-        const int y = rg.y0 + rr;
-        const unsigned base = (unsigned)y < (unsigned)geo.H ? (unsigned)(t.n * geo.H + y) * row_bytes : kOutOfRange;
-        char *dst = lds + rr * row_stride;
-#pragma unroll
-        for (int c = 0; c < kMaxRowChunks; ++c) {
-            if (c * 64 < row_slots && c * 64 + lane < row_slots)
-                dma<16>(r, dst + c * 64 * 16, (base == kOutOfRange || lo[c] == kOutOfRange) ? kOutOfRange : base + lo[c]);
-        }
-    }
-}
-
 // A block owns a th x tw output tile of one image and gb groups; per pixel,
 // gb x `lanes` threads (groups, then channel chunks, fastest), DP channels
 // each (one lane per group of a 16-bit pixel of 16 channels), so that a
@@ -154,8 +67,8 @@ __global__ __launch_bounds__(kMaxTileThreads) __attribute__((amdgpu_waves_per_eu
     constexpr int es = (int)sizeof(T);
     constexpr int NV = DP * es / 16;
     const Geom &geo = a.geo;
-    const Tile t = fwd_tile(a);
-    const Region rg = fwd_region(a, t);
+    const Tile t = block_tile(a);
+    const Region rg = tile_region(a, t);
     char *val_s = reinterpret_cast<char *>(smem);
     stage_region(a, t, rg, val_s, es);
 
@@ -355,7 +268,7 @@ __global__ __launch_bounds__(kMaxTileThreads) __attribute__((amdgpu_waves_per_eu
             // would copy the table to scratch memory)
             int gi, gj;
             grid_point(geo, k, gi, gj);
-            NearSample s;
+            SampleLoc s;
             s.lh = __builtin_fmaf(geo.scale, dy, bh0 + (float)(gj * geo.dh));
             s.lw = __builtin_fmaf(geo.scale, dx, bw0 + (float)(gi * geo.dw));
             s.fh = __builtin_floorf(s.lh);
