@@ -228,8 +228,12 @@ constexpr int kForwardRmax = DCNV4_FWD_RMAX;   // largest halo of the forward ti
 #define DCNV4_BWD_RMAX 7
 #endif
 constexpr int kBackwardRmax = DCNV4_BWD_RMAX;  // near radius of the backward's grad_value cell tiles
+#ifndef DCNV4_BWD_RMAX_LARGE
+#define DCNV4_BWD_RMAX_LARGE 11
+#endif
+constexpr int kBackwardRmaxLarge = DCNV4_BWD_RMAX_LARGE;   // ... on large maps
 #ifndef DCNV4_BWD_REGION_RMAX
-#define DCNV4_BWD_REGION_RMAX 5
+#define DCNV4_BWD_REGION_RMAX 4
 #endif
 constexpr int kBackwardRegionRmax = DCNV4_BWD_REGION_RMAX;   // largest halo of the grad_offset_mask tiles
 constexpr int kTiledMaxLds = 80 * 1024;
@@ -480,14 +484,22 @@ int compute_backward_tiled(const Problem &p, TilePlan *tp)
         return st;
     // cell tiles for grad_value: LDS holds the bins, up to src_cap*K sorted
     // samples of 16 bytes and src_cap staged grad_output pixels
-    tp->Rc = kBackwardRmax;
     tp->gps = (p.Cg * p.elem / 16) | 1;
     tp->rec_offset = kCellBinBytes;
     tp->src_cap = std::min(kCellThreads, (kCellTileLds - kCellBinBytes) / (16 * (p.K + tp->gps)));
     if (tp->src_cap < 1)
         return DCNV4_ERR_UNSUPPORTED;
-    if (!choose_cell_tile(p, tp->Rc, tp->src_cap, tp->gps, &tp->ch, &tp->cw))
-        return DCNV4_ERR_UNSUPPORTED;
+    // The near radius of the cell tiles.  A sample beyond it costs the
+    // grad_offset_mask kernel a device atomic per channel and corner; one
+    // within it costs every cell tile whose source window holds its pixel,
+    // and the windows grow with the radius.  Offsets in pixels grow with the
+    // map, so the radius does too: 7 up to 95 pixels on the shorter side,
+    // then one more per 32 pixels, up to 11 from 192 pixels.
+    const int side = std::min(p.H, p.W);
+    tp->Rc = std::min(kBackwardRmaxLarge, kBackwardRmax + std::max(0, (side - 64) / 32));
+    while (!choose_cell_tile(p, tp->Rc, tp->src_cap, tp->gps, &tp->ch, &tp->cw))
+        if (--tp->Rc < 1)
+            return DCNV4_ERR_UNSUPPORTED;
     tp->gs_offset = tp->rec_offset + tp->src_cap * p.K * 16;
     tp->splat_lds_bytes = tp->gs_offset + tp->src_cap * tp->gps * 16;
     tp->ctiles_y = (p.H + tp->ch - 1) / tp->ch;

@@ -5,7 +5,7 @@ kernel (1, 3, 5 or 7 per axis), stride, padding, dilation, remove_center,
 offset_scale, offset spread, storage dtype and the DCNv3 softmax mode from
 one seeded generator, so the tile planner meets shapes that the named cases
 do not: rectangular and 1-wide kernels, ragged tiles along both axes, maps
-from 1 to 96 pixels a side, offsets far beyond the halo, and shapes the
+from 1 to 200 pixels a side, offsets far beyond the halo, and shapes the
 tiled kernels decline (channel rows that are not a power of two of 16-byte
 vectors, more than 25 points), which go to the general kernels.  Forward
 and backward wherever the library takes the call; where it declines (the
@@ -72,6 +72,9 @@ CASES = _draw_cases(160)
 # maps of 25 to 96 pixels a side: several output and cell tiles per image,
 # ragged along both axes
 CASES += _draw_cases(32, seed=2025, size=(25, 97), batch=(1, 3), prefix="big")
+# maps of 128 to 200 pixels a side: the backward's cell tiles take a near
+# radius of 9 to 11 there (7 below), with offsets far beyond it
+CASES += _draw_cases(6, seed=2027, size=(128, 201), batch=(1, 2), prefix="wide")
 # shapes the tiled kernels decline (channel rows that are not a power of two
 # of 16-byte vectors, more than 25 points): the general kernels
 CASES += _draw_cases(48, seed=2026, size=(1, 30), batch=(1, 3), prefix="gen", general=True)
