@@ -224,6 +224,10 @@ constexpr int kMaxTiledK = 25;        // grid points of the tiled kernels
 #define DCNV4_FWD_RMAX 5
 #endif
 constexpr int kForwardRmax = DCNV4_FWD_RMAX;   // largest halo of the forward tiles
+#ifndef DCNV4_FWD_RMAX_LARGE
+#define DCNV4_FWD_RMAX_LARGE 7
+#endif
+constexpr int kForwardRmaxLarge = DCNV4_FWD_RMAX_LARGE;   // ... on large maps
 #ifndef DCNV4_BWD_RMAX
 #define DCNV4_BWD_RMAX 7
 #endif
@@ -236,6 +240,14 @@ constexpr int kBackwardRmaxLarge = DCNV4_BWD_RMAX_LARGE;   // ... on large maps
 #define DCNV4_BWD_REGION_RMAX 4
 #endif
 constexpr int kBackwardRegionRmax = DCNV4_BWD_REGION_RMAX;   // largest halo of the grad_offset_mask tiles
+#ifndef DCNV4_BWD_REGION_RMAX_LARGE
+#define DCNV4_BWD_REGION_RMAX_LARGE 4
+#endif
+#ifndef DCNV4_BWD_SLICE_LARGE
+#define DCNV4_BWD_SLICE_LARGE 128
+#endif
+constexpr int kBackwardRegionRmaxLarge = DCNV4_BWD_REGION_RMAX_LARGE;   // ... on large maps
+constexpr int kBackwardSliceLarge = DCNV4_BWD_SLICE_LARGE;   // pixel slice bytes of its blocks there
 constexpr int kTiledMaxLds = 80 * 1024;
 constexpr int kLdsPerCu = 160 * 1024;
 // A block's LDS is allocated in 1280-byte units: 7-wave forward blocks of
@@ -408,11 +420,11 @@ bool choose_tile(const Problem &p, int lanes, int dp, int gb, int pst, int R, in
 }
 
 // Output tiles of the forward and of the backward's grad_offset_mask
-// kernel: channels per lane, groups per block, halo radius (the largest up
-// to r_max with a tile in the LDS budget) and the tile.  group_row_bytes:
-// LDS per pixel and group beyond the value region (the backward's gradient
-// rows; 0 for the forward).
-int plan_out_tiles(const Problem &p, int r_max, int max_waves, int group_row_bytes, TilePlan *tp)
+// kernel: channels per lane, groups per block (pixel slices of at most
+// slice_bytes), halo radius (the largest up to r_max with a tile in the LDS
+// budget) and the tile.  group_row_bytes: LDS per pixel and group beyond the
+// value region (the backward's gradient rows; 0 for the forward).
+int plan_out_tiles(const Problem &p, int r_max, int max_waves, int group_row_bytes, int slice_bytes, TilePlan *tp)
 {
     // near-sample addresses take floors below 2^22 in magnitude
     if ((p.Cg * p.elem) % 16 != 0 || p.K > kMaxTiledK || p.H > (1 << 21) || p.W > (1 << 21))
@@ -437,10 +449,10 @@ int plan_out_tiles(const Problem &p, int r_max, int max_waves, int group_row_byt
     if (!pow2(tp->lanes) || tp->lanes > 64)
         return DCNV4_ERR_UNSUPPORTED;
     // groups per block: the largest power of two dividing G whose slices of
-    // a pixel make at most one 128-byte line, so that staging, offset/mask
-    // loads and output stores cover whole lines
+    // a pixel make at most slice_bytes (128: one whole cache line, so that
+    // staging, offset/mask loads and output stores cover whole lines)
     tp->gb = 1;
-    while (p.G % (2 * tp->gb) == 0 && 2 * tp->gb * tp->nvp * 16 <= 128)
+    while (p.G % (2 * tp->gb) == 0 && 2 * tp->gb * tp->nvp * 16 <= slice_bytes)
         tp->gb *= 2;
     const int nvb = tp->gb * tp->nvp;
     tp->ps = nvb | 1;   // odd LDS pixel stride: random pixel reads spread over the banks
@@ -459,10 +471,22 @@ int plan_out_tiles(const Problem &p, int r_max, int max_waves, int group_row_byt
     return DCNV4_ERR_UNSUPPORTED;
 }
 
+// Large maps: at least this many pixels on the shorter side.  Offsets in
+// pixels grow with the map, so there the output tiles take a wider halo with
+// narrower pixel slices (at 128 bytes a halo of 7 leaves tiles too small),
+// and the cell tiles a larger near radius.
+constexpr int kLargeMapSide = 192;
+
+bool large_map(const Problem &p)
+{
+    return std::min(p.H, p.W) >= kLargeMapSide;
+}
+
 int compute_forward_tiled(const Problem &p, TilePlan *tp)
 {
     *tp = TilePlan{};
-    const int st = plan_out_tiles(p, kForwardRmax, 24, 0, tp);
+    const bool large = large_map(p);
+    const int st = plan_out_tiles(p, large ? kForwardRmaxLarge : kForwardRmax, 24, 0, large ? 64 : 128, tp);
     if (st != DCNV4_OK)
         return st;
     tp->images_per_launch = (int)(kMaxBytesPerLaunch / image_bytes_max(p, false));
@@ -479,7 +503,9 @@ int compute_backward_tiled(const Problem &p, TilePlan *tp)
     // grad_offset_mask tiles: as the forward's, with the tile's gradient rows
     // (3K fp32 per pixel and group) in the same LDS at the end; the kernel
     // keeps more registers, so fewer waves share a CU
-    int st = plan_out_tiles(p, kBackwardRegionRmax, 16, 3 * p.K * 4, tp);
+    const bool large = large_map(p);
+    int st = plan_out_tiles(p, large ? kBackwardRegionRmaxLarge : kBackwardRegionRmax, 16, 3 * p.K * 4,
+                            large ? kBackwardSliceLarge : 128, tp);
     if (st != DCNV4_OK)
         return st;
     // cell tiles for grad_value: LDS holds the bins, up to src_cap*K sorted
