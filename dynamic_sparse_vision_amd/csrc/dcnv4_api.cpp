@@ -248,7 +248,10 @@ constexpr int kBackwardRegionRmax = DCNV4_BWD_REGION_RMAX;   // largest halo of 
 #endif
 constexpr int kBackwardRegionRmaxLarge = DCNV4_BWD_REGION_RMAX_LARGE;   // ... on large maps
 constexpr int kBackwardSliceLarge = DCNV4_BWD_SLICE_LARGE;   // pixel slice bytes of its blocks there
-constexpr int kTiledMaxLds = 80 * 1024;
+#ifndef DCNV4_TILED_LDS_KB
+#define DCNV4_TILED_LDS_KB 80
+#endif
+constexpr int kTiledMaxLds = DCNV4_TILED_LDS_KB * 1024;
 constexpr int kLdsPerCu = 160 * 1024;
 // A block's LDS is allocated in 1280-byte units: 7-wave forward blocks of
 // 54000 bytes averaged 10.5 resident waves per CU (two blocks fit, not three),
