@@ -1,5 +1,5 @@
 // Internal interface between the C-ABI layer (dcnv4_api.cpp) and the HIP
-// kernels (dcnv4_kernels.hip: general path; dcnv4_tiled.hip: LDS-tiled
+// kernels (dcnv4_kernels.hip: general path; dcnv4_tiled_*.hip: LDS-tiled
 // path).  Not installed; not part of the ABI.
 #pragma once
 

@@ -13,7 +13,7 @@
 // offset/mask rows are staged in LDS (blog "DCNv4架构解析", section
 // "并行计算架构设计"), corners are 128-bit raw buffer loads whose range check
 // returns 0 outside the tensor, and grad_value is summed with device atomics.
-// The tiled kernels (dcnv4_tiled.hip) are used where their LDS budget fits.
+// The tiled kernels (dcnv4_tiled_*.hip) are used where their LDS budget fits.
 
 #include "dcnv4_device.h"
 #include "dcnv4_internal.h"
