@@ -273,6 +273,18 @@ __device__ __forceinline__ float unit_sum(float x, int lanes)
     return x;
 }
 
+// Maximum over the `lanes` lanes of a unit (aligned groups, a power of two).
+__device__ __forceinline__ float unit_max(float x, int lanes)
+{
+    if (lanes >= 2)
+        x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)));
+    if (lanes >= 4)
+        x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)));
+    for (int d = 4; d < lanes; d <<= 1)
+        x = fmaxf(x, __shfl_xor(x, d));
+    return x;
+}
+
 // ---- forward --------------------------------------------------------------
 
 template <typename T, int U>
@@ -443,7 +455,8 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd_loc(Args a)
     f32x4 *rec_lds = lds4;                                                            // [upb * LK] (ST)
     unsigned *key_lds = reinterpret_cast<unsigned *>(lds + (ST ? upb * LK * 16 : 0));  // [upb * LK] (ST)
     float *ga_lds = reinterpret_cast<float *>(lds + (ST ? upb * LK * 20 : 0));        // [upb * LK]
-    T *grow_lds = reinterpret_cast<T *>(lds + upb * LK * (ST ? 24 : 4));              // [upb * P] (ST)
+    float *att_lds = ga_lds + upb * LK;                                               // [upb * LK]
+    T *grow_lds = reinterpret_cast<T *>(lds + upb * LK * (ST ? 28 : 8));              // [upb * P] (ST)
     const int blk = xcd_tile(blockIdx.x, gridDim.x);
     const int lu = (int)threadIdx.x / U;
     const int lane = (int)threadIdx.x % U;
@@ -457,8 +470,29 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd_loc(Args a)
     const T *row = static_cast<const T *>(a.loc_attn) + qrow * a.P;
     T *grow = ST ? grow_lds + lu * a.P : static_cast<T *>(a.grad_loc) + qrow * a.P;
     float *ga = ga_lds + lu * LK;
-    float mx, inv;
-    softmax_stats(row + 2 * LK, LK, mx, inv);
+    // the attention weights: a softmax over the unit's LK logits, each lane
+    // taking every U-th one, into LDS, where the sample loop and the logit
+    // gradients read them (the unit's lanes are one wave: its LDS accesses
+    // are performed in order, the fences only keep the compiler's order)
+    float *att_s = att_lds + lu * LK;
+    {
+        float mx = -__builtin_huge_valf();
+        for (int j = lane; j < LK; j += U)
+            mx = fmaxf(mx, ld1(row + 2 * LK + j));
+        mx = unit_max(mx, U);
+        float sum = 0.0f;
+        for (int j = lane; j < LK; j += U) {
+            const float e = expf(ld1(row + 2 * LK + j) - mx);
+            att_s[j] = e;
+            sum += e;
+        }
+        const float inv = 1.0f / unit_sum(sum, U);
+        for (int j = lane; j < LK; j += U)
+            att_s[j] *= inv;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
     float g[8];
     {
         const u32x4 *gp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.grad_out) + qrow * a.D + lane * 8);
@@ -482,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd_loc(Args a)
             const float x = __builtin_fmaf(u, Wf, -0.5f);
             const float y = __builtin_fmaf(v, Hf, -0.5f);
             const bool in = live(y, x, Hf, Wf);
-            const float att = expf(ld1(row + 2 * LK + i) - mx) * inv;
+            const float att = att_s[i];
             // a dead sample (huge or NaN location included) is placed at
             // (-1, -1): only bounded floors are converted to integers
             const Corners c = corners(in ? y : -1.0f, in ? x : -1.0f, H, W, start, a.pix_bytes, base);
@@ -491,18 +525,24 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd_loc(Args a)
             load8<T>(vr, in ? c.o[1] : kOutOfRange, v1);
             load8<T>(vr, in ? c.o[2] : kOutOfRange, v2);
             load8<T>(vr, in ? c.o[3] : kOutOfRange, v3);
-            float gs = 0.0f, gx = 0.0f, gy = 0.0f;
+            // grad_output dotted with each corner's channels, summed over
+            // the unit's lanes; the sample's value and its derivatives along
+            // x and y are linear in the corners, so their products with
+            // grad_output follow from these four sums
+            float t0 = 0.0f, t1 = 0.0f, t2 = 0.0f, t3 = 0.0f;
             for (int e = 0; e < 8; ++e) {
-                const float sm = c.w[0] * v0[e] + c.w[1] * v1[e] + c.w[2] * v2[e] + c.w[3] * v3[e];
-                const float dxv = c.hy * (v1[e] - v0[e]) + c.ly * (v3[e] - v2[e]);
-                const float dyv = c.hx * (v2[e] - v0[e]) + c.lx * (v3[e] - v1[e]);
-                gs = __builtin_fmaf(g[e], sm, gs);
-                gx = __builtin_fmaf(g[e], dxv, gx);
-                gy = __builtin_fmaf(g[e], dyv, gy);
+                t0 = __builtin_fmaf(g[e], v0[e], t0);
+                t1 = __builtin_fmaf(g[e], v1[e], t1);
+                t2 = __builtin_fmaf(g[e], v2[e], t2);
+                t3 = __builtin_fmaf(g[e], v3[e], t3);
             }
-            gs = unit_sum(in ? gs : 0.0f, U);
-            gx = unit_sum(in ? gx : 0.0f, U);
-            gy = unit_sum(in ? gy : 0.0f, U);
+            t0 = unit_sum(t0, U);
+            t1 = unit_sum(t1, U);
+            t2 = unit_sum(t2, U);
+            t3 = unit_sum(t3, U);
+            const float gs = in ? c.w[0] * t0 + c.w[1] * t1 + c.w[2] * t2 + c.w[3] * t3 : 0.0f;
+            const float gx = in ? c.hy * (t1 - t0) + c.ly * (t3 - t2) : 0.0f;
+            const float gy = in ? c.hx * (t2 - t0) + c.lx * (t3 - t1) : 0.0f;
             dot += att * gs;
             if (lane == (i & (U - 1))) {
                 st2(grow + 2 * i, att * Wf * gx, att * Hf * gy);
@@ -526,10 +566,8 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd_loc(Args a)
         }
     }
     // logits: a_i (g_i - sum_j a_j g_j); lane i % U wrote ga[i] itself
-    for (int j = lane; j < LK; j += U) {
-        const float att = expf(ld1(row + 2 * LK + j) - mx) * inv;
-        grow[2 * LK + j] = Store<T>::make(att * (ga[j] - dot));
-    }
+    for (int j = lane; j < LK; j += U)
+        grow[2 * LK + j] = Store<T>::make(att_s[j] * (ga[j] - dot));
     for (int e = 3 * LK + lane; e < a.P; e += U)
         grow[e] = Store<T>::make(0.0f);
     }
@@ -854,7 +892,7 @@ hipError_t launch_bwd_loc_t(const Args &a, hipStream_t stream)
 {
     const int upb = kThreads / (a.D / 8);
     const int blocks = (a.units + upb - 1) / upb;
-    const size_t ga = (size_t)upb * a.LK * sizeof(float);
+    const size_t ga = 2 * (size_t)upb * a.LK * sizeof(float);   // lane sums and attention weights
     const size_t staged = ga + (size_t)upb * a.LK * (sizeof(unsigned) + sizeof(f32x4)) +
                           (size_t)upb * a.P * (a.elem_bytes);
     if (staged <= 64 * 1024)
