@@ -285,11 +285,39 @@ __device__ __forceinline__ float unit_max(float x, int lanes)
     return x;
 }
 
+// The attention weights of a unit: a softmax over its n logits, each of the
+// unit's `lanes` lanes taking every lanes-th one, written to att_s; a weight
+// is exp(z - mx) * inv.  The unit's lanes are one wave: its LDS accesses are
+// performed in order, and the fences only keep the compiler's order, so
+// every lane may read any weight afterwards.
+template <typename T>
+__device__ __forceinline__ void unit_softmax(const T *logits, int n, int lane, int lanes, float *att_s, float &mx,
+                                             float &inv)
+{
+    mx = -__builtin_huge_valf();
+    for (int j = lane; j < n; j += lanes)
+        mx = fmaxf(mx, ld1(logits + j));
+    mx = unit_max(mx, lanes);
+    float sum = 0.0f;
+    for (int j = lane; j < n; j += lanes) {
+        const float e = expf(ld1(logits + j) - mx);
+        att_s[j] = e;
+        sum += e;
+    }
+    inv = 1.0f / unit_sum(sum, lanes);
+    for (int j = lane; j < n; j += lanes)
+        att_s[j] *= inv;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---- forward --------------------------------------------------------------
 
 template <typename T, int U>
 __global__ __launch_bounds__(kThreads) void fdattn_fwd(Args a)
 {
+    extern __shared__ float att_lds[];   // [units per block][LK]: attention weights
     constexpr int es = (int)sizeof(T);
     constexpr int upb = kThreads / U;
     const int blk = xcd_tile(blockIdx.x, gridDim.x);
@@ -303,8 +331,9 @@ __global__ __launch_bounds__(kThreads) void fdattn_fwd(Args a)
     const size_t qrow = ((size_t)n * a.Q + (unit - nm * a.Q)) * a.M + m;   // (n, q, m) row
     const int LK = a.LK;
     const T *row = static_cast<const T *>(a.loc_attn) + qrow * a.P;
+    float *att_s = att_lds + ((int)threadIdx.x / U) * LK;
     float mx, inv;
-    softmax_stats(row + 2 * LK, LK, mx, inv);
+    unit_softmax(row + 2 * LK, LK, lane, U, att_s, mx, inv);
 
     const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, (int)a.value_bytes);
     const unsigned base = (unsigned)n * a.img_bytes + (unsigned)((m * a.D + lane * 8) * es);
@@ -326,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void fdattn_fwd(Args a)
             const float x = __builtin_fmaf(u, Wf, -0.5f);
             const float y = __builtin_fmaf(v, Hf, -0.5f);
             const bool in = live(y, x, Hf, Wf);
-            const float att = expf(ld1(row + 2 * LK + i) - mx) * inv;
+            const float att = att_s[i];
             // a dead sample (huge or NaN location included) is placed at
             // (-1, -1): only bounded floors are converted to integers
             Corners c = corners(in ? y : -1.0f, in ? x : -1.0f, H, W, start, a.pix_bytes, base);
@@ -455,8 +484,7 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd_loc(Args a)
     f32x4 *rec_lds = lds4;                                                            // [upb * LK] (ST)
     unsigned *key_lds = reinterpret_cast<unsigned *>(lds + (ST ? upb * LK * 16 : 0));  // [upb * LK] (ST)
     float *ga_lds = reinterpret_cast<float *>(lds + (ST ? upb * LK * 20 : 0));        // [upb * LK]
-    float *att_lds = ga_lds + upb * LK;                                               // [upb * LK]
-    T *grow_lds = reinterpret_cast<T *>(lds + upb * LK * (ST ? 28 : 8));              // [upb * P] (ST)
+    T *grow_lds = reinterpret_cast<T *>(lds + upb * LK * (ST ? 24 : 4));              // [upb * P] (ST)
     const int blk = xcd_tile(blockIdx.x, gridDim.x);
     const int lu = (int)threadIdx.x / U;
     const int lane = (int)threadIdx.x % U;
@@ -470,29 +498,11 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd_loc(Args a)
     const T *row = static_cast<const T *>(a.loc_attn) + qrow * a.P;
     T *grow = ST ? grow_lds + lu * a.P : static_cast<T *>(a.grad_loc) + qrow * a.P;
     float *ga = ga_lds + lu * LK;
-    // the attention weights: a softmax over the unit's LK logits, each lane
-    // taking every U-th one, into LDS, where the sample loop and the logit
-    // gradients read them (the unit's lanes are one wave: its LDS accesses
-    // are performed in order, the fences only keep the compiler's order)
-    float *att_s = att_lds + lu * LK;
-    {
-        float mx = -__builtin_huge_valf();
-        for (int j = lane; j < LK; j += U)
-            mx = fmaxf(mx, ld1(row + 2 * LK + j));
-        mx = unit_max(mx, U);
-        float sum = 0.0f;
-        for (int j = lane; j < LK; j += U) {
-            const float e = expf(ld1(row + 2 * LK + j) - mx);
-            att_s[j] = e;
-            sum += e;
-        }
-        const float inv = 1.0f / unit_sum(sum, U);
-        for (int j = lane; j < LK; j += U)
-            att_s[j] *= inv;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
+    // the attention weights, in the slots of the lane sums: sample i's
+    // weight is read by every lane of the unit before one lane overwrites it
+    // with the sample's sum (in program order, and the lanes are one wave)
+    float mx, inv;
+    unit_softmax(row + 2 * LK, LK, lane, U, ga, mx, inv);
     float g[8];
     {
         const u32x4 *gp = reinterpret_cast<const u32x4 *>(static_cast<const T *>(a.grad_out) + qrow * a.D + lane * 8);
@@ -516,7 +526,7 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd_loc(Args a)
             const float x = __builtin_fmaf(u, Wf, -0.5f);
             const float y = __builtin_fmaf(v, Hf, -0.5f);
             const bool in = live(y, x, Hf, Wf);
-            const float att = att_s[i];
+            const float att = ga[i];
             // a dead sample (huge or NaN location included) is placed at
             // (-1, -1): only bounded floors are converted to integers
             const Corners c = corners(in ? y : -1.0f, in ? x : -1.0f, H, W, start, a.pix_bytes, base);
@@ -566,8 +576,10 @@ __global__ __launch_bounds__(kThreads) void fdattn_bwd_loc(Args a)
         }
     }
     // logits: a_i (g_i - sum_j a_j g_j); lane i % U wrote ga[i] itself
-    for (int j = lane; j < LK; j += U)
-        grow[2 * LK + j] = Store<T>::make(att_s[j] * (ga[j] - dot));
+    for (int j = lane; j < LK; j += U) {
+        const float att = expf(ld1(row + 2 * LK + j) - mx) * inv;
+        grow[2 * LK + j] = Store<T>::make(att * (ga[j] - dot));
+    }
     for (int e = 3 * LK + lane; e < a.P; e += U)
         grow[e] = Store<T>::make(0.0f);
     }
@@ -863,27 +875,38 @@ hipError_t launch_fwd_t(const Args &a, hipStream_t stream)
     const int U = a.D / 8;
     const int upb = kThreads / U;
     const int blocks = (a.units + upb - 1) / upb;
+    const size_t lds = (size_t)upb * a.LK * sizeof(float);   // attention weights
+    void (*fn)(Args) = nullptr;
     switch (U) {
-    case 1: hipLaunchKernelGGL((fdattn_fwd<T, 1>), dim3(blocks), dim3(kThreads), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((fdattn_fwd<T, 2>), dim3(blocks), dim3(kThreads), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((fdattn_fwd<T, 4>), dim3(blocks), dim3(kThreads), 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((fdattn_fwd<T, 8>), dim3(blocks), dim3(kThreads), 0, stream, a); break;
-    case 16: hipLaunchKernelGGL((fdattn_fwd<T, 16>), dim3(blocks), dim3(kThreads), 0, stream, a); break;
+    case 1: fn = fdattn_fwd<T, 1>; break;
+    case 2: fn = fdattn_fwd<T, 2>; break;
+    case 4: fn = fdattn_fwd<T, 4>; break;
+    case 8: fn = fdattn_fwd<T, 8>; break;
+    case 16: fn = fdattn_fwd<T, 16>; break;
     default: return hipErrorInvalidValue;
     }
+    const hipError_t e = dcnv4::allow_dynamic_lds(reinterpret_cast<const void *>(fn), lds);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(fn, dim3(blocks), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
 }
 
 template <typename T, bool ST>
 hipError_t launch_bwd_loc_st(const Args &a, int blocks, size_t lds, hipStream_t stream)
 {
+    void (*fn)(Args) = nullptr;
     switch (a.D / 8) {
-    case 1: hipLaunchKernelGGL((fdattn_bwd_loc<T, 1, ST>), dim3(blocks), dim3(kThreads), lds, stream, a); break;
-    case 2: hipLaunchKernelGGL((fdattn_bwd_loc<T, 2, ST>), dim3(blocks), dim3(kThreads), lds, stream, a); break;
-    case 4: hipLaunchKernelGGL((fdattn_bwd_loc<T, 4, ST>), dim3(blocks), dim3(kThreads), lds, stream, a); break;
-    case 8: hipLaunchKernelGGL((fdattn_bwd_loc<T, 8, ST>), dim3(blocks), dim3(kThreads), lds, stream, a); break;
+    case 1: fn = fdattn_bwd_loc<T, 1, ST>; break;
+    case 2: fn = fdattn_bwd_loc<T, 2, ST>; break;
+    case 4: fn = fdattn_bwd_loc<T, 4, ST>; break;
+    case 8: fn = fdattn_bwd_loc<T, 8, ST>; break;
     default: return hipErrorInvalidValue;
     }
+    const hipError_t e = dcnv4::allow_dynamic_lds(reinterpret_cast<const void *>(fn), lds);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(fn, dim3(blocks), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -892,7 +915,7 @@ hipError_t launch_bwd_loc_t(const Args &a, hipStream_t stream)
 {
     const int upb = kThreads / (a.D / 8);
     const int blocks = (a.units + upb - 1) / upb;
-    const size_t ga = 2 * (size_t)upb * a.LK * sizeof(float);   // lane sums and attention weights
+    const size_t ga = (size_t)upb * a.LK * sizeof(float);   // attention weights, then lane sums
     const size_t staged = ga + (size_t)upb * a.LK * (sizeof(unsigned) + sizeof(f32x4)) +
                           (size_t)upb * a.P * (a.elem_bytes);
     if (staged <= 64 * 1024)

@@ -115,6 +115,9 @@ CASES = [
     _w("l1k1_fp32", shapes=((11, 13),), K=1, Q=40),
     # the largest point count: 16 levels x 8 points
     _w("l16k8_fp32", shapes=tuple((2 + l % 3, 3 + l % 4) for l in range(16)), K=8, M=2, Q=9),
+    # the same with one lane per query (D = 8): 256 queries per block, whose
+    # attention weights and lane sums take 128 KB of LDS
+    _w("l16k8_d8_fp32", shapes=tuple((2 + l % 3, 3 + l % 4) for l in range(16)), K=8, M=1, D=8, Q=300),
     # encoder queries over four levels
     FDA_WORKLOADS["fda_small_fp32"],
     # 16-bit storage
@@ -130,7 +133,7 @@ def test_parity(w):
     run_case(w)
 
 
-ATOMIC_CASES = [c for c in CASES if c.name in ("d32_fp32", "spread_fp32", "l16k8_fp32", "d16_bf16")]
+ATOMIC_CASES = [c for c in CASES if c.name in ("d32_fp32", "spread_fp32", "l16k8_fp32", "l16k8_d8_fp32", "d16_bf16")]
 
 
 @pytest.mark.parametrize("w", ATOMIC_CASES, ids=[c.name for c in ATOMIC_CASES])
