@@ -17,6 +17,9 @@
 //   * Forward: D/8 lanes per unit, 8 channels per lane (the D' channels per
 //     thread and 128-bit loads of the walkthrough "DCNv4论文解析", section
 //     2.2); a corner is one (fp16/bf16) or two (fp32) 128-bit buffer loads.
+//     The softmax is taken once per unit, its lanes sharing the logits, into
+//     LDS; the unit's lanes then place one sample each and broadcast its
+//     corner offsets and weights to the others.
 //   * Backward, with a caller workspace (the sorted path): the location and
 //     logit gradients in the forward's mapping (lane sums by DPP), which
 //     also emits each live sample's bin -- the cell of its top-left corner
@@ -44,6 +47,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 
 namespace fdattn {
 namespace {
@@ -312,6 +316,34 @@ __device__ __forceinline__ void unit_softmax(const T *logits, int n, int lane, i
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Lane R's value of x in every lane of its aligned group of U lanes.  Groups
+// of two and four lanes use a DPP quad permutation, wider ones a
+// permute through the LDS crossbar.
+template <int U, int R>
+__device__ __forceinline__ unsigned group_bcast(unsigned x)
+{
+    if constexpr (U == 1) {
+        return x;
+    } else if constexpr (U == 2) {
+        return (unsigned)__builtin_amdgcn_mov_dpp((int)x, R | R << 2 | (2 + R) << 4 | (2 + R) << 6, 0xF, 0xF, false);
+    } else if constexpr (U == 4) {
+        return (unsigned)__builtin_amdgcn_mov_dpp((int)x, R * 0x55, 0xF, 0xF, false);
+    } else {
+        const int src = (int)(__lane_id() & ~(unsigned)(U - 1)) | R;
+        return (unsigned)__builtin_amdgcn_ds_bpermute(src << 2, (int)x);
+    }
+}
+
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), in order.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
 // ---- forward --------------------------------------------------------------
 
 template <typename T, int U>
@@ -336,43 +368,59 @@ __global__ __launch_bounds__(kThreads) void fdattn_fwd(Args a)
     unit_softmax(row + 2 * LK, LK, lane, U, att_s, mx, inv);
 
     const __amdgpu_buffer_rsrc_t vr = rsrc(a.value, (int)a.value_bytes);
-    const unsigned base = (unsigned)n * a.img_bytes + (unsigned)((m * a.D + lane * 8) * es);
+    // corner offsets are the unit's (its image and head); each lane adds its
+    // channels' offset to them
+    const unsigned base = (unsigned)n * a.img_bytes + (unsigned)(m * a.D * es);
+    const unsigned chan = (unsigned)(lane * 8 * es);
     float acc[8];
     for (int c = 0; c < 8; ++c)
         acc[c] = 0.0f;
-    // The sample loop has no branch: a sample outside its map gets zero
-    // weights and out-of-range offsets, so the compiler can overlap the
-    // loads of several samples.
+    // The U lanes of a unit take U samples at a time: each lane places one
+    // (location, bilinear weights times the attention weight, corner
+    // offsets), then the group reads the four corners of each of the U
+    // samples in turn, its offsets and weights broadcast from the lane that
+    // placed it.  No branch: a sample outside its map, or past the level's
+    // last point, gets zero weights and out-of-range offsets (whose loads
+    // return zeros), so the compiler can overlap the loads of the samples.
     for (int l = 0; l < a.L; ++l) {
         const int H = a.lvl_h[l], W = a.lvl_w[l], start = a.lvl_start[l];
         const float Hf = (float)H, Wf = (float)W;
         const int i0 = l * a.K;
-#pragma unroll 4
-        for (int k = 0; k < a.K; ++k) {
-            const int i = i0 + k;
+        for (int kb = 0; kb < a.K; kb += U) {
+            const bool have = kb + lane < a.K;
+            const int i = i0 + (have ? kb + lane : a.K - 1);
             float u, v;
             ld2(row + 2 * i, u, v);
             const float x = __builtin_fmaf(u, Wf, -0.5f);
             const float y = __builtin_fmaf(v, Hf, -0.5f);
-            const bool in = live(y, x, Hf, Wf);
+            const bool in = have && live(y, x, Hf, Wf);
             const float att = att_s[i];
             // a dead sample (huge or NaN location included) is placed at
             // (-1, -1): only bounded floors are converted to integers
-            Corners c = corners(in ? y : -1.0f, in ? x : -1.0f, H, W, start, a.pix_bytes, base);
-            float v0[8], v1[8], v2[8], v3[8];
-            load8<T>(vr, in ? c.o[0] : kOutOfRange, v0);
-            load8<T>(vr, in ? c.o[1] : kOutOfRange, v1);
-            load8<T>(vr, in ? c.o[2] : kOutOfRange, v2);
-            load8<T>(vr, in ? c.o[3] : kOutOfRange, v3);
-            const float a0 = in ? att * c.w[0] : 0.0f, a1 = in ? att * c.w[1] : 0.0f;
-            const float a2 = in ? att * c.w[2] : 0.0f, a3 = in ? att * c.w[3] : 0.0f;
-            for (int e = 0; e < 8; ++e) {
-                float s = acc[e];
-                s = __builtin_fmaf(a0, v0[e], s);
-                s = __builtin_fmaf(a1, v1[e], s);
-                s = __builtin_fmaf(a2, v2[e], s);
-                acc[e] = __builtin_fmaf(a3, v3[e], s);
+            const Corners c = corners(in ? y : -1.0f, in ? x : -1.0f, H, W, start, a.pix_bytes, base);
+            unsigned o[4], w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                o[q] = in ? c.o[q] : kOutOfRange;
+                w[q] = __builtin_bit_cast(unsigned, in ? att * c.w[q] : 0.0f);
             }
+            static_for<U>([&](auto r) {
+                constexpr int R = decltype(r)::value;
+                float vq[4][8], wq[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    // kOutOfRange plus a channel offset stays out of range
+                    load8<T>(vr, group_bcast<U, R>(o[q]) + chan, vq[q]);
+                    wq[q] = __builtin_bit_cast(float, group_bcast<U, R>(w[q]));
+                }
+                for (int e = 0; e < 8; ++e) {
+                    float s = acc[e];
+                    s = __builtin_fmaf(wq[0], vq[0][e], s);
+                    s = __builtin_fmaf(wq[1], vq[1][e], s);
+                    s = __builtin_fmaf(wq[2], vq[2][e], s);
+                    acc[e] = __builtin_fmaf(wq[3], vq[3][e], s);
+                }
+            });
         }
     }
     T *out = static_cast<T *>(a.out) + qrow * a.D + lane * 8;
