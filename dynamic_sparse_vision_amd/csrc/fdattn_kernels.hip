@@ -801,14 +801,18 @@ __global__ __launch_bounds__(kThreads) void fdattn_gather(Args a)
         return;
     f32x2 *stage = stage_lds + lu * UL;
     const int slice = unit / a.S;
-    const int s = unit - slice * a.S;
     const int n = slice / a.M;
     const int m = slice - n * a.M;
-    int l = 0;
-    while (l + 1 < a.L && s >= a.lvl_start[l + 1])
-        ++l;
+    // the cells of a slice are taken from the coarsest level to the finest:
+    // the coarse cells' long lists start early instead of ending the launch
+    int rc = unit - slice * a.S;
+    int l = a.L - 1;
+    while (l > 0 && rc >= a.lvl_h[l] * a.lvl_w[l]) {
+        rc -= a.lvl_h[l] * a.lvl_w[l];
+        --l;
+    }
     const int W = a.lvl_w[l];
-    const int rc = s - a.lvl_start[l];
+    const int s = a.lvl_start[l] + rc;
     const int r = rc / W, c = rc - r * W;
     const size_t bin_lc = (size_t)slice * a.nbs + a.lvl_bin[l] + (size_t)(r + 1) * (W + 1) + c;   // bin (r, c-1)
     const size_t bin_ulc = bin_lc - (W + 1);                                                         // bin (r-1, c-1)
