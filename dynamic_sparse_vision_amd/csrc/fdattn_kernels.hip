@@ -63,6 +63,7 @@ using dcnv4::dev::xcd_tile;
 
 constexpr unsigned kOutOfRange = 0x80000000u;   // beyond any launch's buffer
 constexpr int kSortThreads = 1024;               // one block per (image, head) slice
+constexpr int kSortUnroll = 4;                   // samples per thread and round of the count and place loops
 constexpr size_t kSortLdsMax = 150 * 1024;       // bin counters of one slice, LDS bytes
 #ifndef FDATTN_GATHER_CHANNELS
 #define FDATTN_GATHER_CHANNELS 4
@@ -702,10 +703,19 @@ __global__ __launch_bounds__(kSortThreads) void fdattn_count(Args a)
     __syncthreads();
     size_t s0, s1;
     sort_range(a, slice, sbi, s0, s1);
-    for (size_t si = s0 + tid; si < s1; si += kSortThreads) {
-        const unsigned b = a.keys[si];
-        if (b != ~0u)
-            __hip_atomic_fetch_add(bins + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // kSortUnroll keys per thread are loaded before their counts are added,
+    // so the loads' latency is paid once per kSortUnroll rounds
+    for (size_t si0 = s0 + tid; si0 < s1; si0 += kSortUnroll * kSortThreads) {
+        unsigned b[kSortUnroll];
+#pragma unroll
+        for (int u = 0; u < kSortUnroll; ++u) {
+            const size_t si = si0 + (size_t)u * kSortThreads;
+            b[u] = si < s1 ? a.keys[si] : ~0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kSortUnroll; ++u)
+            if (b[u] != ~0u)
+                __hip_atomic_fetch_add(bins + b[u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     __syncthreads();
     unsigned *gcount = a.counts + (size_t)slice * a.nbs;
@@ -767,11 +777,28 @@ __global__ __launch_bounds__(kSortThreads) void fdattn_place(Args a)
     __syncthreads();
     size_t s0, s1;
     sort_range(a, slice, sbi, s0, s1);
-    for (size_t si = s0 + tid; si < s1; si += kSortThreads) {
-        const unsigned b = a.keys[si];
-        if (b != ~0u) {
-            const unsigned idx = __hip_atomic_fetch_add(cursor + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            a.recs[idx] = a.urecs[si];
+    // kSortUnroll samples per thread: keys and records are loaded before
+    // their places are taken
+    for (size_t si0 = s0 + tid; si0 < s1; si0 += kSortUnroll * kSortThreads) {
+        unsigned b[kSortUnroll];
+        f32x4 r[kSortUnroll];
+#pragma unroll
+        for (int u = 0; u < kSortUnroll; ++u) {
+            const size_t si = si0 + (size_t)u * kSortThreads;
+            b[u] = ~0u;
+            r[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (si < s1) {
+                b[u] = a.keys[si];
+                r[u] = a.urecs[si];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kSortUnroll; ++u) {
+            if (b[u] != ~0u) {
+                const unsigned idx =
+                    __hip_atomic_fetch_add(cursor + b[u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                a.recs[idx] = r[u];
+            }
         }
     }
 }
