@@ -63,8 +63,11 @@ using dcnv4::dev::xcd_tile;
 
 constexpr unsigned kOutOfRange = 0x80000000u;   // beyond any launch's buffer
 constexpr int kSortThreads = 1024;               // one block per (image, head) slice
-constexpr int kSortUnroll = 4;                   // samples per thread and round of the count and place loops
 constexpr size_t kSortLdsMax = 150 * 1024;       // bin counters of one slice, LDS bytes
+constexpr int kSortUnroll = 4;                   // samples per thread and round of the count and place loops
+// rounds of the scan (four bins per thread each) that cover the most bins
+// the LDS sort admits
+constexpr int kScanRounds = (int)((kSortLdsMax / sizeof(unsigned) + 4 * kSortThreads - 1) / (4 * kSortThreads));
 #ifndef FDATTN_GATHER_CHANNELS
 #define FDATTN_GATHER_CHANNELS 4
 #endif
@@ -734,13 +737,24 @@ __global__ __launch_bounds__(kSortThreads) void fdattn_scan(Args a)
     const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
     unsigned *cnt = a.counts + (size_t)slice * a.nbs;   // counts in, bin ends out
     unsigned *st = a.starts + (size_t)slice * a.nbs;
+    // every count of the slice is loaded first (four per thread and round;
+    // the slice's bins fit the LDS, so at most kScanRounds rounds), then the
+    // rounds are scanned one after the other
+    unsigned c[kScanRounds][4];
+#pragma unroll
+    for (int r = 0; r < kScanRounds; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = r * 4 * kSortThreads + 4 * tid + e;
+            c[r][e] = i < a.nbs ? cnt[i] : 0u;
+        }
     unsigned carry = (unsigned)slice * (unsigned)(a.Q * a.LK);
-    for (int base = 0; base < a.nbs; base += 4 * kSortThreads) {
-        const int i0 = base + 4 * tid;
-        unsigned c[4];
-        for (int e = 0; e < 4; ++e)
-            c[e] = i0 + e < a.nbs ? cnt[i0 + e] : 0u;
-        const unsigned mine = c[0] + c[1] + c[2] + c[3];
+#pragma unroll
+    for (int r = 0; r < kScanRounds; ++r) {
+        if (r * 4 * kSortThreads >= a.nbs)
+            break;
+        const int i0 = r * 4 * kSortThreads + 4 * tid;
+        const unsigned mine = c[r][0] + c[r][1] + c[r][2] + c[r][3];
         const unsigned x = wave_prefix(mine);
         if (lane == 63)
             wsum[wave] = x;
@@ -751,12 +765,13 @@ __global__ __launch_bounds__(kSortThreads) void fdattn_scan(Args a)
             tot += wsum[w];
         }
         unsigned e0 = off + x - mine;
+#pragma unroll
         for (int e = 0; e < 4; ++e) {
             if (i0 + e < a.nbs) {
                 st[i0 + e] = e0;
-                cnt[i0 + e] = e0 + c[e];
+                cnt[i0 + e] = e0 + c[r][e];
             }
-            e0 += c[e];
+            e0 += c[r][e];
         }
         carry += tot;
         __syncthreads();   // wsum is rewritten by the next round
