@@ -21,16 +21,19 @@
 //     LDS; the unit's lanes then place one sample each and broadcast its
 //     corner offsets and weights to the others.
 //   * Backward, with a caller workspace (the sorted path): the location and
-//     logit gradients in the forward's mapping (lane sums by DPP), which
-//     also emits each live sample's bin -- the cell of its top-left corner
-//     -- and a 16-byte record; a counting sort per (image, head) slice, its
+//     logit gradients in the forward's mapping -- per sample, grad_output
+//     dotted with each corner and summed over the unit's lanes by DPP, the
+//     rest of the sample's arithmetic done by the lane that placed it --
+//     which also emits each live sample's bin -- the cell of its top-left
+//     corner -- and a 16-byte record; a counting sort per (image, head) slice, its
 //     queries split over several blocks, each counting in LDS (the coarse
 //     levels put hundreds of samples on one bin, which device atomics would
 //     serialise) and merging into the slice's counts with one device atomic
 //     per bin, then a scan and a placement pass; finally every value cell
 //     sums the records of the four bins whose samples have it as a corner --
 //     two runs of adjacent bins -- with D/4 lanes of four channels, and is
-//     written once.
+//     written once (a slice's coarsest level first: its cells have the
+//     longest lists).
 //   * Backward without a workspace (or when a slice's bins do not fit the
 //     LDS): D lanes per unit, one channel each, and every (sample, corner,
 //     channel) is a device fp32 atomic (N*Q*M*L*K*4*D of them, resolved
