@@ -241,10 +241,10 @@ constexpr int kBackwardRmaxLarge = DCNV4_BWD_RMAX_LARGE;   // ... on large maps
 #endif
 constexpr int kBackwardRegionRmax = DCNV4_BWD_REGION_RMAX;   // largest halo of the grad_offset_mask tiles
 #ifndef DCNV4_BWD_REGION_RMAX_LARGE
-#define DCNV4_BWD_REGION_RMAX_LARGE 4
+#define DCNV4_BWD_REGION_RMAX_LARGE 6
 #endif
 #ifndef DCNV4_BWD_SLICE_LARGE
-#define DCNV4_BWD_SLICE_LARGE 128
+#define DCNV4_BWD_SLICE_LARGE 64
 #endif
 constexpr int kBackwardRegionRmaxLarge = DCNV4_BWD_REGION_RMAX_LARGE;   // ... on large maps
 constexpr int kBackwardSliceLarge = DCNV4_BWD_SLICE_LARGE;   // pixel slice bytes of its blocks there
