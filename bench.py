@@ -37,14 +37,17 @@ HBM_PEAK_GBPS = 8000.0
 KERNEL_SRCS = {op: [os.path.join(ROOT, "dynamic_sparse_vision_amd", "csrc", n) for n in names]
                for op, names in (("dcnv4", ("dcnv4_device.h", "dcnv4_kernels.hip", "dcnv4_tiled.h",
                                             "dcnv4_tiled_fwd.hip", "dcnv4_tiled_bwd_offsets.hip",
-                                            "dcnv4_tiled_bwd_values.hip", "dcnv4_tiled_launch.hip")),
-                                 ("fdattn", ("dcnv4_device.h", "dcnv4_kernels.hip", "fdattn_kernels.hip")))}
+                                            "dcnv4_tiled_bwd_values.hip", "dcnv4_tiled_launch.hip",
+                                            "dcnv4_api.cpp")),
+                                 ("fdattn", ("dcnv4_device.h", "dcnv4_kernels.hip", "fdattn_kernels.hip",
+                                             "fdattn_api.cpp")))}
 FDA_METRIC = "flash deformable attention fwd/bwd sampled points/s (N·Q·M·L·K·D) + achieved HBM GB/s % of peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash(op: str = "dcnv4") -> str:
-    """sha256 of the kernel sources of one operator (dcnv4 or fdattn)."""
+    """sha256 of the kernel sources and the tile planner of one operator
+    (dcnv4 or fdattn): what decides the kernels' memory traffic."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS[op]:
         with open(path, "rb") as f:
