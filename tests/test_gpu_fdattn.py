@@ -133,6 +133,24 @@ def test_parity(w):
     run_case(w)
 
 
+# Encoder-ordered queries (Q = S, query q is pixel q of the concatenated
+# levels) with 32-channel heads, the benchmark's layout at small sizes: odd
+# level sizes, one-pixel levels, several images and heads, a wide spread
+# (many samples off their level's map), and 16-bit storage.
+ENCODER_CASES = [
+    _w("enc_odd_fp32", N=2, M=3, Q=0, shapes=((13, 19), (7, 10), (4, 5), (1, 1))),
+    _w("enc_spread_fp32", N=1, M=2, Q=0, shapes=((24, 40), (12, 20), (6, 10)), sigma_px=14.0),
+    _w("enc_fp16", dtype="fp16", N=2, M=2, Q=0, shapes=((16, 24), (8, 12), (4, 6), (2, 3))),
+    _w("enc_bf16", dtype="bf16", N=1, M=4, Q=0, shapes=((9, 17), (5, 9), (3, 5))),
+]
+
+
+@pytest.mark.parametrize("w", ENCODER_CASES, ids=[c.name for c in ENCODER_CASES])
+def test_parity_encoder_windows(w):
+    say(f"[fdattn] {w.name} N={w.N} levels={w.shapes} encoder queries M={w.M} D={w.D} K={w.K} {w.dtype}")
+    run_case(w)
+
+
 ATOMIC_CASES = [c for c in CASES if c.name in ("d32_fp32", "spread_fp32", "l16k8_fp32", "l16k8_d8_fp32", "d16_bf16")]
 
 
