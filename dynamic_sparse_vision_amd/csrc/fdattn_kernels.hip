@@ -18,8 +18,9 @@
 //     thread and 128-bit loads of the walkthrough "DCNv4论文解析", section
 //     2.2); a corner is one (fp16/bf16) or two (fp32) 128-bit buffer loads.
 //     The softmax is taken once per unit, its lanes sharing the logits, into
-//     LDS; the unit's lanes then place one sample each and broadcast its
-//     corner offsets and weights to the others.
+//     LDS; with 16-bit storage the unit's lanes then place one sample each
+//     and broadcast its corner offsets and weights to the others (fp32
+//     lanes place every sample themselves, which measured faster there).
 //   * Backward, with a caller workspace (the sorted path): the location and
 //     logit gradients in the forward's mapping -- per sample, grad_output
 //     dotted with each corner and summed over the unit's lanes by DPP, the
@@ -382,52 +383,89 @@ __global__ __launch_bounds__(kThreads) void fdattn_fwd(Args a)
     float acc[8];
     for (int c = 0; c < 8; ++c)
         acc[c] = 0.0f;
-    // The U lanes of a unit take U samples at a time: each lane places one
-    // (location, bilinear weights times the attention weight, corner
-    // offsets), then the group reads the four corners of each of the U
-    // samples in turn, its offsets and weights broadcast from the lane that
-    // placed it.  No branch: a sample outside its map, or past the level's
-    // last point, gets zero weights and out-of-range offsets (whose loads
-    // return zeros), so the compiler can overlap the loads of the samples.
-    for (int l = 0; l < a.L; ++l) {
-        const int H = a.lvl_h[l], W = a.lvl_w[l], start = a.lvl_start[l];
-        const float Hf = (float)H, Wf = (float)W;
-        const int i0 = l * a.K;
-        for (int kb = 0; kb < a.K; kb += U) {
-            const bool have = kb + lane < a.K;
-            const int i = i0 + (have ? kb + lane : a.K - 1);
-            float u, v;
-            ld2(row + 2 * i, u, v);
-            const float x = __builtin_fmaf(u, Wf, -0.5f);
-            const float y = __builtin_fmaf(v, Hf, -0.5f);
-            const bool in = have && live(y, x, Hf, Wf);
-            const float att = att_s[i];
-            // a dead sample (huge or NaN location included) is placed at
-            // (-1, -1): only bounded floors are converted to integers
-            const Corners c = corners(in ? y : -1.0f, in ? x : -1.0f, H, W, start, a.pix_bytes, base);
-            unsigned o[4], w[4];
+    if constexpr (es == 4) {
+        // fp32: every lane of the unit places every sample itself (two
+        // 128-bit loads per corner; measured faster for fp32 than the
+        // broadcast below, 344 against 354 us on the 800x1280 workload)
+        for (int l = 0; l < a.L; ++l) {
+            const int H = a.lvl_h[l], W = a.lvl_w[l], start = a.lvl_start[l];
+            const float Hf = (float)H, Wf = (float)W;
+            const int i0 = l * a.K;
+#pragma unroll 4
+            for (int k = 0; k < a.K; ++k) {
+                const int i = i0 + k;
+                float u, v;
+                ld2(row + 2 * i, u, v);
+                const float x = __builtin_fmaf(u, Wf, -0.5f);
+                const float y = __builtin_fmaf(v, Hf, -0.5f);
+                const bool in = live(y, x, Hf, Wf);
+                const float att = att_s[i];
+                // a dead sample (huge or NaN location included) is placed at
+                // (-1, -1): only bounded floors are converted to integers
+                const Corners c = corners(in ? y : -1.0f, in ? x : -1.0f, H, W, start, a.pix_bytes, base);
+                float vq[4][8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                o[q] = in ? c.o[q] : kOutOfRange;
-                w[q] = __builtin_bit_cast(unsigned, in ? att * c.w[q] : 0.0f);
-            }
-            static_for<U>([&](auto r) {
-                constexpr int R = decltype(r)::value;
-                float vq[4][8], wq[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    // kOutOfRange plus a channel offset stays out of range
-                    load8<T>(vr, group_bcast<U, R>(o[q]) + chan, vq[q]);
-                    wq[q] = __builtin_bit_cast(float, group_bcast<U, R>(w[q]));
-                }
+                for (int qq = 0; qq < 4; ++qq)   // kOutOfRange plus a channel offset stays out of range
+                    load8<T>(vr, (in ? c.o[qq] : kOutOfRange) + chan, vq[qq]);
+                const float a0 = in ? att * c.w[0] : 0.0f, a1 = in ? att * c.w[1] : 0.0f;
+                const float a2 = in ? att * c.w[2] : 0.0f, a3 = in ? att * c.w[3] : 0.0f;
                 for (int e = 0; e < 8; ++e) {
                     float s = acc[e];
-                    s = __builtin_fmaf(wq[0], vq[0][e], s);
-                    s = __builtin_fmaf(wq[1], vq[1][e], s);
-                    s = __builtin_fmaf(wq[2], vq[2][e], s);
-                    acc[e] = __builtin_fmaf(wq[3], vq[3][e], s);
+                    s = __builtin_fmaf(a0, vq[0][e], s);
+                    s = __builtin_fmaf(a1, vq[1][e], s);
+                    s = __builtin_fmaf(a2, vq[2][e], s);
+                    acc[e] = __builtin_fmaf(a3, vq[3][e], s);
                 }
-            });
+            }
+        }
+    } else {
+        // The U lanes of a unit take U samples at a time: each lane places one
+        // (location, bilinear weights times the attention weight, corner
+        // offsets), then the group reads the four corners of each of the U
+        // samples in turn, its offsets and weights broadcast from the lane that
+        // placed it.  No branch: a sample outside its map, or past the level's
+        // last point, gets zero weights and out-of-range offsets (whose loads
+        // return zeros), so the compiler can overlap the loads of the samples.
+        for (int l = 0; l < a.L; ++l) {
+            const int H = a.lvl_h[l], W = a.lvl_w[l], start = a.lvl_start[l];
+            const float Hf = (float)H, Wf = (float)W;
+            const int i0 = l * a.K;
+            for (int kb = 0; kb < a.K; kb += U) {
+                const bool have = kb + lane < a.K;
+                const int i = i0 + (have ? kb + lane : a.K - 1);
+                float u, v;
+                ld2(row + 2 * i, u, v);
+                const float x = __builtin_fmaf(u, Wf, -0.5f);
+                const float y = __builtin_fmaf(v, Hf, -0.5f);
+                const bool in = have && live(y, x, Hf, Wf);
+                const float att = att_s[i];
+                // a dead sample (huge or NaN location included) is placed at
+                // (-1, -1): only bounded floors are converted to integers
+                const Corners c = corners(in ? y : -1.0f, in ? x : -1.0f, H, W, start, a.pix_bytes, base);
+                unsigned o[4], w[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    o[q] = in ? c.o[q] : kOutOfRange;
+                    w[q] = __builtin_bit_cast(unsigned, in ? att * c.w[q] : 0.0f);
+                }
+                static_for<U>([&](auto r) {
+                    constexpr int R = decltype(r)::value;
+                    float vq[4][8], wq[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        // kOutOfRange plus a channel offset stays out of range
+                        load8<T>(vr, group_bcast<U, R>(o[q]) + chan, vq[q]);
+                        wq[q] = __builtin_bit_cast(float, group_bcast<U, R>(w[q]));
+                    }
+                    for (int e = 0; e < 8; ++e) {
+                        float s = acc[e];
+                        s = __builtin_fmaf(wq[0], vq[0][e], s);
+                        s = __builtin_fmaf(wq[1], vq[1][e], s);
+                        s = __builtin_fmaf(wq[2], vq[2][e], s);
+                        acc[e] = __builtin_fmaf(wq[3], vq[3][e], s);
+                    }
+                });
+            }
         }
     }
     T *out = static_cast<T *>(a.out) + qrow * a.D + lane * 8;
